@@ -1,0 +1,214 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MoE expert-forward library.
+ *
+ * One MoE layer of a batch-1 (or small-batch) decode step, as the Flash-MoE
+ * pages describe for Qwen3.5-397B-A17B:
+ *   router GEMV -> softmax -> top-K -> renormalise            (moe_route)
+ *   dequantised gate/up GEMVs -> SwiGLU -> dequantised down GEMV
+ *   for the K routed experts plus one shared expert -> weighted combine
+ *                                                               (moe_expert_forward)
+ *   both, back to back on one stream                            (moe_layer_decode)
+ *
+ * Sources for the method (web pages; cited by title and section):
+ *   [HL] "Flash-MoE: Running a 397B Parameter Model on a Laptop" (hysenlabs.com),
+ *        section "How the SSD expert streaming pipeline works": 60 layers, 512
+ *        experts per layer, K=4 routed plus one shared expert, hidden size 4096,
+ *        4-bit experts of about 6.75 MB; routing is a softmax followed by a
+ *        top-K; the expert forward pass is followed by a combine.
+ *   [MC] "Flash-MoE: Running a 400 Billion Parameter Model on a MacBook"
+ *        (mattcullerton.com), section "The Architecture": experts are 4-bit,
+ *        about 6.75 MB each, and the inner loop is a dequantising FMA kernel.
+ *   [WK] "Flash-MoE" (wiki.edouardfoussier.com), section "Performance Results"
+ *        (table): 4-bit and 2-bit expert configurations.
+ * The pages state neither the quantisation form, the group size, the
+ * intermediate size, the activation nor the renormalisation; the readings
+ * taken here are written next to each item below.
+ *
+ * ---------------------------------------------------------------------------
+ * Expert blob format (one contiguous byte range per expert)
+ * ---------------------------------------------------------------------------
+ * Parameters: hidden H, intermediate I, bits b in {2,4}, group g = 64.
+ * cpw = 32/b codes per 32-bit little-endian word.
+ * Sections, in this order, each starting at a 256-byte aligned offset from
+ * the start of the blob (with H, I multiples of 256 no padding occurs):
+ *   0 GATE_Q  I rows x H/cpw words   codes of Gate [I][H]
+ *   1 UP_Q    I rows x H/cpw words   codes of Up   [I][H]
+ *   2 DOWN_Q  H rows x I/cpw words   codes of Down [H][I]
+ *   3 GATE_SB I rows x H/g words     (scale, bias) of Gate
+ *   4 UP_SB   I rows x H/g words     (scale, bias) of Up
+ *   5 DOWN_SB H rows x I/g words     (scale, bias) of Down
+ * Code c of row r of a matrix with C columns lives in word r*(C/cpw) + c/cpw
+ * at bit offset b*(c % cpw), lowest bits first; it is an unsigned integer
+ * q in [0, 2^b - 1].
+ * An SB word [r][j] holds two bf16 values: bits 0..15 the scale s, bits
+ * 16..31 the bias z, both applying to columns j*g .. j*g+g-1 of row r.
+ * The dequantised weight is the affine map
+ *     W[r][c] = s[r][c/g] * q[r][c] + z[r][c/g].
+ * With H=4096, I=1024, b=4 a blob is 7,077,888 bytes = 6.75 MiB, the expert
+ * size [HL] and [MC] give; with b=2 it is 3,932,160 bytes.
+ * Readings ([MC] names only a "4-bit" "dequant" with FMAs): affine form with
+ * unsigned codes, groups of 64 along the input dimension, bf16 scale and
+ * bias; the nibble order and section order are this library's own choice.
+ *
+ * The shared expert uses the same format and the same I.
+ * The router is a bf16 matrix [E][H] (row e = expert e), no bias.
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions for every entry point
+ * ---------------------------------------------------------------------------
+ * - All tensor pointers are DEVICE pointers (hipMalloc / torch allocations on
+ *   the current device) unless stated otherwise; the caller owns them.  The
+ *   library never allocates device or pinned memory.
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *   Every compute call only enqueues work on `stream` and returns; none of
+ *   them synchronises the host, except moe_get_device_error.
+ * - Arguments are validated on the host before anything is enqueued; on any
+ *   error nothing is enqueued and the status says why.
+ * - bf16 tensors are passed as uint16_t bit patterns.
+ * - x is bf16 [T][H], row-major, and is expected to be RMS-normalised by the
+ *   caller (the pages place a norm before routing, [HL]).
+ * - y is fp32 [T][H] row-major.  ids int32 [T][K], w fp32 [T][K], per token
+ *   in descending-logit order.
+ * - Results are deterministic: identical inputs give bitwise-identical
+ *   outputs (no floating-point atomics; fixed reduction orders).
+ * - The workspace `ws` (device memory, caller-owned, moe_workspace_bytes
+ *   bytes, 256-byte aligned) must be initialised once with
+ *   moe_workspace_init before its first use; every call leaves it
+ *   initialised again.  Two calls that overlap in time must not share a
+ *   workspace.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = -1,        /* a required pointer is NULL */
+  MOE_ERR_SHAPE = -2,       /* a size is out of range or inconsistent */
+  MOE_ERR_UNSUPPORTED = -3, /* a valid but unimplemented configuration */
+  MOE_ERR_ALIGN = -4,       /* a pointer or stride is misaligned */
+  MOE_ERR_WORKSPACE = -5,   /* workspace too small */
+  MOE_ERR_HIP = -6,         /* a HIP runtime call failed */
+  MOE_ERR_DEVICE = -7       /* the device reported an invalid input */
+} moe_status;
+
+/* Layer dimensions.
+ *   hidden      H: power of two, 256 <= H <= 16384
+ *   inter       I: power of two, 256 <= I <= 16384
+ *   n_experts   E: 1 <= E <= 1024
+ *   top_k       K: 1 <= K <= min(E, 8)
+ *   group       g: must be 64
+ *   bits        b: 2 or 4
+ *   has_shared  0 or 1 (one shared expert, added with weight 1.0) */
+typedef struct {
+  int32_t hidden, inter, n_experts, top_k, group, bits, has_shared;
+} moe_dims;
+
+/* One layer's weights (device pointers).
+ *   router         bf16 [E][H]; 16-byte aligned
+ *   experts        expert e's blob starts at experts + e * expert_stride;
+ *                  256-byte aligned
+ *   expert_stride  bytes; >= moe_expert_bytes(dims), multiple of 256
+ *   shared         the shared expert's blob (256-byte aligned), NULL iff
+ *                  has_shared == 0 */
+typedef struct {
+  const uint16_t *router;
+  const uint8_t *experts;
+  int64_t expert_stride;
+  const uint8_t *shared;
+} moe_layer;
+
+/* Blob sections, in storage order (see the format above). */
+enum {
+  MOE_SEC_GATE_Q = 0, MOE_SEC_UP_Q = 1, MOE_SEC_DOWN_Q = 2,
+  MOE_SEC_GATE_SB = 3, MOE_SEC_UP_SB = 4, MOE_SEC_DOWN_SB = 5
+};
+
+/* Library ABI version (MOE_ABI_VERSION). */
+int32_t moe_abi_version(void);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *moe_status_str(moe_status s);
+
+/* Checks dims against the constraints above.  Host only. */
+moe_status moe_check_dims(const moe_dims *dims);
+
+/* Bytes of one expert blob for dims (0 if dims are invalid).  Host only. */
+size_t moe_expert_bytes(const moe_dims *dims);
+
+/* Byte offsets of the six sections (out[6]); returns MOE_ERR_* for bad dims.
+ * Host only. */
+moe_status moe_blob_layout(const moe_dims *dims, size_t out_offsets[6]);
+
+/* Workspace bytes needed for calls with T tokens (0 if invalid).  Host only. */
+size_t moe_workspace_bytes(const moe_dims *dims, int32_t T);
+
+/* Enqueues the one-time initialisation of a workspace of ws_bytes bytes. */
+moe_status moe_workspace_init(void *ws, size_t ws_bytes, void *stream);
+
+/* Routing ([HL], "How the SSD expert streaming pipeline works": the router
+ * scores feed a softmax and a top-K selection).
+ *   logits[t][e] = sum_c router[e][c] * x[t][c]    (bf16 products, fp32 sums)
+ *   ids[t][0..K-1] = the K largest logits in descending order; equal logits
+ *                    are ordered by lower expert index (a reading: the pages
+ *                    do not say)
+ *   w[t][k] = exp(logit_k) / sum over the K selected of exp(logit)
+ *           = softmax over all E, restricted to the selected K, renormalised
+ *             to sum to 1 (a reading: the pages do not say whether they
+ *             renormalise; here they do).
+ * Arguments: x bf16 [T][H] (16-byte aligned); ids int32 [T][K]; w fp32 [T][K];
+ * logits fp32 [T][E] or NULL.  1 <= T <= 256. */
+moe_status moe_route(const moe_dims *dims, const uint16_t *router,
+                     const uint16_t *x, int32_t T, int32_t *ids, float *w,
+                     float *logits, void *ws, size_t ws_bytes, void *stream);
+
+/* Expert forward and combine ([HL], same section: the expert forward pass
+ * for the K routed experts, then the combine; the shared expert runs beside
+ * them).  For each token t:
+ *   for each selected expert e and for the shared expert:
+ *     g = Gate_e x_t, u = Up_e x_t            (dequantised weights)
+ *     h = silu(g) * u,  silu(v) = v / (1 + exp(-v))   (SwiGLU: a reading)
+ *     d_e = Down_e h
+ *   y[t] = sum_k w[t][k] * d_{ids[t][k]} + d_shared
+ * (the shared expert enters with weight 1: a reading.)
+ * ids/w: device int32/fp32 [T][K] (e.g. from moe_route).  An id outside
+ * [0, E) makes that slot contribute 0 and sets the workspace's sticky error
+ * flag (see moe_get_device_error).  y fp32 [T][H], 16-byte aligned. */
+moe_status moe_expert_forward(const moe_dims *dims, const moe_layer *layer,
+                              const uint16_t *x, int32_t T,
+                              const int32_t *ids, const float *w, float *y,
+                              void *ws, size_t ws_bytes, void *stream);
+
+/* moe_route followed by moe_expert_forward on the same stream, with ids/w
+ * kept on the device.  ids and w may be NULL (then they stay in the
+ * workspace); if given they receive the routing. */
+moe_status moe_layer_decode(const moe_dims *dims, const moe_layer *layer,
+                            const uint16_t *x, int32_t T, float *y,
+                            int32_t *ids, float *w, void *ws, size_t ws_bytes,
+                            void *stream);
+
+/* Test hook: writes the dequantised fp32 matrix `which` (0 Gate [I][H],
+ * 1 Up [I][H], 2 Down [H][I]) of one blob to out (row-major).  Each element
+ * is s*q + z rounded once to fp32 (s*q is exact in fp32), so the result is
+ * bit-exact against any correct decoder of the format. */
+moe_status moe_dequantize(const moe_dims *dims, const uint8_t *blob,
+                          int32_t which, float *out, void *stream);
+
+/* Synchronises `stream`, returns the workspace's sticky device error flags in
+ * *err (0 = none; bit 0 = an expert id was out of range) and clears them.
+ * `err` is a host pointer.  Returns MOE_ERR_DEVICE when *err != 0. */
+moe_status moe_get_device_error(void *ws, void *stream, int32_t *err);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

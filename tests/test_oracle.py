@@ -1,0 +1,391 @@
+"""Pins of the float64 oracle against facts that do not come from the oracle:
+hand-assembled blobs, hand-worked cases, closed forms, brute force, and
+textbook identities.  CPU only."""
+import itertools
+import json
+import math
+import os
+import subprocess
+import sys
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import blobkit
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+SMALL = oracle.Dims(H=256, I=256, E=8, K=4, bits=4)
+
+
+# ---- bf16 and format ----------------------------------------------------------
+
+def test_bf16_decode_exact():
+    assert oracle.lib().or_bf16(0x3F80) == 1.0
+    assert oracle.lib().or_bf16(0xC000) == -2.0
+    assert oracle.lib().or_bf16(0x3C00) == 2.0 ** -7
+    assert oracle.lib().or_bf16(0x3F81) == 1.0 + 2.0 ** -7
+    assert oracle.lib().or_bf16(0x7F7F) == float.fromhex("0x1.fep+127")
+    assert oracle.lib().or_bf16(0x0001) == 2.0 ** -133  # smallest subnormal
+
+
+def test_blob_size_matches_page_expert_size():
+    facts = _gold("page_facts.json")
+    d4 = oracle.Dims(H=facts["hidden"]["value"], I=1024, E=512, K=4, bits=4)
+    assert oracle.blob_bytes(d4) == 7_077_888
+    assert oracle.blob_bytes(d4) == facts["expert_mib_4bit"]["value"] * 2 ** 20
+    d2 = oracle.Dims(H=4096, I=1024, E=512, K=4, bits=2)
+    assert oracle.blob_bytes(d2) == 3_932_160
+    # 60 x 512 experts: the 2-bit stack is about 90 GB smaller (pages: ~89 GB saved)
+    saving_gb = 60 * 512 * (7_077_888 - 3_932_160) / 1e9
+    assert abs(saving_gb - facts["saving_gb_2bit"]["value"]) < 10
+
+
+def test_section_offsets_by_hand():
+    # H = I = 256, 4-bit: code sections 256 rows x 128 B = 32768 B;
+    # (s,z) sections 256 rows x 4 groups x 4 B = 4096 B
+    want = [0, 32768, 65536, 98304, 102400, 106496, 110592]
+    assert [oracle.section_offset(SMALL, s) for s in range(7)] == want
+    # 2-bit, H=512, I=256: gate/up codes 256 x 512/16 x 4 = 32768 B,
+    # down codes 512 x 256/16 x 4 = 32768 B, gate/up sb 256 x 8 x 4 = 8192,
+    # down sb 512 x 4 x 4 = 8192
+    d2 = oracle.Dims(H=512, I=256, E=4, K=2, bits=2)
+    want2 = [0, 32768, 65536, 98304, 106496, 114688, 122880]
+    assert [oracle.section_offset(d2, s) for s in range(7)] == want2
+
+
+def _random_codes_blob(d, rng, s_of=None):
+    bits = d.bits
+    qmax = 2 ** bits
+    qg = rng.integers(0, qmax, (d.I, d.H))
+    qu = rng.integers(0, qmax, (d.I, d.H))
+    qd = rng.integers(0, qmax, (d.H, d.I))
+
+    def sb(rows, cols):
+        if s_of is None:
+            return (np.ones((rows, cols // 64), np.float32), np.zeros((rows, cols // 64), np.float32))
+        return s_of(rows, cols // 64)
+    blob = blobkit.assemble(d.H, d.I, bits, qg, qu, qd, sb(d.I, d.H), sb(d.I, d.H), sb(d.H, d.I))
+    return blob, (qg, qu, qd)
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_code_positions_all_elements(bits):
+    d = oracle.Dims(H=512, I=256, E=4, K=2, bits=bits)
+    rng = np.random.default_rng(7)
+    blob, qs = _random_codes_blob(d, rng)
+    assert blob.size == oracle.blob_bytes(d)
+    for which in range(3):
+        # s = 1, z = 0: the dequantised matrix is the code matrix itself
+        np.testing.assert_array_equal(oracle.dequant_matrix(d, blob, which), qs[which])
+    assert oracle.code(d, blob, 0, 3, 5) == qs[0][3, 5]
+    assert oracle.code(d, blob, 2, 511, 255) == qs[2][511, 255]
+
+
+def test_code_bit_order_hand_word():
+    # one gate row whose first word is 0x76543210: codes 0..7 in order
+    d = SMALL
+    qg = np.zeros((d.I, d.H), int)
+    qg[0, :8] = [0, 1, 2, 3, 4, 5, 6, 7]
+    z = np.zeros
+    sb = (np.ones((256, 4), np.float32), z((256, 4), np.float32))
+    blob = blobkit.assemble(256, 256, 4, qg, z((256, 256), int), z((256, 256), int), sb, sb, sb)
+    assert bytes(blob[:4]) == bytes([0x10, 0x32, 0x54, 0x76])
+    assert [oracle.code(d, blob, 0, 0, c) for c in range(8)] == list(range(8))
+
+
+def test_scale_bias_per_group_and_row():
+    d = SMALL
+    rng = np.random.default_rng(3)
+    # distinct exact-bf16 scales/biases per (row, group)
+    def s_of(rows, groups):
+        s = (1 + rng.integers(0, 127, (rows, groups))) * 2.0 ** -10
+        z = (rng.integers(-127, 128, (rows, groups))) * 2.0 ** -12
+        return s.astype(np.float32), z.astype(np.float32)
+    blob, qs = _random_codes_blob(d, rng, s_of)
+    for which, rows, cols in [(0, d.I, d.H), (1, d.I, d.H), (2, d.H, d.I)]:
+        W = oracle.dequant_matrix(d, blob, which)
+        for (r, c) in [(0, 0), (0, 63), (0, 64), (rows - 1, cols - 1), (17, 130)]:
+            s, z = oracle.scale_bias(d, blob, which, r, c)
+            assert W[r, c] == s * qs[which][r, c] + z
+        # group boundaries: columns 63 and 64 use different (s,z) words
+        s63 = oracle.scale_bias(d, blob, which, 5, 63)
+        s64 = oracle.scale_bias(d, blob, which, 5, 64)
+        s0 = oracle.scale_bias(d, blob, which, 5, 0)
+        assert s63 == s0
+
+
+def test_dequant_closed_forms():
+    hw = 256
+    for q, s, z, want in [(0, 0.0078125, -0.0625, -0.0625),        # q=0 -> z
+                          (15, 0.0078125, -0.0625, 15 * 0.0078125 - 0.0625),
+                          (9, 0.0, 0.03125, 0.03125),              # s=0 -> z
+                          (15, 0.015625, 0.0, 0.234375)]:
+        blob = blobkit.constant_blob(hw, hw, 4, q, s, z)
+        assert oracle.dequant(SMALL, blob, 0, 0, 0) == want
+        assert oracle.dequant(SMALL, blob, 2, 255, 255) == want
+        if s != 0:
+            # round trip: the code is recovered exactly
+            assert (oracle.dequant(SMALL, blob, 1, 7, 9) - z) / s == q
+
+
+def test_dequant_f32_is_one_rounding_of_exact_value():
+    # s = 1 + 2^-7 (bf16 exact), z = 2^-30 * (1 + 2^-7): s*15 + z needs ~37 bits
+    s = 1 + 2 ** -7
+    z = 2 ** -30 * (1 + 2 ** -7)
+    blob = blobkit.constant_blob(256, 256, 4, 15, s, z)
+    exact = Fraction(s) * 15 + Fraction(z)
+    assert Fraction(oracle.dequant(SMALL, blob, 0, 0, 0)) == exact
+    want32 = np.float32(float(exact))  # float(exact) is exact here (< 53 bits)
+    got32 = oracle.lib().or_dequant_f32(oracle.Dims(256, 256, 8, 4).c(), blob.ctypes.data_as(
+        oracle._u8p), 0, 0, 0)
+    assert np.float32(got32) == want32
+    assert float(want32) != float(exact)  # a real rounding happened
+    Wf = oracle.dequant_matrix_f32(SMALL, blob, 0)
+    assert Wf[3, 4] == want32
+
+
+def test_dequant_inexact_aborts():
+    # scale 2^60 and bias 2^-60 cannot be summed exactly in double: the
+    # oracle must refuse instead of returning a rounded weight
+    code = r"""
+import sys; sys.path.insert(0, %r)
+import oracle
+from tests import blobkit
+blob = blobkit.constant_blob(256, 256, 4, 3, 2.0**60, 2.0**-60)
+oracle.dequant(oracle.Dims(256, 256, 8, 4), blob, 0, 0, 0)
+print("NOT ABORTED")
+""" % os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True)
+    assert r.returncode != 0
+    assert "inexact dequant" in r.stderr
+    assert "NOT ABORTED" not in r.stdout
+
+
+# ---- routing -------------------------------------------------------------------
+
+def test_router_matches_numpy_matvec():
+    d = oracle.Dims(H=512, I=256, E=32, K=4)
+    rng = np.random.default_rng(11)
+    W = synth.f32_to_bf16(rng.standard_normal((32, 512)) * 0.02)
+    x = synth.f32_to_bf16(rng.standard_normal(512))
+    got = oracle.router_logits(d, W, x)
+    want = oracle.bf16_to_f64(W) @ oracle.bf16_to_f64(x)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-15)
+
+
+def test_router_one_hot():
+    d = oracle.Dims(H=256, I=256, E=16, K=4)
+    rng = np.random.default_rng(5)
+    W = synth.f32_to_bf16(rng.standard_normal((16, 256)) * 0.02)
+    x = np.zeros(256, np.uint16)
+    x[37] = 0x4040  # 3.0
+    got = oracle.router_logits(d, W, x)
+    np.testing.assert_array_equal(got, 3.0 * oracle.bf16_to_f64(W[:, 37]))
+
+
+@pytest.mark.parametrize("case", ["route_2_1_0_m1_k2", "route_ties_k2", "route_all_k4"])
+def test_route_hand_worked(case):
+    c = _gold("hand_worked.json")[case]
+    d = oracle.Dims(H=256, I=256, E=len(c["logits"]), K=c["K"])
+    ids, w, gap = oracle.route_logits(d, np.array(c["logits"]))
+    assert list(ids) == c["ids"]
+    np.testing.assert_allclose(w, c["w"], rtol=1e-15)
+    assert gap == c["gap"]
+
+
+def test_topk_brute_force_small_E():
+    rng = np.random.default_rng(123)
+    E, K = 16, 4
+    d = oracle.Dims(H=256, I=256, E=E, K=K)
+    for trial in range(50):
+        logits = rng.standard_normal(E) * (1 + trial % 3)
+        ids, w, gap = oracle.route_logits(d, logits)
+        best = max(itertools.combinations(range(E), K), key=lambda s: sum(logits[list(s)]))
+        assert set(ids) == set(best)
+        assert all(logits[ids[i]] >= logits[ids[i + 1]] for i in range(K - 1))
+        srt = np.sort(logits)[::-1]
+        assert gap == pytest.approx(np.min(srt[:K] - srt[1:K + 1]), rel=0, abs=0)
+
+
+def test_renormalised_weights_identities():
+    rng = np.random.default_rng(9)
+    for E, K in [(16, 4), (512, 4), (8, 8), (9, 1)]:
+        d = oracle.Dims(H=256, I=256, E=E, K=K)
+        logits = rng.standard_normal(E) * 1.4
+        ids, w, _ = oracle.route_logits(d, logits)
+        sel = logits[ids]
+        soft_sel = np.exp(sel - sel.max()) / np.sum(np.exp(sel - sel.max()))
+        np.testing.assert_allclose(w, soft_sel, rtol=1e-13)   # = softmax over the kept logits
+        assert abs(np.sum(w) - 1) < 1e-15
+        if K == E:  # K = E: the full softmax
+            full = np.exp(logits - logits.max())
+            full /= full.sum()
+            np.testing.assert_allclose(w, full[ids], rtol=1e-13)
+        if K == 1:
+            assert w[0] == 1.0
+
+
+def test_route_permutation_equivariance():
+    rng = np.random.default_rng(21)
+    E, K = 64, 4
+    d = oracle.Dims(H=256, I=256, E=E, K=K)
+    logits = rng.standard_normal(E)
+    perm = rng.permutation(E)
+    ids, w, _ = oracle.route_logits(d, logits)
+    ids_p, w_p, _ = oracle.route_logits(d, logits[perm])
+    # expert perm[i] of the permuted list is expert i's original index
+    np.testing.assert_array_equal(perm[ids_p], ids)
+    np.testing.assert_allclose(w_p, w, rtol=1e-15)
+
+
+# ---- SwiGLU and the expert MLP --------------------------------------------------
+
+def test_silu_values():
+    assert oracle.silu(0.0) == 0.0
+    assert oracle.silu(1.0) == pytest.approx(_gold("hand_worked.json")["silu_1"]["value"], rel=1e-15)
+    assert oracle.silu(40.0) == pytest.approx(40.0, rel=1e-15)
+    assert abs(oracle.silu(-40.0)) < 1e-15
+    assert oracle.silu(-1.0) == pytest.approx(-1.0 / (1.0 + math.e), rel=1e-15)
+
+
+def _per_matrix_constant_blob(H, I, gate, up, down):
+    def mats(rows, cols, p):
+        return (np.full((rows, cols), p["q"]),
+                (np.full((rows, cols // 64), p["s"], np.float32),
+                 np.full((rows, cols // 64), p["z"], np.float32)))
+    qg, sg = mats(I, H, gate)
+    qu, su = mats(I, H, up)
+    qd, sd = mats(H, I, down)
+    return blobkit.assemble(H, I, 4, qg, qu, qd, sg, su, sd)
+
+
+@pytest.mark.parametrize("case", ["expert_saturated", "expert_silu_1"])
+def test_expert_closed_form(case):
+    c = _gold("hand_worked.json")[case]
+    d = oracle.Dims(H=c["H"], I=c["I"], E=4, K=2)
+    blob = _per_matrix_constant_blob(c["H"], c["I"], c["gate"], c["up"], c["down"])
+    x = np.full(c["H"], c["x"])
+    y = oracle.expert(d, blob, x)
+    np.testing.assert_allclose(y, c["y"], rtol=1e-15)
+
+
+def test_expert_matches_numpy_on_dequantised_matrices():
+    d = oracle.Dims(H=512, I=256, E=4, K=2)
+    p = synth.BlobParams(seed=77, H=512, I=256)
+    blob = synth.blob_host(p, 0, 1)
+    rng = np.random.default_rng(4)
+    x = synth.f32_to_bf16(synth.rms_normalise(rng.standard_normal(512)))
+    xd = oracle.bf16_to_f64(x)
+    G = oracle.dequant_matrix(d, blob, 0)
+    U = oracle.dequant_matrix(d, blob, 1)
+    D = oracle.dequant_matrix(d, blob, 2)
+    assert D.shape == (512, 256)
+    g, u = G @ xd, U @ xd
+    h = g / (1 + np.exp(-g)) * u
+    want = D @ h
+    y, hh = oracle.expert(d, blob, x, want_h=True)
+    np.testing.assert_allclose(hh, h, rtol=1e-11, atol=1e-12 * np.abs(h).max())
+    np.testing.assert_allclose(y, want, rtol=1e-11, atol=1e-12 * np.abs(want).max())
+
+
+def test_group_factorisation_identity():
+    # sum_c (s q_c + z) x_c = s sum_c q_c x_c + z sum_c x_c over one group of
+    # 64: the algebra a dequantising GEMV may use in place of per-weight FMAs
+    rng = np.random.default_rng(8)
+    for _ in range(20):
+        q = rng.integers(0, 16, 64).astype(np.float64)
+        x = rng.standard_normal(64)
+        s, z = rng.uniform(0.005, 0.02), rng.uniform(-0.08, 0.08)
+        lhs = np.sum((s * q + z) * x)
+        rhs = s * np.sum(q * x) + z * np.sum(x)
+        assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs))
+
+
+# ---- layer ---------------------------------------------------------------------
+
+def _layer_inputs(E, K, T, H=256, I=256, seed=31):
+    d = oracle.Dims(H=H, I=I, E=E, K=K)
+    p = synth.BlobParams(seed=seed, H=H, I=I)
+    router = synth.router_weights(seed, 0, E, H)
+    blobs = {e: synth.blob_host(p, 0, e) for e in range(E)}
+    shared = synth.blob_host(p, 0, 100000)
+    x = synth.tokens(seed, 0, T, H)
+    return d, router, blobs, shared, x
+
+
+def test_identical_experts_combine_to_one_expert():
+    # sum_k w_k = 1, so K copies of the same expert give that expert's output
+    d, router, blobs, shared, x = _layer_inputs(E=8, K=4, T=2)
+    same = blobs[0]
+    y, ids, w, _, _ = oracle.layer(d, router, {e: same for e in range(8)}, shared, x)
+    for t in range(2):
+        want = oracle.expert(d, same, x[t]) + oracle.expert(d, shared, x[t])
+        np.testing.assert_allclose(y[t], want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
+
+
+def test_zero_shared_expert_leaves_routed_sum():
+    d, router, blobs, shared, x = _layer_inputs(E=8, K=4, T=1)
+    zero = blobkit.constant_blob(256, 256, 4, 5, 0.0, 0.0)
+    y, ids, w, _, _ = oracle.layer(d, router, blobs, zero, x)
+    want = sum(w[0, k] * oracle.expert(d, blobs[ids[0, k]], x[0]) for k in range(4))
+    np.testing.assert_allclose(y[0], want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
+    d0 = oracle.Dims(H=256, I=256, E=8, K=4, has_shared=0)
+    y0, _, _, _, _ = oracle.layer(d0, router, blobs, None, x)
+    np.testing.assert_allclose(y0[0], want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
+
+
+def test_batched_layer_equals_per_token_layers():
+    d, router, blobs, shared, x = _layer_inputs(E=8, K=2, T=3)
+    yb, idsb, wb, lb, gb = oracle.layer(d, router, blobs, shared, x)
+    for t in range(3):
+        y1, ids1, w1, l1, g1 = oracle.layer(d, router, blobs, shared, x[t:t + 1])
+        np.testing.assert_array_equal(y1[0], yb[t])
+        np.testing.assert_array_equal(ids1[0], idsb[t])
+
+
+def test_expert_forward_invalid_id_contributes_zero():
+    d, router, blobs, shared, x = _layer_inputs(E=8, K=2, T=1)
+    ids = np.array([[3, 99]], np.int32)
+    w = np.array([[0.6, 0.4]])
+    y = oracle.expert_forward(d, blobs, shared, x, ids, w)
+    want = 0.6 * oracle.expert(d, blobs[3], x[0]) + oracle.expert(d, shared, x[0])
+    np.testing.assert_allclose(y[0], want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
+
+
+# ---- generator, read back through the oracle's own parser -----------------------
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_generated_blob_ranges_through_oracle_parser(bits):
+    # a section-offset or field-order mistake in either the generator or the
+    # oracle would put code bits where scales are read (or vice versa)
+    d = oracle.Dims(H=4096, I=1024, E=16, K=4, bits=bits)
+    p = synth.BlobParams(seed=5, bits=bits)
+    blob = synth.blob_host(p, 2, 9)
+    assert blob.size == oracle.blob_bytes(d)
+    rng = np.random.default_rng(0)
+    for which, rows, cols in [(0, 1024, 4096), (1, 1024, 4096), (2, 4096, 1024)]:
+        for _ in range(200):
+            r, c = int(rng.integers(rows)), int(rng.integers(cols))
+            s, z = oracle.scale_bias(d, blob, which, r, c)
+            # bounds widened by half a bf16 ulp (values are rounded to bf16)
+            assert 0.005 * (1 - 2 ** -8) <= s <= 0.02 * (1 + 2 ** -8)
+            assert -0.08 * (1 + 2 ** -8) <= z <= 0.08 * (1 + 2 ** -8)
+    W = oracle.dequant_matrix(d, blob, 2)
+    G = oracle.dequant_matrix(d, blob, 0)
+    # codes uniform: the per-group mean of q is near (2^b - 1)/2
+    q = np.array([oracle.code(d, blob, 0, 0, c) for c in range(4096)])
+    hist = np.bincount(q, minlength=2 ** bits)
+    expect = 4096 / 2 ** bits
+    chi2 = float(np.sum((hist - expect) ** 2 / expect))
+    assert chi2 < 60  # dof 15 (or 3): far below this for a uniform source
+    assert np.isfinite(W).all() and np.isfinite(G).all()
