@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""MoE decode benchmark on one MI355X: 60 HBM-resident layers x 512 4-bit
+experts (plus a shared expert and a bf16 router per layer), batch 1.
+
+A step is one decode token: 60 sequential moe_layer_decode calls (router,
+softmax/top-4/renormalise, dequantised gate/up/down GEMVs of 4 routed experts
+plus the shared expert, SwiGLU, weighted combine), replayed from a hipGraph
+captured per token.  Inputs are synthetic (seeded) and resident in HBM before
+the timed region starts; consecutive tokens are AR(1)-correlated so that about
+70% of the routed experts repeat from one token to the next.
+
+Prints one JSON line (see the repository's design notes for every field).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128, help="timed decode tokens")
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--workload", default="stack60", choices=["stack60", "stack60_2bit"])
+    ap.add_argument("--layers", type=int, default=None, help="override layer count (testing)")
+    ap.add_argument("--tokens", type=int, default=None, help="override distinct tokens")
+    ap.add_argument("--cpu-layers", type=int, default=20,
+                    help="layers of the CPU oracle sample (one token)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--check-layers", type=int, default=3,
+                    help="layers of token 0 checked against the oracle")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import bit_dequant_expert_moe_amd as moe
+    import synth
+    from synth.workloads import WORKLOADS
+
+    wl = WORKLOADS[args.workload]
+    nl = args.layers or wl.layers
+    ntok = args.tokens or wl.tokens
+    dims = moe.Dims(hidden=wl.H, inter=wl.I, n_experts=wl.E, top_k=wl.K, bits=wl.bits,
+                    has_shared=wl.has_shared)
+    blob = moe.moe_expert_bytes(dims)
+    stride = blob
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    params = synth.BlobParams(seed=wl.blob_seed, H=wl.H, I=wl.I, bits=wl.bits)
+    SHARED_ID = 0xFFFF
+
+    # ---- resident inputs ---------------------------------------------------
+    t0 = time.time()
+    experts, shared, routers, layers_c = [], [], [], []
+    routers_h = []
+    for l in range(nl):
+        ex = torch.empty(wl.E * stride, dtype=torch.uint8, device=dev)
+        synth.gen_blobs_dev(params, l, 0, wl.E, ex.data_ptr(), stride, sp)
+        sh = torch.empty(blob, dtype=torch.uint8, device=dev)
+        synth.gen_blobs_dev(params, l, SHARED_ID, 1, sh.data_ptr(), blob, sp)
+        rh = synth.router_weights(wl.seed, l, wl.E, wl.H)
+        routers_h.append(rh)
+        r = torch.from_numpy(rh.view(np.int16)).to(dev)
+        experts.append(ex)
+        shared.append(sh)
+        routers.append(r)
+        layers_c.append(moe.make_layer(r, ex, stride, sh))
+    x_h = np.stack([synth.tokens_ar1(wl.seed, l, ntok, wl.H, wl.rho) for l in range(nl)], axis=1)
+    x = torch.from_numpy(x_h.view(np.int16)).to(dev)            # [ntok][nl][H] bf16
+    y = torch.empty((ntok, nl, wl.H), dtype=torch.float32, device=dev)
+    ids = torch.zeros((ntok, nl, wl.K), dtype=torch.int32, device=dev)
+    wts = torch.zeros((ntok, nl, wl.K), dtype=torch.float32, device=dev)
+    ws_bytes = moe.moe_workspace_bytes(dims, 1)
+    ws = moe.alloc_workspace(dims, 1)
+    torch.cuda.synchronize()
+    log("resident: %d layers x %d experts (%.1f GB) in %.1fs" % (
+        nl, wl.E, nl * (wl.E + 1) * blob / 1e9, time.time() - t0))
+
+    def enqueue_token(t):
+        for l in range(nl):
+            moe.moe_layer_decode(dims, layers_c[l], x[t, l], 1, y[t, l], ids[t, l], wts[t, l],
+                                 ws, ws_bytes, sp)
+
+    # ---- one graph per token ------------------------------------------------
+    enqueue_token(0)  # eager run first (also checks the path)
+    torch.cuda.synchronize()
+    graphs = []
+    cs = torch.cuda.Stream()
+    with torch.cuda.stream(cs):
+        for t in range(ntok):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cs):
+                csp = torch.cuda.current_stream().cuda_stream
+                for l in range(nl):
+                    moe.moe_layer_decode(dims, layers_c[l], x[t, l], 1, y[t, l], ids[t, l],
+                                         wts[t, l], ws, ws_bytes, csp)
+            graphs.append(g)
+    torch.cuda.synchronize()
+    log("captured %d token graphs of %d layers" % (ntok, nl))
+
+    for i in range(args.warmup):
+        graphs[i % ntok].replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        graphs[i % ntok].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    ms_per_step = ms / args.steps
+    tok_s = 1000.0 / ms_per_step
+    expert_bytes_tok = nl * (wl.K + wl.has_shared) * blob
+    router_bytes_tok = nl * wl.E * wl.H * 2
+    expert_gbs = expert_bytes_tok * tok_s / 1e9
+    all_gbs = (expert_bytes_tok + router_bytes_tok) * tok_s / 1e9
+    log("decode: %.3f ms/token, %.1f tok/s, %.0f layers/s, expert GB/s %.0f (%.1f%% of 8 TB/s),"
+        " all-bytes GB/s %.0f" % (ms_per_step, tok_s, tok_s * nl, expert_gbs,
+                                   100 * expert_gbs / HBM_PEAK_GBS, all_gbs))
+
+    # routing reuse between consecutive tokens (from every token's ids)
+    for t in range(ntok):
+        graphs[t].replay()
+    torch.cuda.synchronize()
+    ids_h = ids.cpu().numpy()
+    reuse = np.mean([len(set(ids_h[t, l]) & set(ids_h[t - 1, l])) / wl.K
+                     for t in range(1, ntok) for l in range(nl)]) if ntok > 1 else float("nan")
+    log("expert reuse between consecutive tokens: %.3f" % reuse)
+
+    # ---- per-phase kernel durations with HIP events -------------------------
+    # A spin kernel holds the stream while all launches are enqueued, so the
+    # event intervals measure back-to-back device execution.
+    nrep = min(nl, 60)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nrep)]
+    t_tok = 1
+    torch.cuda._sleep(100_000_000)
+    for l in range(nrep):
+        ev[l][0].record()
+        moe.moe_route(dims, routers[l], x[t_tok, l], 1, ids[t_tok, l], wts[t_tok, l], None, ws,
+                      ws_bytes, sp)
+        ev[l][1].record()
+        moe.moe_expert_forward(dims, layers_c[l], x[t_tok, l], 1, ids[t_tok, l], wts[t_tok, l],
+                               y[t_tok, l], ws, ws_bytes, sp)
+        ev[l][2].record()
+    torch.cuda.synchronize()
+    route_us = np.mean([ev[l][0].elapsed_time(ev[l][1]) * 1e3 for l in range(nrep)])
+    fwd_us = np.mean([ev[l][1].elapsed_time(ev[l][2]) * 1e3 for l in range(nrep)])
+    fwd_bytes = (wl.K + wl.has_shared) * blob
+    achieved = fwd_bytes / (fwd_us * 1e-6) / 1e9
+    log("route %.2f us/launch; expert forward %.2f us/launch -> %.0f GB/s" % (
+        route_us, fwd_us, achieved))
+    err = moe.moe_get_device_error(ws, sp)
+    if err:
+        log("device error flags: %d" % err)
+
+    # ---- spot parity against the oracle (token 0, first layers) --------------
+    check = None
+    if args.check_layers > 0:
+        try:
+            import oracle
+            od = oracle.Dims(H=wl.H, I=wl.I, E=wl.E, K=wl.K, bits=wl.bits,
+                             has_shared=wl.has_shared)
+            graphs[0].replay()
+            torch.cuda.synchronize()
+            worst = 0.0
+            for l in range(min(args.check_layers, nl)):
+                idl = ids[0, l].cpu().numpy()
+                lg = oracle.router_logits(od, routers_h[l], x_h[0, l])
+                sel = lg[idl]
+                wo = np.exp(sel - sel.max())
+                wo /= wo.sum()
+                blobs = {int(e): experts[l][int(e) * stride:int(e) * stride + blob].cpu().numpy()
+                         for e in idl}
+                yo = oracle.expert_forward(od, blobs, shared[l].cpu().numpy(), x_h[0, l][None],
+                                           idl[None], wo[None])[0]
+                worst = max(worst, float(np.max(np.abs(y[0, l].cpu().numpy() - yo))
+                                         / np.max(np.abs(yo))))
+            check = worst
+            log("oracle spot check (%d layers): max|dy|/max|y| = %.2e" % (args.check_layers, worst))
+        except Exception as ex:  # the check is informational; the tests are the gate
+            log("oracle spot check skipped: %r" % (ex,))
+
+    # ---- CPU baseline: the float64 oracle on a bounded sample ----------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        od = oracle.Dims(H=wl.H, I=wl.I, E=wl.E, K=wl.K, bits=wl.bits, has_shared=wl.has_shared)
+        ncl = min(args.cpu_layers, nl)
+        data = []
+        for l in range(ncl):
+            # host copies of the experts the oracle itself selects (not timed)
+            ido, _, _, _ = oracle.route(od, routers_h[l], x_h[0, l][None])
+            blobs = {int(e): experts[l][int(e) * stride:int(e) * stride + blob].cpu().numpy()
+                     for e in ido[0]}
+            data.append((blobs, shared[l].cpu().numpy()))
+        tc = time.perf_counter()
+        for l in range(ncl):
+            oracle.layer(od, routers_h[l], data[l][0], data[l][1], x_h[0, l][None])
+        dt = time.perf_counter() - tc
+        cpu_tok_s = 1.0 / (dt * nl / ncl)
+        cpu = {"value": cpu_tok_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": "token 0, layers 0..%d of %d (%.1f s), scaled to %d layers" % (
+                   ncl - 1, nl, dt, nl)}
+        log("cpu oracle: %.1f s for %d layers -> %.4f tok/s" % (dt, ncl, cpu_tok_s))
+
+    out = {
+        "metric": "MoE decode tokens/s (60 layers, batch 1) + expert-weight GB/s as % HBM peak",
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u%d" % wl.bits + "+bf16/fp32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "layers": nl, "experts": wl.E, "top_k": wl.K,
+                   "shared_experts": wl.has_shared, "hidden": wl.H, "inter": wl.I,
+                   "bits": wl.bits, "group": 64, "batch": 1, "tokens": ntok,
+                   "expert_reuse": reuse},
+        "expert_weight_GBps": expert_gbs,
+        "expert_weight_frac_hbm_peak": expert_gbs / HBM_PEAK_GBS,
+        "all_bytes_GBps": all_gbs,
+        "layers_per_s": tok_s * nl,
+        "roofline": {"bound": "hbm", "kernel": "moe_expert_forward (k_gateup + k_down)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "avg_launch_us": fwd_us, "bytes_per_launch": fwd_bytes},
+        "route_us": route_us,
+        "oracle_check_max_rel_err": check,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

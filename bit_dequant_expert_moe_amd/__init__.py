@@ -1,0 +1,202 @@
+"""Thin ctypes binding of libmoe.so (include/moe.h).
+
+Argument marshalling only: every step of the MoE layer runs in the HIP
+kernels of libmoe.so.  Tensors are torch tensors on the current HIP device;
+the stream is torch's current stream unless one is passed.  There is no CPU
+fallback: importing fails loudly if the library is not built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_OK = 0
+STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_UNSUPPORTED",
+          -4: "MOE_ERR_ALIGN", -5: "MOE_ERR_WORKSPACE", -6: "MOE_ERR_HIP", -7: "MOE_ERR_DEVICE"}
+SEC_GATE_Q, SEC_UP_Q, SEC_DOWN_Q, SEC_GATE_SB, SEC_UP_SB, SEC_DOWN_SB = range(6)
+
+# Entry points that libmoe.so exports (one per declaration in include/moe.h).
+EXPORTS = ("moe_abi_version", "moe_status_str", "moe_check_dims", "moe_expert_bytes",
+           "moe_blob_layout", "moe_workspace_bytes", "moe_workspace_init", "moe_route",
+           "moe_expert_forward", "moe_layer_decode", "moe_dequantize", "moe_get_device_error")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__("%s: %s (%d)" % (where, STATUS.get(status, "?"), status))
+        self.status = status
+
+
+class moe_dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("hidden", "inter", "n_experts", "top_k", "group", "bits", "has_shared")]
+
+
+class moe_layer(ctypes.Structure):
+    _fields_ = [("router", ctypes.c_void_p), ("experts", ctypes.c_void_p),
+                ("expert_stride", ctypes.c_int64), ("shared", ctypes.c_void_p)]
+
+
+@dataclass(frozen=True)
+class Dims:
+    hidden: int = 4096
+    inter: int = 1024
+    n_experts: int = 512
+    top_k: int = 4
+    group: int = 64
+    bits: int = 4
+    has_shared: int = 1
+
+    def c(self) -> moe_dims:
+        return moe_dims(self.hidden, self.inter, self.n_experts, self.top_k, self.group,
+                        self.bits, self.has_shared)
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Loads libmoe.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libmoe.so is not built (run __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        dp, lp = ctypes.POINTER(moe_dims), ctypes.POINTER(moe_layer)
+        sig = {
+            "moe_abi_version": (i32, []),
+            "moe_status_str": (ctypes.c_char_p, [i32]),
+            "moe_check_dims": (i32, [dp]),
+            "moe_expert_bytes": (sz, [dp]),
+            "moe_blob_layout": (i32, [dp, ctypes.POINTER(sz)]),
+            "moe_workspace_bytes": (sz, [dp, i32]),
+            "moe_workspace_init": (i32, [vp, sz, vp]),
+            "moe_route": (i32, [dp, vp, vp, i32, vp, vp, vp, vp, sz, vp]),
+            "moe_expert_forward": (i32, [dp, lp, vp, i32, vp, vp, vp, vp, sz, vp]),
+            "moe_layer_decode": (i32, [dp, lp, vp, i32, vp, vp, vp, vp, sz, vp]),
+            "moe_dequantize": (i32, [dp, vp, i32, vp, vp]),
+            "moe_get_device_error": (i32, [vp, vp, ctypes.POINTER(i32)]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc: int, where: str):
+    if rc != MOE_OK:
+        raise MoeError(rc, where)
+
+
+# ---- host-only queries ---------------------------------------------------------
+
+def moe_abi_version() -> int:
+    return int(lib().moe_abi_version())
+
+
+def moe_status_str(status: int) -> str:
+    return lib().moe_status_str(status).decode()
+
+
+def moe_check_dims(d: Dims) -> int:
+    return int(lib().moe_check_dims(ctypes.byref(d.c())))
+
+
+def moe_expert_bytes(d: Dims) -> int:
+    return int(lib().moe_expert_bytes(ctypes.byref(d.c())))
+
+
+def moe_blob_layout(d: Dims):
+    out = (ctypes.c_size_t * 6)()
+    _check(lib().moe_blob_layout(ctypes.byref(d.c()), out), "moe_blob_layout")
+    return list(out)
+
+
+def moe_workspace_bytes(d: Dims, T: int) -> int:
+    return int(lib().moe_workspace_bytes(ctypes.byref(d.c()), T))
+
+
+# ---- device calls (enqueue on a stream) ---------------------------------------
+
+def make_layer(router, experts, expert_stride: int, shared=None) -> moe_layer:
+    return moe_layer(_ptr(router), _ptr(experts), int(expert_stride), _ptr(shared))
+
+
+def moe_workspace_init(ws, ws_bytes: int, stream=None):
+    _check(lib().moe_workspace_init(_ptr(ws), ws_bytes, _stream(stream)), "moe_workspace_init")
+
+
+def alloc_workspace(d: Dims, T: int, device=None, stream=None):
+    """Allocates (torch uint8, 256-byte aligned) and initialises a workspace."""
+    import torch
+    n = moe_workspace_bytes(d, T)
+    if n == 0:
+        raise MoeError(-2, "moe_workspace_bytes")
+    ws = torch.empty(n + 256, dtype=torch.uint8, device=device or "cuda")
+    off = (-ws.data_ptr()) % 256
+    ws = ws[off:off + n]
+    moe_workspace_init(ws, n, stream)
+    return ws
+
+
+def moe_route(d: Dims, router, x, T: int, ids, w, logits=None, ws=None, ws_bytes=None,
+              stream=None):
+    rc = lib().moe_route(ctypes.byref(d.c()), _ptr(router), _ptr(x), T, _ptr(ids), _ptr(w),
+                         _ptr(logits), _ptr(ws), ws_bytes if ws_bytes is not None else ws.numel(),
+                         _stream(stream))
+    _check(rc, "moe_route")
+
+
+def moe_expert_forward(d: Dims, layer: moe_layer, x, T: int, ids, w, y, ws, ws_bytes=None,
+                       stream=None):
+    rc = lib().moe_expert_forward(ctypes.byref(d.c()), ctypes.byref(layer), _ptr(x), T,
+                                  _ptr(ids), _ptr(w), _ptr(y), _ptr(ws),
+                                  ws_bytes if ws_bytes is not None else ws.numel(),
+                                  _stream(stream))
+    _check(rc, "moe_expert_forward")
+
+
+def moe_layer_decode(d: Dims, layer: moe_layer, x, T: int, y, ids=None, w=None, ws=None,
+                     ws_bytes=None, stream=None):
+    rc = lib().moe_layer_decode(ctypes.byref(d.c()), ctypes.byref(layer), _ptr(x), T, _ptr(y),
+                                _ptr(ids), _ptr(w), _ptr(ws),
+                                ws_bytes if ws_bytes is not None else ws.numel(),
+                                _stream(stream))
+    _check(rc, "moe_layer_decode")
+
+
+def moe_dequantize(d: Dims, blob, which: int, out, stream=None):
+    _check(lib().moe_dequantize(ctypes.byref(d.c()), _ptr(blob), which, _ptr(out),
+                                _stream(stream)), "moe_dequantize")
+
+
+def moe_get_device_error(ws, stream=None) -> int:
+    err = ctypes.c_int32(0)
+    rc = lib().moe_get_device_error(_ptr(ws), _stream(stream), ctypes.byref(err))
+    if rc not in (MOE_OK, -7):
+        raise MoeError(rc, "moe_get_device_error")
+    return int(err.value)

@@ -1,0 +1,33 @@
+"""Builds libmoe.so (the C-ABI library) in-tree with hipcc for gfx950."""
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libmoe.so")
+SOURCES = [os.path.join(CSRC, "moe_host.cpp"), os.path.join(CSRC, "moe_kernels.hip")]
+HEADERS = [os.path.join(CSRC, "moe_internal.h"),
+           os.path.join(os.path.dirname(HERE), "include", "moe.h")]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+         "-Wall", "-Wno-unused-function",
+         # no packed-FP32 instructions in device code
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def build(force: bool = True, extra=None) -> str:
+    srcs = SOURCES + HEADERS
+    if not force and os.path.exists(LIB) and all(
+            os.path.getmtime(s) <= os.path.getmtime(LIB) for s in srcs):
+        return LIB
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *FLAGS, *(extra or []), "-o", tmp, *SOURCES]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + r.stdout + r.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build())

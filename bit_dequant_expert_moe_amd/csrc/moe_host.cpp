@@ -1,0 +1,205 @@
+// moe_host.cpp -- the C ABI of include/moe.h: argument validation, blob and
+// workspace geometry, and dispatch to the kernel launchers.  Validation is
+// pure host code and runs before anything is enqueued, so every error path
+// is testable without a GPU.
+#include <stdint.h>
+#include <string.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+static bool pow2_in(int v, int lo, int hi) {
+  return v >= lo && v <= hi && (v & (v - 1)) == 0;
+}
+
+static bool aligned(const void *p, size_t a) {
+  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+BlobLayout blob_layout(const moe_dims &d) {
+  BlobLayout L;
+  const size_t H = (size_t)d.hidden, I = (size_t)d.inter, b = (size_t)d.bits;
+  const size_t g = (size_t)d.group;
+  const size_t sizes[6] = {I * H * b / 8, I * H * b / 8, H * I * b / 8,
+                           I * (H / g) * 4, I * (H / g) * 4, H * (I / g) * 4};
+  size_t o = 0;
+  for (int s = 0; s < 6; ++s) {
+    L.off[s] = o;
+    o = align_up(o + sizes[s], kAlign);
+  }
+  L.off[6] = o;
+  return L;
+}
+
+WsLayout ws_layout(const moe_dims &d, int T) {
+  WsLayout W;
+  const size_t slots = (size_t)d.top_k + (size_t)d.has_shared;
+  size_t o = 0;
+  W.ctrl = o;
+  o = align_up(o + sizeof(Ctrl), kAlign);
+  W.logits = o;
+  o = align_up(o + (size_t)T * d.n_experts * 4, kAlign);
+  W.ids = o;
+  o = align_up(o + (size_t)T * d.top_k * 4, kAlign);
+  W.w = o;
+  o = align_up(o + (size_t)T * d.top_k * 4, kAlign);
+  W.h = o;
+  o = align_up(o + (size_t)T * slots * d.inter * 4, kAlign);
+  W.total = o;
+  return W;
+}
+
+static moe_status check_dims(const moe_dims *d) {
+  if (!d) return MOE_ERR_NULL;
+  if (d->group != kGroup) return MOE_ERR_UNSUPPORTED;
+  if (d->bits != 2 && d->bits != 4) return MOE_ERR_UNSUPPORTED;
+  if (!pow2_in(d->hidden, 256, 16384) || !pow2_in(d->inter, 256, 16384)) return MOE_ERR_SHAPE;
+  if (d->n_experts < 1 || d->n_experts > kMaxE) return MOE_ERR_SHAPE;
+  if (d->top_k < 1 || d->top_k > kMaxK || d->top_k > d->n_experts) return MOE_ERR_SHAPE;
+  if (d->has_shared != 0 && d->has_shared != 1) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+static moe_status check_layer(const moe_dims *d, const moe_layer *L) {
+  if (!L || !L->experts) return MOE_ERR_NULL;
+  if (d->has_shared && !L->shared) return MOE_ERR_NULL;
+  if (!d->has_shared && L->shared) return MOE_ERR_SHAPE;
+  const size_t eb = blob_layout(*d).off[6];
+  if (L->expert_stride < 0 || (size_t)L->expert_stride < eb) return MOE_ERR_SHAPE;
+  if (L->expert_stride % (int64_t)kAlign != 0) return MOE_ERR_ALIGN;
+  if (!aligned(L->experts, kAlign)) return MOE_ERR_ALIGN;
+  if (L->shared && !aligned(L->shared, kAlign)) return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+static moe_status check_ws(const moe_dims *d, int T, const void *ws, size_t ws_bytes) {
+  if (!ws) return MOE_ERR_NULL;
+  if (!aligned(ws, kAlign)) return MOE_ERR_ALIGN;
+  if (ws_bytes < ws_layout(*d, T).total) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+static moe_status check_T(int T) { return (T < 1 || T > kMaxT) ? MOE_ERR_SHAPE : MOE_OK; }
+
+}  // namespace moe
+
+using namespace moe;
+
+#define MOE_TRY(expr)                \
+  do {                               \
+    moe_status s_ = (expr);          \
+    if (s_ != MOE_OK) return s_;     \
+  } while (0)
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char *moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "null pointer";
+    case MOE_ERR_SHAPE: return "invalid shape or size";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_ALIGN: return "misaligned pointer or stride";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    case MOE_ERR_DEVICE: return "device reported invalid input";
+  }
+  return "unknown status";
+}
+
+moe_status moe_check_dims(const moe_dims *dims) { return check_dims(dims); }
+
+size_t moe_expert_bytes(const moe_dims *dims) {
+  if (check_dims(dims) != MOE_OK) return 0;
+  return blob_layout(*dims).off[6];
+}
+
+moe_status moe_blob_layout(const moe_dims *dims, size_t out_offsets[6]) {
+  MOE_TRY(check_dims(dims));
+  if (!out_offsets) return MOE_ERR_NULL;
+  BlobLayout L = blob_layout(*dims);
+  for (int s = 0; s < 6; ++s) out_offsets[s] = L.off[s];
+  return MOE_OK;
+}
+
+size_t moe_workspace_bytes(const moe_dims *dims, int32_t T) {
+  if (check_dims(dims) != MOE_OK || check_T(T) != MOE_OK) return 0;
+  return ws_layout(*dims, T).total;
+}
+
+moe_status moe_workspace_init(void *ws, size_t ws_bytes, void *stream) {
+  if (!ws) return MOE_ERR_NULL;
+  if (!aligned(ws, kAlign)) return MOE_ERR_ALIGN;
+  if (ws_bytes < sizeof(Ctrl)) return MOE_ERR_WORKSPACE;
+  return launch_ws_init(ws, ws_bytes, stream) == 0 ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_route(const moe_dims *dims, const uint16_t *router, const uint16_t *x,
+                     int32_t T, int32_t *ids, float *w, float *logits, void *ws,
+                     size_t ws_bytes, void *stream) {
+  MOE_TRY(check_dims(dims));
+  MOE_TRY(check_T(T));
+  if (!router || !x || !ids || !w) return MOE_ERR_NULL;
+  if (!aligned(router, 16) || !aligned(x, 16) || !aligned(ids, 4) || !aligned(w, 4) ||
+      (logits && !aligned(logits, 4)))
+    return MOE_ERR_ALIGN;
+  MOE_TRY(check_ws(dims, T, ws, ws_bytes));
+  return launch_route(*dims, router, x, T, ids, w, logits, ws, stream) == 0 ? MOE_OK
+                                                                            : MOE_ERR_HIP;
+}
+
+moe_status moe_expert_forward(const moe_dims *dims, const moe_layer *layer, const uint16_t *x,
+                              int32_t T, const int32_t *ids, const float *w, float *y,
+                              void *ws, size_t ws_bytes, void *stream) {
+  MOE_TRY(check_dims(dims));
+  MOE_TRY(check_T(T));
+  MOE_TRY(check_layer(dims, layer));
+  if (!x || !ids || !w || !y) return MOE_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ids, 4) || !aligned(w, 4))
+    return MOE_ERR_ALIGN;
+  MOE_TRY(check_ws(dims, T, ws, ws_bytes));
+  return launch_expert_forward(*dims, *layer, x, T, ids, w, y, ws, stream) == 0 ? MOE_OK
+                                                                                : MOE_ERR_HIP;
+}
+
+moe_status moe_layer_decode(const moe_dims *dims, const moe_layer *layer, const uint16_t *x,
+                            int32_t T, float *y, int32_t *ids, float *w, void *ws,
+                            size_t ws_bytes, void *stream) {
+  MOE_TRY(check_dims(dims));
+  MOE_TRY(check_T(T));
+  MOE_TRY(check_layer(dims, layer));
+  if (!x || !y) return MOE_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(y, 16) || (ids && !aligned(ids, 4)) || (w && !aligned(w, 4)))
+    return MOE_ERR_ALIGN;
+  MOE_TRY(check_ws(dims, T, ws, ws_bytes));
+  const WsLayout W = ws_layout(*dims, T);
+  uint8_t *base = static_cast<uint8_t *>(ws);
+  int32_t *ids_d = ids ? ids : reinterpret_cast<int32_t *>(base + W.ids);
+  float *w_d = w ? w : reinterpret_cast<float *>(base + W.w);
+  if (launch_route(*dims, layer->router, x, T, ids_d, w_d, nullptr, ws, stream) != 0)
+    return MOE_ERR_HIP;
+  if (launch_expert_forward(*dims, *layer, x, T, ids_d, w_d, y, ws, stream) != 0)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+moe_status moe_dequantize(const moe_dims *dims, const uint8_t *blob, int32_t which, float *out,
+                          void *stream) {
+  MOE_TRY(check_dims(dims));
+  if (!blob || !out) return MOE_ERR_NULL;
+  if (which < 0 || which > 2) return MOE_ERR_SHAPE;
+  if (!aligned(blob, kAlign) || !aligned(out, 16)) return MOE_ERR_ALIGN;
+  return launch_dequantize(*dims, blob, which, out, stream) == 0 ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_get_device_error(void *ws, void *stream, int32_t *err) {
+  if (!ws || !err) return MOE_ERR_NULL;
+  if (!aligned(ws, kAlign)) return MOE_ERR_ALIGN;
+  if (read_device_error(ws, stream, err) != 0) return MOE_ERR_HIP;
+  return *err ? MOE_ERR_DEVICE : MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// moe_internal.h -- shared declarations between the host ABI (moe_host.cpp)
+// and the kernels (moe_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+constexpr int kGroup = 64;
+constexpr int kMaxT = 256;
+constexpr int kMaxK = 8;
+constexpr int kMaxE = 1024;
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t n, size_t a) { return (n + a - 1) / a * a; }
+
+// Byte offsets of the six blob sections plus the total (offsets[6]).
+struct BlobLayout {
+  size_t off[7];
+};
+BlobLayout blob_layout(const moe_dims &d);
+
+// Workspace map (byte offsets from the workspace base).
+//   ctrl    : 256 bytes of control words (see Ctrl)
+//   logits  : fp32 [T][E]
+//   ids     : int32 [T][K]
+//   w       : fp32 [T][K]
+//   h       : fp32 [T][K+1][I]   activations silu(g)*u per slot
+struct Ctrl {
+  uint32_t route_counter;  // blocks of the routing kernel that finished
+  uint32_t err;            // sticky device error flags
+  uint32_t pad[62];
+};
+static_assert(sizeof(Ctrl) == 256, "control block is 256 bytes");
+
+struct WsLayout {
+  size_t ctrl, logits, ids, w, h, total;
+};
+WsLayout ws_layout(const moe_dims &d, int T);
+
+// Geometry of one matrix row in 16-byte segments as the GEMV kernels see it.
+struct RowGeo {
+  int seg_per_row;  // row bytes / 16
+  int lpr;          // lanes of a wave that share one row (<= 64)
+  int rpl;          // rows covered by one wave-wide load (64 / lpr)
+  int nseg;         // segments per lane per row (seg_per_row / lpr)
+};
+inline RowGeo row_geo(int cols, int bits) {
+  RowGeo g;
+  g.seg_per_row = cols * bits / 128;
+  g.lpr = g.seg_per_row < 64 ? g.seg_per_row : 64;
+  g.rpl = 64 / g.lpr;
+  g.nseg = g.seg_per_row / g.lpr;
+  return g;
+}
+
+// Kernel launchers (moe_kernels.hip).  Each returns hipSuccess (0) or the
+// HIP error of the launch.
+int launch_ws_init(void *ws, size_t bytes, void *stream);
+int launch_route(const moe_dims &d, const uint16_t *router, const uint16_t *x, int T,
+                 int32_t *ids, float *w, float *logits, void *ws, void *stream);
+int launch_expert_forward(const moe_dims &d, const moe_layer &L, const uint16_t *x, int T,
+                          const int32_t *ids, const float *w, float *y, void *ws,
+                          void *stream);
+int launch_dequantize(const moe_dims &d, const uint8_t *blob, int which, float *out,
+                      void *stream);
+int read_device_error(void *ws, void *stream, int32_t *err);
+
+}  // namespace moe

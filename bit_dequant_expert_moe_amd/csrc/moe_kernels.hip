@@ -1,0 +1,678 @@
+// moe_kernels.hip -- gfx950 kernels of the MoE layer and their launchers.
+//
+// The method (Flash-MoE pages): "Flash-MoE: Running a 397B Parameter Model on
+// a Laptop" (hysenlabs.com), section "How the SSD expert streaming pipeline
+// works" -- router, softmax + top-K, the forward pass of the selected
+// experts and of the shared expert, combine; "Flash-MoE: Running a 400
+// Billion Parameter Model on a MacBook" (mattcullerton.com), section "The
+// Architecture" -- 4-bit experts whose dequantisation is folded into the
+// FMA inner loop of the matrix-vector product.
+//
+// Kernels
+//   k_route        router GEMV (bf16 x bf16 -> fp32, v_dot2_f32_bf16); the
+//                  last block to finish selects the top-K per token and
+//                  writes the renormalised weights.
+//   k_gateup       gate and up rows of the selected experts and the shared
+//                  expert, SwiGLU epilogue; activations h to the workspace.
+//   k_down         down rows of every slot, weighted combine into y.
+//   k_dequantize   test hook: one matrix of a blob as fp32.
+//
+// Inner-loop arithmetic.  A group of 64 weights shares (s, z), so
+//   sum_c (s q_c + z) x_c = s * sum_c q_c x_c + z * sum_c x_c,
+// and the GEMV needs sum_c q_c x_c only.  Codes are turned into packed
+// 16-bit floats with one v_and_or_b32 per pair: OR-ing a 4-bit field into
+// the mantissa of 1024.0 (fp16 0x6400) gives 1024 + q (or 1024 + 16 q for a
+// field 4 bits up), which v_dot2_f32_f16 multiplies with a pair of x values
+// (pre-divided by 16 where the field sits 4 bits up).  The constant 1024 *
+// sum x is removed once per 16-byte segment.  The down projection uses the
+// same trick in bf16 (128 + q, 0x4300) with h split into bf16 hi + lo so
+// that h keeps ~16 significant bits.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16f(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (finite values).
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
+  h2_t v;
+  v.x = (_Float16)lo;
+  v.y = (_Float16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float h2_sum(uint32_t p) {
+  h2_t v = __builtin_bit_cast(h2_t, p);
+  return (float)v.x + (float)v.y;
+}
+
+// (w & m) | c in one VALU op (the compiler would otherwise emit AND and OR
+// with two literal operands).
+__device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "s"(m), "v"(c));
+  return r;
+}
+
+__device__ __forceinline__ float dot2h(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, a), __builtin_bit_cast(h2_t, b), c,
+                                false);
+}
+
+__device__ __forceinline__ float dot2b(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2_t, a),
+                                         __builtin_bit_cast(b2_t, b), c, false);
+}
+
+// Sum over aligned groups of `width` lanes (power of two <= 64).
+__device__ __forceinline__ float group_sum(float v, int width) {
+  for (int off = width >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ uint4 ldg16(const uint8_t *p) {
+  return *reinterpret_cast<const uint4 *>(p);
+}
+
+constexpr uint32_t kMagicH = 0x64006400u;  // fp16 pair (1024, 1024)
+constexpr uint32_t kMagicB = 0x43004300u;  // bf16 pair (128, 128)
+
+// ---------------------------------------------------------------------------
+// x staging for the gate/up GEMV.  For each 16-byte code segment of a row
+// (32 codes at 4 bits, 64 at 2 bits) the LDS holds the packed fp16 x pairs in
+// the order the unpack produces them, plus two floats:
+//   C = 1024 * (sum of the fp16 values of the pairs)   (removes the magic)
+//   X = sum of x over the segment's columns            (bias term)
+// ---------------------------------------------------------------------------
+template <int BITS>
+struct XSeg {
+  static constexpr int kCols = 128 / BITS;      // columns per segment
+  static constexpr int kPairs = kCols / 2;      // packed pairs per segment
+};
+
+template <int BITS>
+__device__ void stage_x(const uint16_t *__restrict__ x, int H, uint32_t *xp, float2 *cx) {
+  constexpr int kCols = XSeg<BITS>::kCols, kPairs = XSeg<BITS>::kPairs;
+  const int nseg = H / kCols;
+  for (int sg = threadIdx.x; sg < nseg; sg += blockDim.x) {
+    const uint16_t *xs = x + sg * kCols;
+    float C = 0.f, X = 0.f;
+    for (int wd = 0; wd < 4; ++wd) {
+      if (BITS == 4) {
+        // word wd holds codes 8wd .. 8wd+7; pairs (0,4) (1,5)/16 (2,6) (3,7)/16
+        float v[8];
+        for (int j = 0; j < 8; ++j) v[j] = bf16f(xs[8 * wd + j]);
+        for (int j = 0; j < 8; ++j) X += v[j];
+        const float sc[4] = {1.f, 0.0625f, 1.f, 0.0625f};
+        for (int p = 0; p < 4; ++p) {
+          uint32_t pr = pack_h2(v[p] * sc[p], v[p + 4] * sc[p]);
+          xp[sg * kPairs + 4 * wd + p] = pr;
+          C += h2_sum(pr);
+        }
+      } else {
+        // word wd holds codes 16wd .. 16wd+15; pair k = (k, k+8) scaled by
+        // 4^-k (k < 5) or 4^-(k-5) (k >= 5, taken from the word shifted by 10)
+        float v[16];
+        for (int j = 0; j < 16; ++j) v[j] = bf16f(xs[16 * wd + j]);
+        for (int j = 0; j < 16; ++j) X += v[j];
+        for (int k = 0; k < 8; ++k) {
+          const int e = k < 5 ? k : k - 5;
+          const float sc = 1.f / (float)(1 << (2 * e));
+          uint32_t pr = pack_h2(v[k] * sc, v[k + 8] * sc);
+          xp[sg * kPairs + 8 * wd + k] = pr;
+          C += h2_sum(pr);
+        }
+      }
+    }
+    cx[sg] = make_float2(1024.f * C, X);
+  }
+}
+
+// sum_c (magic_c + q_c) * xtilde_c over one 16-byte segment.
+template <int BITS>
+__device__ __forceinline__ float seg_dot_x(uint4 c, const uint32_t *xp) {
+  const uint32_t M = kMagicH;
+  float acc = 0.f;
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int wd = 0; wd < 4; ++wd) {
+    const uint32_t u = w[wd];
+    if (BITS == 4) {
+      const uint32_t u8 = u >> 8;
+      acc = dot2h(and_or(u, 0x000F000Fu, M), xp[4 * wd + 0], acc);
+      acc = dot2h(and_or(u, 0x00F000F0u, M), xp[4 * wd + 1], acc);
+      acc = dot2h(and_or(u8, 0x000F000Fu, M), xp[4 * wd + 2], acc);
+      acc = dot2h(and_or(u8, 0x00F000F0u, M), xp[4 * wd + 3], acc);
+    } else {
+      const uint32_t u10 = u >> 10;
+      acc = dot2h(and_or(u, 0x00030003u, M), xp[8 * wd + 0], acc);
+      acc = dot2h(and_or(u, 0x000C000Cu, M), xp[8 * wd + 1], acc);
+      acc = dot2h(and_or(u, 0x00300030u, M), xp[8 * wd + 2], acc);
+      acc = dot2h(and_or(u, 0x00C000C0u, M), xp[8 * wd + 3], acc);
+      acc = dot2h(and_or(u, 0x03000300u, M), xp[8 * wd + 4], acc);
+      acc = dot2h(and_or(u10, 0x00030003u, M), xp[8 * wd + 5], acc);
+      acc = dot2h(and_or(u10, 0x000C000Cu, M), xp[8 * wd + 6], acc);
+      acc = dot2h(and_or(u10, 0x00300030u, M), xp[8 * wd + 7], acc);
+    }
+  }
+  return acc;
+}
+
+// ---------------------------------------------------------------------------
+// h staging for the down GEMV: per segment of I (32 or 64 activations) the
+// bf16 hi pairs, then the bf16 lo pairs, in the order the unpack produces
+// them (4-bit: (j, j+4) for shift 4j; 2-bit: (k, k+8) for shift 2k), plus
+//   C = 128 * sum(hi + lo), X = sum h.
+// ---------------------------------------------------------------------------
+template <int BITS>
+__device__ void stage_h(const float *__restrict__ h, int I, uint32_t *hp, float2 *cx) {
+  constexpr int kCols = XSeg<BITS>::kCols, kPairs = XSeg<BITS>::kPairs;
+  constexpr int kPerWord = 32 / BITS;  // codes per word
+  constexpr int kHalf = kPerWord / 2;  // pairs per word
+  const int nseg = I / kCols;
+  for (int sg = threadIdx.x; sg < nseg; sg += blockDim.x) {
+    const float *hs = h + sg * kCols;
+    float C = 0.f, X = 0.f;
+    for (int wd = 0; wd < 4; ++wd) {
+      for (int j = 0; j < kHalf; ++j) {
+        const float a = hs[kPerWord * wd + j], b = hs[kPerWord * wd + j + kHalf];
+        const uint32_t ah = f2bf(a), bh = f2bf(b);
+        const float ar = a - bf16f(ah), br = b - bf16f(bh);
+        const uint32_t al = f2bf(ar), bl = f2bf(br);
+        hp[sg * 2 * kPairs + kHalf * wd + j] = ah | (bh << 16);
+        hp[sg * 2 * kPairs + kPairs + kHalf * wd + j] = al | (bl << 16);
+        C += (bf16f(ah) + bf16f(al)) + (bf16f(bh) + bf16f(bl));
+        X += a + b;
+      }
+    }
+    cx[sg] = make_float2(128.f * C, X);
+  }
+}
+
+template <int BITS>
+__device__ __forceinline__ float seg_dot_h(uint4 c, const uint32_t *hp) {
+  constexpr int kPairs = XSeg<BITS>::kPairs;
+  const uint32_t M = kMagicB;
+  float acc = 0.f;
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int wd = 0; wd < 4; ++wd) {
+    const uint32_t u = w[wd];
+    if (BITS == 4) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t v = and_or(u >> (4 * j), 0x000F000Fu, M);
+        acc = dot2b(v, hp[4 * wd + j], acc);
+        acc = dot2b(v, hp[kPairs + 4 * wd + j], acc);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t v = and_or(u >> (2 * k), 0x00030003u, M);
+        acc = dot2b(v, hp[8 * wd + k], acc);
+        acc = dot2b(v, hp[kPairs + 8 * wd + k], acc);
+      }
+    }
+  }
+  return acc;
+}
+
+// ---------------------------------------------------------------------------
+// Routing
+// ---------------------------------------------------------------------------
+struct RouteArgs {
+  const uint16_t *router, *x;
+  int32_t *ids;
+  float *w, *logits_out, *logits;
+  Ctrl *ctrl;
+  int H, E, K, T;
+};
+
+__global__ void __launch_bounds__(256) k_route(RouteArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int e = blockIdx.x * 4 + wave;
+  if (e < a.E) {
+    const uint4 *wr = reinterpret_cast<const uint4 *>(a.router + (size_t)e * a.H);
+    const int nq = a.H / 8;
+    for (int t = 0; t < a.T; ++t) {
+      const uint4 *xr = reinterpret_cast<const uint4 *>(a.x + (size_t)t * a.H);
+      float acc = 0.f;
+      for (int i = lane; i < nq; i += 64) {
+        const uint4 wv = wr[i], xv = xr[i];
+        acc = dot2b(wv.x, xv.x, acc);
+        acc = dot2b(wv.y, xv.y, acc);
+        acc = dot2b(wv.z, xv.z, acc);
+        acc = dot2b(wv.w, xv.w, acc);
+      }
+      acc = group_sum(acc, 64);
+      if (lane == 0) {
+        a.logits[(size_t)t * a.E + e] = acc;
+        if (a.logits_out) a.logits_out[(size_t)t * a.E + e] = acc;
+      }
+    }
+  }
+  // The last block to finish selects the experts of every token.
+  __shared__ int s_last;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();
+    const uint32_t prev = __hip_atomic_fetch_add(&a.ctrl->route_counter, 1u, __ATOMIC_ACQ_REL,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == gridDim.x - 1;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  for (int t = wave; t < a.T; t += 4) {
+    const float *lt = a.logits + (size_t)t * a.E;
+    float v[kMaxE / 64];
+#pragma unroll
+    for (int j = 0; j < kMaxE / 64; ++j) {
+      const int idx = lane + 64 * j;
+      v[j] = idx < a.E ? __hip_atomic_load(lt + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                       : __builtin_nanf("");
+    }
+    float sel_v[kMaxK];
+    int sel_i[kMaxK];
+    for (int k = 0; k < a.K; ++k) {
+      // largest logit; equal logits -> lower index; removed entries are NaN
+      float bv = -__builtin_inff();
+      int bi = 0x7FFFFFFF;
+#pragma unroll
+      for (int j = 0; j < kMaxE / 64; ++j) {
+        const int idx = lane + 64 * j;
+        if (v[j] > bv || (v[j] == bv && idx < bi)) {
+          bv = v[j];
+          bi = idx;
+        }
+      }
+      for (int off = 32; off > 0; off >>= 1) {
+        const float ov = __shfl_xor(bv, off, 64);
+        const int oi = __shfl_xor(bi, off, 64);
+        if (ov > bv || (ov == bv && oi < bi)) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      sel_v[k] = bv;
+      sel_i[k] = bi;
+#pragma unroll
+      for (int j = 0; j < kMaxE / 64; ++j)
+        if (lane + 64 * j == bi) v[j] = __builtin_nanf("");
+    }
+    if (lane == 0) {
+      float den = 0.f, p[kMaxK];
+      for (int k = 0; k < a.K; ++k) {
+        p[k] = expf(sel_v[k] - sel_v[0]);
+        den += p[k];
+      }
+      for (int k = 0; k < a.K; ++k) {
+        a.ids[(size_t)t * a.K + k] = sel_i[k];
+        a.w[(size_t)t * a.K + k] = p[k] / den;
+      }
+    }
+  }
+  if (threadIdx.x == 0)
+    __hip_atomic_store(&a.ctrl->route_counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
+// Gate/up + SwiGLU.  Block = (token, slot, block of rows).  Each wave covers
+// kLoadsGU wave-wide loads of gate and up rows (rpl rows per load).
+// ---------------------------------------------------------------------------
+constexpr int kLoadsGU = 2;
+constexpr int kLoadsDown = 2;
+
+struct GateUpArgs {
+  const uint16_t *x;
+  const uint8_t *experts, *shared;
+  int64_t stride;
+  const int32_t *ids;
+  float *h;
+  Ctrl *ctrl;
+  int H, I, E, K, slots, T;
+  int64_t off_gq, off_uq, off_gsb, off_usb;
+  RowGeo geo;
+  int rows_per_block, blocks_per_slot;
+};
+
+template <int BITS>
+__global__ void __launch_bounds__(256) k_gateup(GateUpArgs a) {
+  extern __shared__ uint32_t smem[];
+  constexpr int kPairs = XSeg<BITS>::kPairs;
+  const int nseg_row = a.geo.seg_per_row;
+  uint32_t *xp = smem;
+  float2 *cx = reinterpret_cast<float2 *>(smem + nseg_row * kPairs);
+
+  const int rb = blockIdx.x % a.blocks_per_slot;
+  const int slot = (blockIdx.x / a.blocks_per_slot) % a.slots;
+  const int t = blockIdx.x / (a.blocks_per_slot * a.slots);
+
+  const uint8_t *blob;
+  if (slot < a.K) {
+    const int e = a.ids[(size_t)t * a.K + slot];
+    if (e < 0 || e >= a.E) {
+      // invalid id: this slot contributes nothing
+      const int r = rb * a.rows_per_block + threadIdx.x;
+      if (threadIdx.x < a.rows_per_block)
+        a.h[((size_t)t * a.slots + slot) * a.I + r] = 0.f;
+      if (threadIdx.x == 0) atomicOr(&a.ctrl->err, 1u);
+      return;
+    }
+    blob = a.experts + (size_t)e * a.stride;
+  } else {
+    blob = a.shared;
+  }
+
+  stage_x<BITS>(a.x + (size_t)t * a.H, a.H, xp, cx);
+  __syncthreads();
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lpr = a.geo.lpr, rpl = a.geo.rpl;
+  const int sl = lane % lpr;
+  const size_t row_bytes = (size_t)nseg_row * 16;
+  const int groups = a.H / kGroup;
+  const uint8_t *gq = blob + a.off_gq, *uq = blob + a.off_uq;
+  const uint32_t *gsb = reinterpret_cast<const uint32_t *>(blob + a.off_gsb);
+  const uint32_t *usb = reinterpret_cast<const uint32_t *>(blob + a.off_usb);
+  const int row0 = rb * a.rows_per_block + wave * (kLoadsGU * rpl);
+
+#pragma unroll
+  for (int ld = 0; ld < kLoadsGU; ++ld) {
+    const int r = row0 + ld * rpl + lane / lpr;
+    float pg = 0.f, pu = 0.f;
+    for (int k = 0; k < a.geo.nseg; ++k) {
+      const int sg = sl + k * lpr;
+      const uint4 cg = ldg16(gq + r * row_bytes + (size_t)sg * 16);
+      const uint4 cu = ldg16(uq + r * row_bytes + (size_t)sg * 16);
+      const int grp = sg * XSeg<BITS>::kCols / kGroup;
+      const uint32_t sbg = gsb[(size_t)r * groups + grp];
+      const uint32_t sbu = usb[(size_t)r * groups + grp];
+      const uint32_t *xs = xp + sg * kPairs;
+      const float2 c = cx[sg];
+      const float ag = seg_dot_x<BITS>(cg, xs) - c.x;
+      const float au = seg_dot_x<BITS>(cu, xs) - c.x;
+      pg += bf16f(sbg & 0xFFFFu) * ag + bf16f(sbg >> 16) * c.y;
+      pu += bf16f(sbu & 0xFFFFu) * au + bf16f(sbu >> 16) * c.y;
+    }
+    pg = group_sum(pg, lpr);
+    pu = group_sum(pu, lpr);
+    if (sl == 0) {
+      const float hv = pg / (1.f + expf(-pg)) * pu;
+      a.h[((size_t)t * a.slots + slot) * a.I + r] = hv;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Down + combine.  Block = (token, block of output rows); it walks the slots
+// in order (routed experts in rank order, then the shared expert), staging
+// each slot's activations in LDS, and accumulates w_k * (Down_k h_k) per row.
+// ---------------------------------------------------------------------------
+struct DownArgs {
+  const uint8_t *experts, *shared;
+  int64_t stride;
+  const int32_t *ids;
+  const float *w;
+  const float *h;
+  float *y;
+  Ctrl *ctrl;
+  int H, I, E, K, slots, T;
+  int64_t off_dq, off_dsb;
+  RowGeo geo;
+  int rows_per_block, blocks_per_token;
+};
+
+template <int BITS>
+__global__ void __launch_bounds__(256) k_down(DownArgs a) {
+  extern __shared__ uint32_t smem[];
+  constexpr int kPairs = XSeg<BITS>::kPairs;
+  const int nseg_row = a.geo.seg_per_row;
+  uint32_t *hp = smem;
+  float2 *cx = reinterpret_cast<float2 *>(smem + nseg_row * 2 * kPairs);
+
+  const int rb = blockIdx.x % a.blocks_per_token;
+  const int t = blockIdx.x / a.blocks_per_token;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lpr = a.geo.lpr, rpl = a.geo.rpl;
+  const int sl = lane % lpr;
+  const size_t row_bytes = (size_t)nseg_row * 16;
+  const int groups = a.I / kGroup;
+  const int row0 = rb * a.rows_per_block + wave * (kLoadsDown * rpl);
+
+  float acc[kLoadsDown];
+#pragma unroll
+  for (int ld = 0; ld < kLoadsDown; ++ld) acc[ld] = 0.f;
+
+  for (int slot = 0; slot < a.slots; ++slot) {
+    const uint8_t *blob;
+    float wk;
+    if (slot < a.K) {
+      const int e = a.ids[(size_t)t * a.K + slot];
+      if (e < 0 || e >= a.E) continue;  // uniform across the block
+      blob = a.experts + (size_t)e * a.stride;
+      wk = a.w[(size_t)t * a.K + slot];
+    } else {
+      blob = a.shared;
+      wk = 1.f;
+    }
+    __syncthreads();
+    stage_h<BITS>(a.h + ((size_t)t * a.slots + slot) * a.I, a.I, hp, cx);
+    __syncthreads();
+    const uint8_t *dq = blob + a.off_dq;
+    const uint32_t *dsb = reinterpret_cast<const uint32_t *>(blob + a.off_dsb);
+#pragma unroll
+    for (int ld = 0; ld < kLoadsDown; ++ld) {
+      const int r = row0 + ld * rpl + lane / lpr;
+      float p = 0.f;
+      for (int k = 0; k < a.geo.nseg; ++k) {
+        const int sg = sl + k * lpr;
+        const uint4 c = ldg16(dq + r * row_bytes + (size_t)sg * 16);
+        const uint32_t sb = dsb[(size_t)r * groups + sg * XSeg<BITS>::kCols / kGroup];
+        const float2 cc = cx[sg];
+        const float q = seg_dot_h<BITS>(c, hp + sg * 2 * kPairs) - cc.x;
+        p += bf16f(sb & 0xFFFFu) * q + bf16f(sb >> 16) * cc.y;
+      }
+      acc[ld] += wk * p;
+    }
+  }
+#pragma unroll
+  for (int ld = 0; ld < kLoadsDown; ++ld) {
+    const float v = group_sum(acc[ld], lpr);
+    const int r = row0 + ld * rpl + lane / lpr;
+    if (sl == 0) a.y[(size_t)t * a.H + r] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Dequantisation hook: one thread per code word.
+// ---------------------------------------------------------------------------
+struct DequantArgs {
+  const uint32_t *q, *sb;
+  float *out;
+  int rows, cols, bits;
+};
+
+__global__ void __launch_bounds__(256) k_dequantize(DequantArgs a) {
+  const int cpw = 32 / a.bits;
+  const int wpr = a.cols / cpw;
+  const size_t n = (size_t)a.rows * wpr;
+  const uint32_t mask = (1u << a.bits) - 1u;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const size_t r = i / wpr;
+    const int c0 = (int)(i - r * wpr) * cpw;
+    const uint32_t w = a.q[i];
+    const uint32_t sz = a.sb[r * (a.cols / kGroup) + c0 / kGroup];
+    const float s = bf16f(sz & 0xFFFFu), z = bf16f(sz >> 16);
+    float *o = a.out + r * a.cols + c0;
+    for (int j = 0; j < cpw; ++j) o[j] = fmaf(s, (float)((w >> (a.bits * j)) & mask), z);
+  }
+}
+
+__global__ void k_ws_init(uint32_t *ctrl, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) ctrl[i] = 0u;
+}
+
+inline hipStream_t S(void *s) { return static_cast<hipStream_t>(s); }
+
+constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
+
+// Allows `bytes` of dynamic LDS for kernel f (the default cap is 64 KB).
+template <typename F>
+int allow_lds(F f, size_t bytes) {
+  if (bytes > kMaxLds) return (int)hipErrorInvalidValue;
+  if (bytes <= 64 * 1024) return 0;
+  return (int)hipFuncSetAttribute(reinterpret_cast<const void *>(f),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+int launch_ws_init(void *ws, size_t, void *stream) {
+  hipLaunchKernelGGL(k_ws_init, dim3(1), dim3(64), 0, S(stream), static_cast<uint32_t *>(ws),
+                     (int)(sizeof(Ctrl) / 4));
+  return (int)hipGetLastError();
+}
+
+int launch_route(const moe_dims &d, const uint16_t *router, const uint16_t *x, int T,
+                 int32_t *ids, float *w, float *logits, void *ws, void *stream) {
+  const WsLayout W = ws_layout(d, T);
+  uint8_t *base = static_cast<uint8_t *>(ws);
+  RouteArgs a;
+  a.router = router;
+  a.x = x;
+  a.ids = ids;
+  a.w = w;
+  a.logits_out = logits;
+  a.logits = reinterpret_cast<float *>(base + W.logits);
+  a.ctrl = reinterpret_cast<Ctrl *>(base + W.ctrl);
+  a.H = d.hidden;
+  a.E = d.n_experts;
+  a.K = d.top_k;
+  a.T = T;
+  hipLaunchKernelGGL(k_route, dim3((d.n_experts + 3) / 4), dim3(256), 0, S(stream), a);
+  return (int)hipGetLastError();
+}
+
+int launch_expert_forward(const moe_dims &d, const moe_layer &L, const uint16_t *x, int T,
+                          const int32_t *ids, const float *w, float *y, void *ws,
+                          void *stream) {
+  const WsLayout W = ws_layout(d, T);
+  const BlobLayout B = blob_layout(d);
+  uint8_t *base = static_cast<uint8_t *>(ws);
+  float *h = reinterpret_cast<float *>(base + W.h);
+  Ctrl *ctrl = reinterpret_cast<Ctrl *>(base + W.ctrl);
+  const int slots = d.top_k + d.has_shared;
+  const int pairs = 64 / d.bits;  // packed pairs per 16-byte segment
+
+  GateUpArgs g;
+  g.x = x;
+  g.experts = L.experts;
+  g.shared = L.shared;
+  g.stride = L.expert_stride;
+  g.ids = ids;
+  g.h = h;
+  g.ctrl = ctrl;
+  g.H = d.hidden;
+  g.I = d.inter;
+  g.E = d.n_experts;
+  g.K = d.top_k;
+  g.slots = slots;
+  g.T = T;
+  g.off_gq = (int64_t)B.off[MOE_SEC_GATE_Q];
+  g.off_uq = (int64_t)B.off[MOE_SEC_UP_Q];
+  g.off_gsb = (int64_t)B.off[MOE_SEC_GATE_SB];
+  g.off_usb = (int64_t)B.off[MOE_SEC_UP_SB];
+  g.geo = row_geo(d.hidden, d.bits);
+  g.rows_per_block = 4 * kLoadsGU * g.geo.rpl;
+  if (g.rows_per_block > d.inter) return (int)hipErrorInvalidValue;
+  g.blocks_per_slot = d.inter / g.rows_per_block;
+  const size_t lds_gu = (size_t)g.geo.seg_per_row * (pairs * 4 + 8);
+  const dim3 grid_gu((unsigned)(g.blocks_per_slot * slots * T));
+
+  DownArgs dn;
+  dn.experts = L.experts;
+  dn.shared = L.shared;
+  dn.stride = L.expert_stride;
+  dn.ids = ids;
+  dn.w = w;
+  dn.h = h;
+  dn.y = y;
+  dn.ctrl = ctrl;
+  dn.H = d.hidden;
+  dn.I = d.inter;
+  dn.E = d.n_experts;
+  dn.K = d.top_k;
+  dn.slots = slots;
+  dn.T = T;
+  dn.off_dq = (int64_t)B.off[MOE_SEC_DOWN_Q];
+  dn.off_dsb = (int64_t)B.off[MOE_SEC_DOWN_SB];
+  dn.geo = row_geo(d.inter, d.bits);
+  dn.rows_per_block = 4 * kLoadsDown * dn.geo.rpl;
+  if (dn.rows_per_block > d.hidden) return (int)hipErrorInvalidValue;
+  dn.blocks_per_token = d.hidden / dn.rows_per_block;
+  const size_t lds_dn = (size_t)dn.geo.seg_per_row * (2 * pairs * 4 + 8);
+  const dim3 grid_dn((unsigned)(dn.blocks_per_token * T));
+
+  if (d.bits == 4) {
+    if (allow_lds(k_gateup<4>, lds_gu) || allow_lds(k_down<4>, lds_dn))
+      return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_gateup<4>, grid_gu, dim3(256), lds_gu, S(stream), g);
+    hipLaunchKernelGGL(k_down<4>, grid_dn, dim3(256), lds_dn, S(stream), dn);
+  } else {
+    if (allow_lds(k_gateup<2>, lds_gu) || allow_lds(k_down<2>, lds_dn))
+      return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_gateup<2>, grid_gu, dim3(256), lds_gu, S(stream), g);
+    hipLaunchKernelGGL(k_down<2>, grid_dn, dim3(256), lds_dn, S(stream), dn);
+  }
+  return (int)hipGetLastError();
+}
+
+int launch_dequantize(const moe_dims &d, const uint8_t *blob, int which, float *out,
+                      void *stream) {
+  const BlobLayout B = blob_layout(d);
+  DequantArgs a;
+  a.q = reinterpret_cast<const uint32_t *>(blob + B.off[which]);
+  a.sb = reinterpret_cast<const uint32_t *>(blob + B.off[3 + which]);
+  a.out = out;
+  a.rows = which == 2 ? d.hidden : d.inter;
+  a.cols = which == 2 ? d.inter : d.hidden;
+  a.bits = d.bits;
+  const size_t words = (size_t)a.rows * a.cols / (32 / d.bits);
+  size_t blocks = (words + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(k_dequantize, dim3((unsigned)blocks), dim3(256), 0, S(stream), a);
+  return (int)hipGetLastError();
+}
+
+int read_device_error(void *ws, void *stream, int32_t *err) {
+  Ctrl *ctrl = static_cast<Ctrl *>(ws);
+  hipError_t e = hipStreamSynchronize(S(stream));
+  if (e != hipSuccess) return (int)e;
+  uint32_t v = 0;
+  e = hipMemcpy(&v, &ctrl->err, 4, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return (int)e;
+  const uint32_t zero = 0;
+  e = hipMemcpy(&ctrl->err, &zero, 4, hipMemcpyHostToDevice);
+  if (e != hipSuccess) return (int)e;
+  *err = (int32_t)v;
+  return 0;
+}
+
+}  // namespace moe

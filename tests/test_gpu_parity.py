@@ -1,0 +1,183 @@
+"""GPU parity of the HIP path against the float64 oracle, through the C ABI.
+
+Bar: routed ids exact (away from float64 near-ties, see gpu_util), routing
+weights within 1e-5, dequantised weights bit-exact, outputs within
+2e-3 * max|oracle| (fp32 accumulation on the device)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import bit_dequant_expert_moe_amd as moe  # noqa: E402
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    # one layer, 16 experts, hidden 4096, intermediate 1024, top-4 + shared
+    return gu.DeviceLayer(4096, 1024, 16, 4, bits=4, seed=1000)
+
+
+@pytest.fixture(scope="module")
+def full():
+    # one full layer, 512 experts
+    return gu.DeviceLayer(4096, 1024, 512, 4, bits=4, seed=1001)
+
+
+# ---- generator and dequantisation -----------------------------------------------
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_device_generator_matches_host(bits):
+    L = gu.DeviceLayer(4096, 1024, 4, 2, bits=bits, seed=42)
+    for e in [0, 3]:
+        np.testing.assert_array_equal(L.blob_host(e), synth.blob_host(L.params, 0, e))
+    np.testing.assert_array_equal(L.shared_host(), synth.blob_host(L.params, 0, gu.SHARED_ID))
+
+
+def _dequant_dev(L, blob_dev, which):
+    rows, cols = (L.dims.hidden, L.dims.inter) if which == 2 else (L.dims.inter, L.dims.hidden)
+    out = torch.empty((rows, cols), dtype=torch.float32, device="cuda")
+    moe.moe_dequantize(L.dims, blob_dev, which, out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("shape", [(4096, 1024, 4), (4096, 1024, 2), (256, 512, 4), (1024, 256, 2)])
+def test_dequantize_bit_exact(shape):
+    H, I, bits = shape
+    _say("dequant", shape)
+    L = gu.DeviceLayer(H, I, 3, 2, bits=bits, seed=7)
+    for e in [0, 2]:
+        blob_dev = L.experts[e * L.stride:]
+        for which in range(3):
+            got = _dequant_dev(L, blob_dev, which)
+            want = oracle.dequant_matrix_f32(L.od, L.blob_host(e), which)
+            np.testing.assert_array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_dequantize_shared_tiny(tiny):
+    for which in range(3):
+        got = _dequant_dev(tiny, tiny.shared, which)
+        want = oracle.dequant_matrix_f32(tiny.od, tiny.shared_host(), which)
+        np.testing.assert_array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+# ---- routing ------------------------------------------------------------------
+
+@pytest.mark.parametrize("which,T", [("tiny", 1), ("tiny", 37), ("full", 1), ("full", 64)])
+def test_route_parity(which, T, tiny, full):
+    L = tiny if which == "tiny" else full
+    _say("route", which, T)
+    x = synth.tokens(L.seed + 17, 0, T, 4096)
+    out = L.decode(x, want_logits=True)
+    ids_o, w_o, logits_o, gap_o = oracle.route(L.od, L.router_h, x)
+    # logits: fp32 sums of exact products vs float64
+    assert np.max(np.abs(out["logits"] - logits_o)) < 1e-4
+    exact = gu.check_routing(L.od, out["ids"], out["w"], logits_o, gap_o, L.dims.top_k)
+    _say("  tokens with exact ids:", exact, "of", T)
+    assert exact >= 0.8 * T
+
+
+# ---- full layer -----------------------------------------------------------------
+
+def _layer_check(L, x, label):
+    out = L.decode(x, want_logits=True)
+    T = x.shape[0]
+    ids_o, w_o, logits_o, gap_o = oracle.route(L.od, L.router_h, x)
+    gu.check_routing(L.od, out["ids"], out["w"], logits_o, gap_o, L.dims.top_k)
+    # teacher-forced: the oracle combines the experts the GPU picked, with the
+    # float64 weights of that pick
+    w_for_gpu = np.empty_like(out["w"], dtype=np.float64)
+    for t in range(T):
+        sel = logits_o[t][out["ids"][t]]
+        ww = np.exp(sel - sel.max())
+        w_for_gpu[t] = ww / ww.sum()
+    y_o = oracle.expert_forward(L.od, L.blob_host, L.shared_host(), x, out["ids"], w_for_gpu)
+    err = gu.max_rel_err(out["y"], y_o)
+    _say("  %s: max|dy|/max|y| = %.3e" % (label, err))
+    assert err <= gu.Y_TOL
+    assert out["err"] == 0
+    return out
+
+
+def test_layer_decode_tiny(tiny):
+    x = synth.tokens(1000, 0, 1, 4096)
+    _layer_check(tiny, x, "tiny T=1")
+
+
+def test_layer_decode_full(full):
+    x = synth.tokens(1001, 0, 1, 4096)
+    _layer_check(full, x, "full T=1")
+
+
+def test_layer_decode_full_batch(full):
+    x = synth.tokens(1001, 5, 4, 4096)
+    _layer_check(full, x, "full T=4")
+
+
+def test_layer_decode_2bit_tiny():
+    L = gu.DeviceLayer(4096, 1024, 16, 4, bits=2, seed=1000, blob_seed=1004)
+    x = synth.tokens(1000, 0, 2, 4096)
+    _layer_check(L, x, "2-bit tiny T=2")
+
+
+@pytest.mark.parametrize("cfg", [
+    (256, 256, 8, 2, 4, 1), (512, 2048, 32, 8, 4, 1), (1024, 256, 4, 4, 2, 0),
+    (8192, 512, 64, 1, 4, 1), (2048, 4096, 16, 3, 2, 1), (16384, 256, 2, 2, 4, 1)])
+def test_layer_decode_shapes(cfg):
+    H, I, E, K, bits, sh = cfg
+    _say("shape", cfg)
+    L = gu.DeviceLayer(H, I, E, K, bits=bits, has_shared=sh, seed=300 + H + I + E)
+    x = synth.tokens(L.seed, 1, 3, H)
+    _layer_check(L, x, "shape %s" % (cfg,))
+
+
+def test_expert_stride_padding():
+    # experts placed at a stride larger than the blob
+    L = gu.DeviceLayer(1024, 512, 8, 2, bits=4, seed=55, stride=2 * 1024 * 1024)
+    x = synth.tokens(55, 0, 2, 1024)
+    _layer_check(L, x, "padded stride")
+
+
+# ---- expert forward with given routing ----------------------------------------------
+
+def test_expert_forward_given_ids_and_invalid_id(tiny):
+    L = tiny
+    x = synth.tokens(999, 0, 2, 4096)
+    ids = np.array([[3, 9, 1, 12], [15, 0, 7, 9999]], np.int32)
+    w = np.array([[0.4, 0.3, 0.2, 0.1], [0.25, 0.25, 0.25, 0.25]], np.float32)
+    ws = moe.alloc_workspace(L.dims, 2)
+    y = torch.empty((2, 4096), dtype=torch.float32, device="cuda")
+    moe.moe_expert_forward(L.dims, L.L, L.x_dev(x), 2, torch.from_numpy(ids).cuda(),
+                           torch.from_numpy(w).cuda(), y, ws)
+    torch.cuda.synchronize()
+    err = moe.moe_get_device_error(ws)
+    assert err == 1  # the out-of-range id was reported
+    assert moe.moe_get_device_error(ws) == 0  # and cleared
+    y_o = oracle.expert_forward(L.od, L.blob_host, L.shared_host(), x, ids,
+                                w.astype(np.float64))
+    assert gu.max_rel_err(y.cpu().numpy(), y_o) <= gu.Y_TOL
+
+
+# ---- invariants ---------------------------------------------------------------------
+
+def test_batched_equals_single_and_deterministic(full):
+    x = synth.tokens(1001, 9, 8, 4096)
+    ob = full.decode(x)
+    ob2 = full.decode(x)
+    np.testing.assert_array_equal(ob["y"], ob2["y"])          # deterministic
+    for t in range(8):
+        o1 = full.decode(x[t:t + 1])
+        np.testing.assert_array_equal(o1["ids"][0], ob["ids"][t])
+        np.testing.assert_array_equal(o1["y"][0], ob["y"][t])   # batched == single
