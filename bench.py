@@ -150,28 +150,26 @@ def main():
                      for t in range(1, ntok) for l in range(nl)]) if ntok > 1 else float("nan")
     log("expert reuse between consecutive tokens: %.3f" % reuse)
 
-    # ---- per-phase kernel durations with HIP events -------------------------
+    # ---- per-launch duration of the layer call, with HIP events ---------------
     # A spin kernel holds the stream while all launches are enqueued, so the
-    # event intervals measure back-to-back device execution.
-    nrep = min(nl, 60)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nrep)]
-    t_tok = 1
+    # event intervals measure back-to-back device execution.  On the
+    # single-token path one moe_layer_decode is one kernel (k_layer1).
+    fused = os.environ.get("MOE_DISABLE_FUSED", "0") != "1"
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(nl)]
+    t_tok = 1 % ntok
     torch.cuda._sleep(100_000_000)
-    for l in range(nrep):
+    for l in range(nl):
         ev[l][0].record()
-        moe.moe_route(dims, routers[l], x[t_tok, l], 1, ids[t_tok, l], wts[t_tok, l], None, ws,
-                      ws_bytes, sp)
+        moe.moe_layer_decode(dims, layers_c[l], x[t_tok, l], 1, y[t_tok, l], ids[t_tok, l],
+                             wts[t_tok, l], ws, ws_bytes, sp)
         ev[l][1].record()
-        moe.moe_expert_forward(dims, layers_c[l], x[t_tok, l], 1, ids[t_tok, l], wts[t_tok, l],
-                               y[t_tok, l], ws, ws_bytes, sp)
-        ev[l][2].record()
     torch.cuda.synchronize()
-    route_us = np.mean([ev[l][0].elapsed_time(ev[l][1]) * 1e3 for l in range(nrep)])
-    fwd_us = np.mean([ev[l][1].elapsed_time(ev[l][2]) * 1e3 for l in range(nrep)])
-    fwd_bytes = (wl.K + wl.has_shared) * blob
-    achieved = fwd_bytes / (fwd_us * 1e-6) / 1e9
-    log("route %.2f us/launch; expert forward %.2f us/launch -> %.0f GB/s" % (
-        route_us, fwd_us, achieved))
+    layer_us = float(np.mean([ev[l][0].elapsed_time(ev[l][1]) * 1e3 for l in range(nl)]))
+    launch_bytes = router_bytes_tok // nl + (wl.K + wl.has_shared) * blob
+    achieved = launch_bytes / (layer_us * 1e-6) / 1e9
+    log("layer call %.2f us/launch -> %.0f GB/s of algorithmic bytes (%d B per launch)" % (
+        layer_us, achieved, launch_bytes))
     err = moe.moe_get_device_error(ws, sp)
     if err:
         log("device error flags: %d" % err)
@@ -247,11 +245,13 @@ def main():
         "expert_weight_frac_hbm_peak": expert_gbs / HBM_PEAK_GBS,
         "all_bytes_GBps": all_gbs,
         "layers_per_s": tok_s * nl,
-        "roofline": {"bound": "hbm", "kernel": "moe_expert_forward (k_gateup + k_down)",
+        "roofline": {"bound": "hbm",
+                     "kernel": "k_layer1 (moe_layer_decode)" if fused else
+                               "moe_layer_decode (k_route + k_gateup + k_down)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "avg_launch_us": fwd_us, "bytes_per_launch": fwd_bytes},
-        "route_us": route_us,
+                     "avg_launch_us": layer_us, "bytes_per_launch": launch_bytes},
+        "device_error_flags": err,
         "oracle_check_max_rel_err": check,
         "cpu_baseline": cpu,
     }

@@ -1,0 +1,656 @@
+// moe_fused.hip -- the whole MoE layer for one token in one launch.
+//
+// Method: "Flash-MoE: Running a 397B Parameter Model on a Laptop"
+// (hysenlabs.com), section "How the SSD expert streaming pipeline works":
+// router -> softmax + top-K -> expert forward of the K selected experts and
+// the shared expert -> combine.  "Flash-MoE: Running a 400 Billion Parameter
+// Model on a MacBook" (mattcullerton.com), section "The Architecture": 4-bit
+// experts dequantised inside the FMA inner loop.
+//
+// Why one launch: a decode layer moves ~40 MB, about 6 us of HBM time on
+// MI355X, while a dependent kernel boundary costs ~1.7 us and a full
+// device-wide barrier across 256 workgroups ~2.3 us.  This kernel keeps every
+// workgroup resident (one per CU) and replaces the two data dependencies of
+// the layer with cheap one-way signals:
+//   * routing: each workgroup writes its logits as (value, epoch) 64-bit
+//     words; every workgroup polls the E words until all carry the current
+//     epoch, so the data arrives with the signal, then selects the top-K
+//     itself (the selection is deterministic, so all agree);
+//   * activations h of slot k: the four gate/up waves of a workgroup hand
+//     their values to the comm wave in LDS; it stores them, adds the
+//     workgroup to a per-group counter (groups = blockIdx % 8, 32 workgroups
+//     each), and the last workgroup of a group raises the group's flag; every
+//     workgroup's comm wave waits for the eight flags of the slot and copies
+//     the slot's h into LDS for its down waves;
+//   * every datum that all workgroups read (logits, h, flags) is stored once
+//     per reader group, so each cache line has ~32 coherent readers: a line
+//     read coherently by all 256 CUs at once serialises at its memory channel
+//     for several microseconds.
+// Each workgroup has 9 waves: waves 0-3 compute gate/up rows (one row of
+// every slot each), waves 4-7 compute down rows (four output rows of every
+// slot each), wave 8 selects the top-K and publishes the workgroup's h
+// values.  The roles keep separate in-order load queues: the down waves'
+// weight loads are in flight while gate/up is still streaming, the
+// activations they wait for do not queue behind gate/up weights, and the
+// comm wave's wait for its own stores never waits for weight loads.
+// No agent-scope fence is used: a cache writeback/invalidate issued by every
+// CU at once costs tens of microseconds.
+// Every weight byte a workgroup needs is requested as soon as its address is
+// known: router, shared expert and x at launch; routed experts right after
+// the top-K.
+//
+// Termination: every wait is bounded; a wait that times out sets bit 1 of
+// the sticky error word and the kernel runs to completion.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+using namespace dev;
+
+constexpr int kG = 256;          // workgroups
+constexpr int kGuWaves = 4;      // gate/up waves 0..3
+constexpr int kDownWaves = 4;    // down waves 4..7
+constexpr int kCommWave = 8;     // routing selection and publication of h
+constexpr int kNT = 64 * (kGuWaves + kDownWaves + 1);
+constexpr int kNR = 64 * (kGuWaves + kDownWaves);  // threads that load the router
+constexpr long kSpinMax = 1L << 18;
+
+// Cross-workgroup data goes through agent-scope relaxed atomics, which the
+// gfx950 memory model implements as coherent (sc1) loads and stores; no
+// cache writeback or invalidate is issued.  Ordering between a workgroup's
+// data and its signal is given by waiting for the data stores to complete
+// (s_waitcnt vmcnt(0)) in the comm wave, which has no weight loads in flight.
+__device__ __forceinline__ uint32_t ld_rlx(const uint32_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_rlx64(const uint64_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// 16-byte coherent load (buffer_load_dwordx4 with the sc1 policy, the same
+// policy as an agent-scope relaxed atomic load), coalesced across the wave.
+__device__ __forceinline__ uint4 ld_coh16(const void *base, uint32_t byte_off) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, 0x7fffffff, 0x00020000);
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 16 /* sc1 */);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+template <int BITS, int H, int I, int K>
+struct Geo {
+  static constexpr int COLS = 128 / BITS;           // columns per 16-byte segment
+  static constexpr int PAIRS = COLS / 2;            // packed x pairs per segment
+  static constexpr int SEG_X = H * BITS / 128;      // segments per gate/up row
+  static constexpr int LSEG = SEG_X / 64;           // segments per lane per gate/up row
+  static constexpr int XLD = COLS * 2 / 16;         // 16-byte x loads per segment
+  static constexpr int RCH = H / 8;                 // 16-byte chunks per router row
+  static constexpr int RXC = RCH / kNR;             // router x chunks per thread
+  static constexpr int GU_ROWS = I / kG;            // gate/up rows per workgroup and slot
+  static constexpr int SEG_D = I * BITS / 128;      // segments per down row
+  static constexpr int LPR = SEG_D < 64 ? SEG_D : 64;  // lanes per down row
+  static constexpr int RPL = 64 / LPR;              // down rows per wave-wide load
+  static constexpr int NSEGD = SEG_D / LPR;         // segments per lane per down row
+  static constexpr int D_ROWS = H / kG;             // down rows per workgroup
+  static constexpr int D_ROWS_W = D_ROWS / kDownWaves;  // per down wave
+  static constexpr int DLD = D_ROWS_W / RPL;        // down loads per lane per slot
+  static_assert(LSEG >= 1 && SEG_X % 64 == 0, "gate/up row must span a wave");
+  static_assert(GU_ROWS == kGuWaves, "one gate/up row per gate/up wave and slot");
+  static_assert(NSEGD == 1, "one down segment per lane");
+  static_assert(DLD >= 1 && D_ROWS_W % RPL == 0, "down rows must tile the waves");
+  static_assert(RXC >= 1 && RCH % kNR == 0, "router row must span the loading threads");
+  static_assert(SEG_X <= 64 * kGuWaves, "one x segment per gate/up thread");
+};
+
+struct FusedArgs {
+  const uint16_t *x, *router;
+  const uint8_t *experts, *shared;
+  int64_t stride;
+  const int32_t *ids_in;  // given routing (then the router is skipped), or null
+  const float *w_in;
+  int32_t *ids_out;       // optional outputs
+  float *w_out;
+  float *y;
+  Ctrl *ctrl;
+  FCtrl *fc;
+  uint64_t *tags;         // [kGroups][kMaxE]
+  float *hrep;            // [kGroups][K+1][I]
+  int E, has_shared;
+  int64_t off_gq, off_uq, off_dq, off_gsb, off_usb, off_dsb;
+};
+
+// sum_c q_c h_c over one 16-byte segment of down codes, fp32.
+template <int BITS>
+__device__ __forceinline__ float seg_dot_f32(uint4 c, const float *h) {
+  float acc = 0.f;
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int wd = 0; wd < 4; ++wd) {
+    const uint32_t u = w[wd];
+    if (BITS == 4) {
+      const uint32_t lo = u & 0x0F0F0F0Fu, hi = (u >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc = fmaf((float)((lo >> (8 * j)) & 0xFFu), h[8 * wd + 2 * j], acc);
+        acc = fmaf((float)((hi >> (8 * j)) & 0xFFu), h[8 * wd + 2 * j + 1], acc);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t m = (u >> (2 * k)) & 0x03030303u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc = fmaf((float)((m >> (8 * j)) & 0xFFu), h[16 * wd + 4 * j + k], acc);
+      }
+    }
+  }
+  return acc;
+}
+
+__device__ __forceinline__ float wave_sum(float v) { return wave_sum64(v); }
+
+// Sum over aligned groups of LPR lanes (16, 32 or 64) without LDS traffic.
+template <int LPR>
+__device__ __forceinline__ float lane_group_sum(float v, int lane) {
+  static_assert(LPR == 16 || LPR == 32 || LPR == 64, "group of 16, 32 or 64 lanes");
+  if (LPR == 16) return row16_sum(v);
+  if (LPR == 32) return half_sum32(v, lane);
+  return wave_sum64(v);
+}
+
+// Bounded wait on a workgroup-local flag written by another wave.
+__device__ __forceinline__ void wait_lds(volatile uint32_t *p, uint32_t want) {
+  long spins = 0;
+  while (*p < want) {
+    if (++spins > (kSpinMax << 4)) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+template <int BITS, int H, int I, int K, int RR>
+__global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
+  using Gm = Geo<BITS, H, I, K>;
+  constexpr int COLS = Gm::COLS, PAIRS = Gm::PAIRS, LSEG = Gm::LSEG;
+  constexpr int NSL = K + 1;  // slot K is the shared expert
+  __shared__ float s_red[kNR / 64][RR];
+  __shared__ uint32_t s_xp[Gm::SEG_X][PAIRS];  // packed x pairs per segment
+  __shared__ float2 s_cx[Gm::SEG_X];           // (1024 * sum of pairs, sum of x)
+  __shared__ float s_hb[NSL][I];               // h of every slot, for the down waves
+  __shared__ int32_t s_ids[K];
+  __shared__ float s_w[K];
+  __shared__ float s_h[NSL][kGuWaves];         // this workgroup's h values
+  __shared__ uint32_t s_cnt[NSL];              // gate/up waves done, per slot
+  __shared__ uint32_t s_hready[NSL];           // s_hb[slot] filled
+  __shared__ uint32_t s_epoch;
+  __shared__ uint32_t s_ready;                 // routing selected
+
+  const int b = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int grp = b % kGroups;
+  const bool routing = a.ids_in == nullptr;
+  constexpr int rr = RR;  // router rows per workgroup (E <= RR * kG)
+
+  // the epoch is read now and published to the workgroup at barrier (A)
+  const uint32_t epoch0 = tid == 0 ? ld_rlx(&a.fc->epoch) + 1u : 0u;
+  if (tid < NSL) {
+    s_cnt[tid] = 0u;
+    s_hready[tid] = 0u;
+  }
+  if (tid == 0) s_ready = 0u;
+
+  // ---- router loads (waves 0..7) -------------------------------------------
+  uint4 rw[RR * Gm::RXC], rx[Gm::RXC];
+  if (routing && wave < kCommWave) {
+#pragma unroll
+    for (int j = 0; j < Gm::RXC; ++j)
+      rx[j] = *reinterpret_cast<const uint4 *>(a.x + (size_t)(tid + kNR * j) * 8);
+#pragma unroll
+    for (int i = 0; i < RR * Gm::RXC; ++i) {
+      const int row = i / Gm::RXC, e = b * rr + row;
+      const int ch = tid + kNR * (i % Gm::RXC);
+      // rows past E read row E-1 and are never published (loads stay
+      // unconditional so the load counter can be tracked statically)
+      const int ec = e < a.E ? e : a.E - 1;
+      rw[i] = *reinterpret_cast<const uint4 *>(a.router + (size_t)ec * H + (size_t)ch * 8);
+    }
+  }
+  auto router_partials = [&]() {
+    float part[RR];
+#pragma unroll
+    for (int row = 0; row < RR; ++row) part[row] = 0.f;
+#pragma unroll
+    for (int i = 0; i < RR * Gm::RXC; ++i) {
+      const uint4 wv = rw[i], xv = rx[i % Gm::RXC];
+      float acc = part[i / Gm::RXC];
+      acc = dot2b(wv.x, xv.x, acc);
+      acc = dot2b(wv.y, xv.y, acc);
+      acc = dot2b(wv.z, xv.z, acc);
+      acc = dot2b(wv.w, xv.w, acc);
+      part[i / Gm::RXC] = acc;
+    }
+#pragma unroll
+    for (int row = 0; row < RR; ++row) {
+      const float v = wave_sum(part[row]);
+      if (lane == 0) s_red[wave][row] = v;
+    }
+  };
+
+  if (wave < kGuWaves) {
+    // ========================= gate/up waves ================================
+    const int r = b * Gm::GU_ROWS + wave;  // this wave's row of every slot
+    const size_t rbytes = (size_t)H * BITS / 8;
+    const int groups = H / kGroup;
+    // x segments to stage (one per thread of the gate/up waves)
+    const int xs = tid;
+    uint4 xr[Gm::XLD];
+#pragma unroll
+    for (int t = 0; t < Gm::XLD; ++t)
+      xr[t] = *reinterpret_cast<const uint4 *>(a.x + (size_t)(xs % Gm::SEG_X) * COLS + 8 * t);
+    uint4 gq[NSL][LSEG], uq[NSL][LSEG];
+    uint32_t gsb[NSL][LSEG], usb[NSL][LSEG];
+    auto load_rows = [&](int slot, const uint8_t *bl) {
+#pragma unroll
+      for (int j = 0; j < LSEG; ++j) {
+        const int sg = lane + 64 * j;
+        gq[slot][j] = ldg16(bl + a.off_gq + r * rbytes + (size_t)sg * 16);
+        uq[slot][j] = ldg16(bl + a.off_uq + r * rbytes + (size_t)sg * 16);
+        gsb[slot][j] = reinterpret_cast<const uint32_t *>(bl + a.off_gsb)[(size_t)r * groups + sg * COLS / kGroup];
+        usb[slot][j] = reinterpret_cast<const uint32_t *>(bl + a.off_usb)[(size_t)r * groups + sg * COLS / kGroup];
+      }
+      // keep the slots' loads in issue order = consumption order (the load
+      // counter completes in order)
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // without a shared expert slot K reads expert 0 and is never used
+    load_rows(K, a.has_shared ? a.shared : a.experts);
+    if (routing) router_partials();
+    // x pairs and per-segment corrections, one code word at a time, to LDS
+    if (xs < Gm::SEG_X) {
+      float C = 0.f, X = 0.f;
+      const uint32_t *xw = reinterpret_cast<const uint32_t *>(&xr[0]);
+#pragma unroll
+      for (int wd = 0; wd < 4; ++wd) {
+        constexpr int CPW = 32 / BITS;  // columns per code word
+        float v[CPW];
+#pragma unroll
+        for (int m = 0; m < CPW / 2; ++m) {
+          const uint32_t pr = xw[wd * CPW / 2 + m];
+          v[2 * m] = bf16f(pr & 0xFFFFu);
+          v[2 * m + 1] = bf16f(pr >> 16);
+        }
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) X += v[c];
+        if (BITS == 4) {
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const float sc = (p & 1) ? 0.0625f : 1.f;
+            const uint32_t pr = pack_h2(v[p] * sc, v[p + 4] * sc);
+            s_xp[xs][4 * wd + p] = pr;
+            C += h2_sum(pr);
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const int e = k < 5 ? k : k - 5;
+            const float sc = 1.f / (float)(1 << (2 * e));
+            const uint32_t pr = pack_h2(v[k] * sc, v[k + 8] * sc);
+            s_xp[xs][8 * wd + k] = pr;
+            C += h2_sum(pr);
+          }
+        }
+      }
+      s_cx[xs] = make_float2(1024.f * C, X);
+    }
+    auto gateup = [&](int slot) -> float {
+      float pg = 0.f, pu = 0.f;
+#pragma unroll
+      for (int j = 0; j < LSEG; ++j) {
+        const int sg = lane + 64 * j;
+        uint32_t xp[PAIRS];
+#pragma unroll
+        for (int p = 0; p < PAIRS; p += 4) {
+          const uint4 q = *reinterpret_cast<const uint4 *>(&s_xp[sg][p]);
+          xp[p] = q.x;
+          xp[p + 1] = q.y;
+          xp[p + 2] = q.z;
+          xp[p + 3] = q.w;
+        }
+        const float2 cx = s_cx[sg];
+        const float ag = seg_dot_x<BITS>(gq[slot][j], xp) - cx.x;
+        const float au = seg_dot_x<BITS>(uq[slot][j], xp) - cx.x;
+        pg += bf16f(gsb[slot][j] & 0xFFFFu) * ag + bf16f(gsb[slot][j] >> 16) * cx.y;
+        pu += bf16f(usb[slot][j] & 0xFFFFu) * au + bf16f(usb[slot][j] >> 16) * cx.y;
+      }
+      pg = wave_sum(pg);
+      pu = wave_sum(pu);
+      return pg / (1.f + expf(-pg)) * pu;
+    };
+    // hand h of (slot, this row) to the comm wave through LDS
+    auto hand_over = [&](int slot, float hv) {
+      if (lane == 0) {
+        s_h[slot][wave] = hv;
+        __hip_atomic_fetch_add(&s_cnt[slot], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+    };
+    if (tid == 0) s_epoch = epoch0;
+    __syncthreads();  // (A) router partials in s_red, x pairs in s_xp, epoch in s_epoch
+    if (a.has_shared) hand_over(K, gateup(K));
+    wait_lds(&s_ready, 1u);
+    int eid[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      eid[k] = s_ids[k];
+      const bool ok = eid[k] >= 0 && eid[k] < a.E;
+      // an invalid id reads expert 0 and contributes 0
+      load_rows(k, a.experts + (size_t)(ok ? eid[k] : 0) * a.stride);
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const bool ok = eid[k] >= 0 && eid[k] < a.E;
+      hand_over(k, ok ? gateup(k) : 0.f);
+    }
+  } else if (wave < kCommWave) {
+    // =========================== down waves =================================
+    const int dw = wave - kGuWaves;
+    const int seg = lane % Gm::LPR;
+    const size_t rbytes = (size_t)I * BITS / 8;
+    const int groups = I / kGroup;
+    int rows[Gm::DLD];
+#pragma unroll
+    for (int ld = 0; ld < Gm::DLD; ++ld)
+      rows[ld] = b * Gm::D_ROWS + dw * Gm::D_ROWS_W + ld * Gm::RPL + lane / Gm::LPR;
+    uint4 dq[NSL][Gm::DLD];
+    uint32_t dsb[NSL][Gm::DLD];
+    auto load_rows = [&](int slot, const uint8_t *bl) {
+#pragma unroll
+      for (int ld = 0; ld < Gm::DLD; ++ld) {
+        dq[slot][ld] = ldg16(bl + a.off_dq + rows[ld] * rbytes + (size_t)seg * 16);
+        dsb[slot][ld] = reinterpret_cast<const uint32_t *>(bl + a.off_dsb)[(size_t)rows[ld] * groups + seg * COLS / kGroup];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    load_rows(K, a.has_shared ? a.shared : a.experts);
+    if (routing) router_partials();
+    __syncthreads();  // (A)
+    const uint32_t epoch = s_epoch;
+
+    float acc[Gm::DLD];
+#pragma unroll
+    for (int ld = 0; ld < Gm::DLD; ++ld) acc[ld] = 0.f;
+    auto down = [&](int slot, float wk) {
+      wait_lds(&s_hready[slot], 1u);
+      float hv[COLS];
+#pragma unroll
+      for (int t = 0; t < COLS / 4; ++t) {
+        const float4 v = *reinterpret_cast<const float4 *>(&s_hb[slot][seg * COLS + 4 * t]);
+        hv[4 * t] = v.x;
+        hv[4 * t + 1] = v.y;
+        hv[4 * t + 2] = v.z;
+        hv[4 * t + 3] = v.w;
+      }
+      float Hs = 0.f;
+#pragma unroll
+      for (int c = 0; c < COLS; ++c) Hs += hv[c];
+#pragma unroll
+      for (int ld = 0; ld < Gm::DLD; ++ld) {
+        const float q = seg_dot_f32<BITS>(dq[slot][ld], hv);
+        const uint32_t sb = dsb[slot][ld];
+        acc[ld] += wk * (bf16f(sb & 0xFFFFu) * q + bf16f(sb >> 16) * Hs);
+      }
+    };
+    wait_lds(&s_ready, 1u);
+    int eid[K];
+    float wk[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      eid[k] = s_ids[k];
+      wk[k] = s_w[k];
+      const bool ok = eid[k] >= 0 && eid[k] < a.E;
+      load_rows(k, a.experts + (size_t)(ok ? eid[k] : 0) * a.stride);
+    }
+    if (a.has_shared) down(K, 1.f);
+#pragma unroll
+    for (int k = 0; k < K; ++k) down(k, (eid[k] >= 0 && eid[k] < a.E) ? wk[k] : 0.f);
+#pragma unroll
+    for (int ld = 0; ld < Gm::DLD; ++ld) {
+      const float v = lane_group_sum<Gm::LPR>(acc[ld], lane);
+      if (seg == 0) a.y[rows[ld]] = v;
+    }
+    // every workgroup has published every slot, so all have passed barrier
+    // (A), where they read the epoch
+    if (b == 0 && dw == 0 && lane == 0)
+      __hip_atomic_store(&a.fc->epoch, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    // ============================ comm wave ==================================
+    __syncthreads();  // (A)
+    const uint32_t epoch = s_epoch;
+    const uint64_t *tags_mine = a.tags + (size_t)grp * kMaxE;  // this group's copy
+    const float *hrep_mine = a.hrep + (size_t)grp * NSL * I;
+    // 0. this workgroup's logits, one copy per reader group
+    if (routing && lane < kGroups * rr) {
+      const int rep = lane / rr, row = lane % rr, e = b * rr + row;
+      if (e < a.E) {
+        float l = 0.f;
+#pragma unroll
+        for (int w = 0; w < kNR / 64; ++w) l += s_red[w][row];
+        const uint64_t v = ((uint64_t)epoch << 32) | (uint64_t)__float_as_uint(l);
+        __hip_atomic_store(&a.tags[(size_t)rep * kMaxE + e], v, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    // publish this workgroup's h of `slot` (one copy per reader group), then
+    // count the workgroup in; the last workgroup of the group raises the
+    // group's flag in every reader group's flag line
+    auto publish = [&](int slot) {
+      if (lane < kGroups * kGuWaves) {
+        const int rep = lane / kGuWaves, row = lane % kGuWaves;
+        __hip_atomic_store(&a.hrep[((size_t)rep * NSL + slot) * I + b * Gm::GU_ROWS + row],
+                           s_h[slot][row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      wait_stores();
+      uint32_t last = 0;
+      if (lane == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(&a.fc->cnt[slot][grp][0], 1u,
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = (old & (kG / kGroups - 1)) == kG / kGroups - 1;
+      }
+      last = __builtin_amdgcn_readfirstlane(last);
+      if (last && lane < kGroups)
+        __hip_atomic_store(&a.fc->rflag[lane][slot][grp], epoch, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    };
+    // are all groups' flags of `slot` up (as seen in this group's flag line)?
+    auto slot_complete = [&](int slot) -> bool {
+      const uint32_t f = lane < kGroups ? ld_rlx(&a.fc->rflag[grp][slot][lane]) : epoch;
+      return __all((int32_t)(f - epoch) >= 0);
+    };
+    // copy h of `slot` from this group's copy into LDS for the down waves
+    auto consume = [&](int slot) {
+      const uint32_t base = (uint32_t)(slot * I * 4);
+#pragma unroll
+      for (int t = 0; t < I / 256; ++t) {
+        const uint4 v = ld_coh16(hrep_mine, base + (uint32_t)(t * 256 + lane * 4) * 4);
+        *reinterpret_cast<uint4 *>(&s_hb[slot][t * 256 + lane * 4]) = v;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      if (lane == 0) s_hready[slot] = 1u;
+    };
+
+    // 1. the shared expert's h is ready first
+    if (a.has_shared) {
+      wait_lds(&s_cnt[K], (uint32_t)kGuWaves);
+      publish(K);
+    }
+    // 2. routing: wait for every workgroup's tagged logits in this group's
+    //    copy, select the top-K.  Lane l holds experts 128 i + 2 l + {0, 1}.
+    if (routing) {
+      constexpr int NV = kMaxE / 64;
+      float v[NV];
+      long spins = 0;
+      while (true) {
+        bool ok = true;
+#pragma unroll
+        for (int i = 0; i < NV / 2; ++i) {
+          const int idx = 128 * i + 2 * lane;
+          if (idx < a.E) {
+            const uint4 t = ld_coh16(tags_mine, (uint32_t)idx * 8u);
+            ok &= t.y == epoch && (idx + 1 >= a.E || t.w == epoch);
+            v[2 * i] = __uint_as_float(t.x);
+            v[2 * i + 1] = idx + 1 < a.E ? __uint_as_float(t.z) : __builtin_nanf("");
+          } else {
+            v[2 * i] = v[2 * i + 1] = __builtin_nanf("");
+          }
+        }
+        if (__all(ok)) break;
+        if (++spins > kSpinMax) {
+          if (lane == 0) atomicOr(&a.ctrl->err, 2u);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      // key = (order-preserving logit bits, ~index): the largest key is the
+      // largest logit, and among equal logits the lowest index
+      uint64_t key[NV];
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const uint32_t idx = 128u * (j / 2) + 2u * lane + (j & 1);
+        key[j] = ((uint64_t)f32_order_key(v[j]) << 32) | (0xFFFFFFFFu - idx);
+      }
+      float sel_v[K];
+      int sel_i[K];
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        uint64_t best = 0;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) best = key[j] > best ? key[j] : best;
+        const uint64_t m = wave_max_u64(best);
+        const uint32_t k32 = (uint32_t)(m >> 32);
+        sel_i[k] = (int)(0xFFFFFFFFu - (uint32_t)m);
+        sel_v[k] = __uint_as_float((k32 & 0x80000000u) ? (k32 & 0x7FFFFFFFu) : ~k32);
+        if (m == 0) sel_i[k] = -1;  // fewer than K finite logits
+#pragma unroll
+        for (int j = 0; j < NV; ++j) key[j] = key[j] == m ? 0 : key[j];
+      }
+      if (lane == 0) {
+        float den = 0.f, p[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          p[k] = expf(sel_v[k] - sel_v[0]);
+          den += p[k];
+        }
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          s_ids[k] = sel_i[k];
+          s_w[k] = p[k] / den;
+          if (b == 0 && a.ids_out) {
+            a.ids_out[k] = sel_i[k];
+            a.w_out[k] = p[k] / den;
+          }
+        }
+      }
+    } else if (lane < K) {
+      const int e = a.ids_in[lane];
+      s_ids[lane] = e;
+      s_w[lane] = a.w_in[lane];
+      if ((e < 0 || e >= a.E) && b == 0) atomicOr(&a.ctrl->err, 1u);
+    }
+    if (lane == 0)
+      __hip_atomic_store(&s_ready, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    // 3. publish the routed slots as the gate/up waves finish them, and copy
+    //    every slot's complete h into LDS as soon as all groups published it.
+    //    Consumption order: shared, then routed slots 0..K-1; a slot is
+    //    consumed only after this workgroup has published it.
+    const int nslots = K + a.has_shared;
+    int p = 0, c = 0;
+    long spins = 0;
+    volatile uint32_t *vcnt = s_cnt;
+    while (p < K || c < nslots) {
+      if (p < K && vcnt[p] >= (uint32_t)kGuWaves) {
+        publish(p);
+        ++p;
+        continue;
+      }
+      if (c < nslots) {
+        const int slot = a.has_shared ? (c == 0 ? K : c - 1) : c;
+        if ((slot == K || slot < p) && slot_complete(slot)) {
+          consume(slot);
+          ++c;
+          continue;
+        }
+      }
+      if (++spins > kSpinMax) {
+        if (lane == 0) atomicOr(&a.ctrl->err, 2u);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+}
+
+inline hipStream_t S(void *s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+// Returns true if the fused single-token kernel covers these dims.
+bool fused_supported(const moe_dims &d) {
+  static int ncu = -1;
+  if (ncu < 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      ncu = 0;
+  }
+  return ncu == kG && d.hidden == 4096 && d.inter == 1024 && d.top_k == 4 &&
+         (d.bits == 4 || d.bits == 2);
+}
+
+int launch_layer_fused(const moe_dims &d, const moe_layer &L, const uint16_t *x,
+                       const int32_t *ids_in, const float *w_in, int32_t *ids_out,
+                       float *w_out, float *y, void *ws, void *stream) {
+  const WsLayout W = ws_layout(d, 1);
+  const BlobLayout B = blob_layout(d);
+  uint8_t *base = static_cast<uint8_t *>(ws);
+  FusedArgs a;
+  a.x = x;
+  a.router = L.router;
+  a.experts = L.experts;
+  a.shared = L.shared;
+  a.stride = L.expert_stride;
+  a.ids_in = ids_in;
+  a.w_in = w_in;
+  a.ids_out = ids_out;
+  a.w_out = w_out;
+  a.y = y;
+  a.ctrl = reinterpret_cast<Ctrl *>(base + W.ctrl);
+  a.fc = reinterpret_cast<FCtrl *>(base + W.fctrl);
+  a.tags = reinterpret_cast<uint64_t *>(base + W.logits_tag);
+  a.hrep = reinterpret_cast<float *>(base + W.hrep);
+  a.E = d.n_experts;
+  a.has_shared = d.has_shared;
+  a.off_gq = (int64_t)B.off[MOE_SEC_GATE_Q];
+  a.off_uq = (int64_t)B.off[MOE_SEC_UP_Q];
+  a.off_dq = (int64_t)B.off[MOE_SEC_DOWN_Q];
+  a.off_gsb = (int64_t)B.off[MOE_SEC_GATE_SB];
+  a.off_usb = (int64_t)B.off[MOE_SEC_UP_SB];
+  a.off_dsb = (int64_t)B.off[MOE_SEC_DOWN_SB];
+  const int rr = (d.n_experts + kG - 1) / kG;
+#define MOE_LAUNCH_L1(B, R) \
+  hipLaunchKernelGGL((k_layer1<B, 4096, 1024, 4, R>), dim3(kG), dim3(kNT), 0, S(stream), a)
+  if (d.bits == 4) {
+    if (rr == 1) MOE_LAUNCH_L1(4, 1);
+    else if (rr == 2) MOE_LAUNCH_L1(4, 2);
+    else MOE_LAUNCH_L1(4, 4);
+  } else {
+    if (rr == 1) MOE_LAUNCH_L1(2, 1);
+    else if (rr == 2) MOE_LAUNCH_L1(2, 2);
+    else MOE_LAUNCH_L1(2, 4);
+  }
+#undef MOE_LAUNCH_L1
+  return (int)hipGetLastError();
+}
+
+}  // namespace moe

@@ -3,6 +3,7 @@
 // pure host code and runs before anything is enqueued, so every error path
 // is testable without a GPU.
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "moe_internal.h"
@@ -35,9 +36,10 @@ BlobLayout blob_layout(const moe_dims &d) {
 WsLayout ws_layout(const moe_dims &d, int T) {
   WsLayout W;
   const size_t slots = (size_t)d.top_k + (size_t)d.has_shared;
-  size_t o = 0;
-  W.ctrl = o;
-  o = align_up(o + sizeof(Ctrl), kAlign);
+  W.ctrl = kCtrlOff;
+  W.fctrl = kFCtrlOff;
+  W.logits_tag = kTagOff;
+  size_t o = align_up(kHeaderBytes, kAlign);
   W.logits = o;
   o = align_up(o + (size_t)T * d.n_experts * 4, kAlign);
   W.ids = o;
@@ -46,6 +48,8 @@ WsLayout ws_layout(const moe_dims &d, int T) {
   o = align_up(o + (size_t)T * d.top_k * 4, kAlign);
   W.h = o;
   o = align_up(o + (size_t)T * slots * d.inter * 4, kAlign);
+  W.hrep = o;  // always K+1 slots: the single-token kernel indexes the shared slot as K
+  o = align_up(o + (size_t)kGroups * (d.top_k + 1) * d.inter * 4, kAlign);
   W.total = o;
   return W;
 }
@@ -78,6 +82,18 @@ static moe_status check_ws(const moe_dims *d, int T, const void *ws, size_t ws_b
   if (!aligned(ws, kAlign)) return MOE_ERR_ALIGN;
   if (ws_bytes < ws_layout(*d, T).total) return MOE_ERR_WORKSPACE;
   return MOE_OK;
+}
+
+// The single-token fused kernel is used when it covers the dims; setting
+// MOE_DISABLE_FUSED=1 in the environment selects the three-kernel path
+// (used to compare the two).
+static bool use_fused(const moe_dims &d, int T) {
+  static int disabled = -1;
+  if (disabled < 0) {
+    const char *e = getenv("MOE_DISABLE_FUSED");
+    disabled = (e && e[0] == '1') ? 1 : 0;
+  }
+  return T == 1 && !disabled && fused_supported(d);
 }
 
 static moe_status check_T(int T) { return (T < 1 || T > kMaxT) ? MOE_ERR_SHAPE : MOE_OK; }
@@ -133,7 +149,7 @@ size_t moe_workspace_bytes(const moe_dims *dims, int32_t T) {
 moe_status moe_workspace_init(void *ws, size_t ws_bytes, void *stream) {
   if (!ws) return MOE_ERR_NULL;
   if (!aligned(ws, kAlign)) return MOE_ERR_ALIGN;
-  if (ws_bytes < sizeof(Ctrl)) return MOE_ERR_WORKSPACE;
+  if (ws_bytes < kHeaderBytes) return MOE_ERR_WORKSPACE;
   return launch_ws_init(ws, ws_bytes, stream) == 0 ? MOE_OK : MOE_ERR_HIP;
 }
 
@@ -161,6 +177,10 @@ moe_status moe_expert_forward(const moe_dims *dims, const moe_layer *layer, cons
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ids, 4) || !aligned(w, 4))
     return MOE_ERR_ALIGN;
   MOE_TRY(check_ws(dims, T, ws, ws_bytes));
+  if (use_fused(*dims, T))
+    return launch_layer_fused(*dims, *layer, x, ids, w, nullptr, nullptr, y, ws, stream) == 0
+               ? MOE_OK
+               : MOE_ERR_HIP;
   return launch_expert_forward(*dims, *layer, x, T, ids, w, y, ws, stream) == 0 ? MOE_OK
                                                                                 : MOE_ERR_HIP;
 }
@@ -175,6 +195,12 @@ moe_status moe_layer_decode(const moe_dims *dims, const moe_layer *layer, const 
   if (!aligned(x, 16) || !aligned(y, 16) || (ids && !aligned(ids, 4)) || (w && !aligned(w, 4)))
     return MOE_ERR_ALIGN;
   MOE_TRY(check_ws(dims, T, ws, ws_bytes));
+  if (!layer->router) return MOE_ERR_NULL;
+  if (!aligned(layer->router, 16)) return MOE_ERR_ALIGN;
+  if (use_fused(*dims, T))
+    return launch_layer_fused(*dims, *layer, x, nullptr, nullptr, ids, w, y, ws, stream) == 0
+               ? MOE_OK
+               : MOE_ERR_HIP;
   const WsLayout W = ws_layout(*dims, T);
   uint8_t *base = static_cast<uint8_t *>(ws);
   int32_t *ids_d = ids ? ids : reinterpret_cast<int32_t *>(base + W.ids);

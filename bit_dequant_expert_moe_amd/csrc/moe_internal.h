@@ -23,12 +23,17 @@ struct BlobLayout {
 };
 BlobLayout blob_layout(const moe_dims &d);
 
-// Workspace map (byte offsets from the workspace base).
-//   ctrl    : 256 bytes of control words (see Ctrl)
-//   logits  : fp32 [T][E]
-//   ids     : int32 [T][K]
-//   w       : fp32 [T][K]
-//   h       : fp32 [T][K+1][I]   activations silu(g)*u per slot
+// Workspace map (byte offsets from the workspace base).  The first
+// kHeaderBytes hold control words and are zeroed by moe_workspace_init:
+//   ctrl       : Ctrl (256 bytes)
+//   fctrl      : FCtrl, synchronisation words of the fused single-token kernel
+//   logits_tag : uint64 [kGroups][kMaxE]  (fp32 logit bits | epoch << 32)
+// then, not initialised:
+//   logits     : fp32 [T][E]
+//   ids        : int32 [T][K]
+//   w          : fp32 [T][K]
+//   h          : fp32 [T][K+1][I]   activations silu(g)*u per slot
+//   hrep       : fp32 [kGroups][K+1][I]   copies of h for the single-token kernel
 struct Ctrl {
   uint32_t route_counter;  // blocks of the routing kernel that finished
   uint32_t err;            // sticky device error flags
@@ -36,8 +41,25 @@ struct Ctrl {
 };
 static_assert(sizeof(Ctrl) == 256, "control block is 256 bytes");
 
+constexpr int kGroups = 8;  // workgroup groups by blockIdx % 8 (one per XCD)
+// Every datum that all workgroups read is stored once per reader group, so
+// that each cache line has ~32 readers instead of 256 (coherent reads of one
+// line from every CU serialise at its memory channel).
+struct FCtrl {
+  uint32_t epoch;                                   // calls completed on this workspace
+  uint32_t pad0[31];
+  uint32_t cnt[kMaxK + 1][kGroups][32];             // arrivals per slot and group (own line)
+  uint32_t rflag[kGroups][kMaxK + 1][kGroups];      // [reader group][slot][source group] = epoch
+};
+
+constexpr size_t kCtrlOff = 0;
+constexpr size_t kFCtrlOff = 256;
+constexpr size_t kTagOff = kFCtrlOff + ((sizeof(FCtrl) + 255) / 256) * 256;
+// tagged logits, one copy per reader group: uint64 [kGroups][kMaxE]
+constexpr size_t kHeaderBytes = kTagOff + (size_t)kGroups * kMaxE * 8;
+
 struct WsLayout {
-  size_t ctrl, logits, ids, w, h, total;
+  size_t ctrl, fctrl, logits_tag, logits, ids, w, h, hrep, total;
 };
 WsLayout ws_layout(const moe_dims &d, int T);
 
@@ -65,6 +87,10 @@ int launch_route(const moe_dims &d, const uint16_t *router, const uint16_t *x, i
 int launch_expert_forward(const moe_dims &d, const moe_layer &L, const uint16_t *x, int T,
                           const int32_t *ids, const float *w, float *y, void *ws,
                           void *stream);
+bool fused_supported(const moe_dims &d);
+int launch_layer_fused(const moe_dims &d, const moe_layer &L, const uint16_t *x,
+                       const int32_t *ids_in, const float *w_in, int32_t *ids_out,
+                       float *w_out, float *y, void *ws, void *stream);
 int launch_dequantize(const moe_dims &d, const uint8_t *blob, int which, float *out,
                       void *stream);
 int read_device_error(void *ws, void *stream, int32_t *err);

@@ -30,145 +30,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "moe_device.h"
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
-
-typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float bf16f(uint32_t b16) { return __uint_as_float(b16 << 16); }
-
-// fp32 -> bf16 bits, round to nearest even (finite values).
-__device__ __forceinline__ uint32_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-__device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
-  h2_t v;
-  v.x = (_Float16)lo;
-  v.y = (_Float16)hi;
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-__device__ __forceinline__ float h2_sum(uint32_t p) {
-  h2_t v = __builtin_bit_cast(h2_t, p);
-  return (float)v.x + (float)v.y;
-}
-
-// (w & m) | c in one VALU op (the compiler would otherwise emit AND and OR
-// with two literal operands).
-__device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t m, uint32_t c) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "s"(m), "v"(c));
-  return r;
-}
-
-__device__ __forceinline__ float dot2h(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, a), __builtin_bit_cast(h2_t, b), c,
-                                false);
-}
-
-__device__ __forceinline__ float dot2b(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2_t, a),
-                                         __builtin_bit_cast(b2_t, b), c, false);
-}
-
-// Sum over aligned groups of `width` lanes (power of two <= 64).
-__device__ __forceinline__ float group_sum(float v, int width) {
-  for (int off = width >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
-
-__device__ __forceinline__ uint4 ldg16(const uint8_t *p) {
-  return *reinterpret_cast<const uint4 *>(p);
-}
-
-constexpr uint32_t kMagicH = 0x64006400u;  // fp16 pair (1024, 1024)
-constexpr uint32_t kMagicB = 0x43004300u;  // bf16 pair (128, 128)
-
-// ---------------------------------------------------------------------------
-// x staging for the gate/up GEMV.  For each 16-byte code segment of a row
-// (32 codes at 4 bits, 64 at 2 bits) the LDS holds the packed fp16 x pairs in
-// the order the unpack produces them, plus two floats:
-//   C = 1024 * (sum of the fp16 values of the pairs)   (removes the magic)
-//   X = sum of x over the segment's columns            (bias term)
-// ---------------------------------------------------------------------------
-template <int BITS>
-struct XSeg {
-  static constexpr int kCols = 128 / BITS;      // columns per segment
-  static constexpr int kPairs = kCols / 2;      // packed pairs per segment
-};
-
-template <int BITS>
-__device__ void stage_x(const uint16_t *__restrict__ x, int H, uint32_t *xp, float2 *cx) {
-  constexpr int kCols = XSeg<BITS>::kCols, kPairs = XSeg<BITS>::kPairs;
-  const int nseg = H / kCols;
-  for (int sg = threadIdx.x; sg < nseg; sg += blockDim.x) {
-    const uint16_t *xs = x + sg * kCols;
-    float C = 0.f, X = 0.f;
-    for (int wd = 0; wd < 4; ++wd) {
-      if (BITS == 4) {
-        // word wd holds codes 8wd .. 8wd+7; pairs (0,4) (1,5)/16 (2,6) (3,7)/16
-        float v[8];
-        for (int j = 0; j < 8; ++j) v[j] = bf16f(xs[8 * wd + j]);
-        for (int j = 0; j < 8; ++j) X += v[j];
-        const float sc[4] = {1.f, 0.0625f, 1.f, 0.0625f};
-        for (int p = 0; p < 4; ++p) {
-          uint32_t pr = pack_h2(v[p] * sc[p], v[p + 4] * sc[p]);
-          xp[sg * kPairs + 4 * wd + p] = pr;
-          C += h2_sum(pr);
-        }
-      } else {
-        // word wd holds codes 16wd .. 16wd+15; pair k = (k, k+8) scaled by
-        // 4^-k (k < 5) or 4^-(k-5) (k >= 5, taken from the word shifted by 10)
-        float v[16];
-        for (int j = 0; j < 16; ++j) v[j] = bf16f(xs[16 * wd + j]);
-        for (int j = 0; j < 16; ++j) X += v[j];
-        for (int k = 0; k < 8; ++k) {
-          const int e = k < 5 ? k : k - 5;
-          const float sc = 1.f / (float)(1 << (2 * e));
-          uint32_t pr = pack_h2(v[k] * sc, v[k + 8] * sc);
-          xp[sg * kPairs + 8 * wd + k] = pr;
-          C += h2_sum(pr);
-        }
-      }
-    }
-    cx[sg] = make_float2(1024.f * C, X);
-  }
-}
-
-// sum_c (magic_c + q_c) * xtilde_c over one 16-byte segment.
-template <int BITS>
-__device__ __forceinline__ float seg_dot_x(uint4 c, const uint32_t *xp) {
-  const uint32_t M = kMagicH;
-  float acc = 0.f;
-  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-  for (int wd = 0; wd < 4; ++wd) {
-    const uint32_t u = w[wd];
-    if (BITS == 4) {
-      const uint32_t u8 = u >> 8;
-      acc = dot2h(and_or(u, 0x000F000Fu, M), xp[4 * wd + 0], acc);
-      acc = dot2h(and_or(u, 0x00F000F0u, M), xp[4 * wd + 1], acc);
-      acc = dot2h(and_or(u8, 0x000F000Fu, M), xp[4 * wd + 2], acc);
-      acc = dot2h(and_or(u8, 0x00F000F0u, M), xp[4 * wd + 3], acc);
-    } else {
-      const uint32_t u10 = u >> 10;
-      acc = dot2h(and_or(u, 0x00030003u, M), xp[8 * wd + 0], acc);
-      acc = dot2h(and_or(u, 0x000C000Cu, M), xp[8 * wd + 1], acc);
-      acc = dot2h(and_or(u, 0x00300030u, M), xp[8 * wd + 2], acc);
-      acc = dot2h(and_or(u, 0x00C000C0u, M), xp[8 * wd + 3], acc);
-      acc = dot2h(and_or(u, 0x03000300u, M), xp[8 * wd + 4], acc);
-      acc = dot2h(and_or(u10, 0x00030003u, M), xp[8 * wd + 5], acc);
-      acc = dot2h(and_or(u10, 0x000C000Cu, M), xp[8 * wd + 6], acc);
-      acc = dot2h(and_or(u10, 0x00300030u, M), xp[8 * wd + 7], acc);
-    }
-  }
-  return acc;
-}
+using namespace dev;
 
 // ---------------------------------------------------------------------------
 // h staging for the down GEMV: per segment of I (32 or 64 activations) the
@@ -545,8 +412,8 @@ int allow_lds(F f, size_t bytes) {
 // Launchers
 // ---------------------------------------------------------------------------
 int launch_ws_init(void *ws, size_t, void *stream) {
-  hipLaunchKernelGGL(k_ws_init, dim3(1), dim3(64), 0, S(stream), static_cast<uint32_t *>(ws),
-                     (int)(sizeof(Ctrl) / 4));
+  hipLaunchKernelGGL(k_ws_init, dim3(1), dim3(256), 0, S(stream), static_cast<uint32_t *>(ws),
+                     (int)(kHeaderBytes / 4));
   return (int)hipGetLastError();
 }
 
