@@ -62,16 +62,15 @@ constexpr long kSpinMax = 1L << 18;
 
 // Cross-workgroup data goes through agent-scope relaxed atomics, which the
 // gfx950 memory model implements as coherent (sc1) loads and stores; no
-// cache writeback or invalidate is issued.  Ordering between a workgroup's
-// data and its signal is given by waiting for the data stores to complete
-// (s_waitcnt vmcnt(0)) in the comm wave, which has no weight loads in flight.
+// cache writeback or invalidate is issued.  Every exchanged word carries the
+// epoch of its call, so no separate signal (and no ordering between data and
+// signal) is needed.
 __device__ __forceinline__ uint32_t ld_rlx(const uint32_t *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint64_t ld_rlx64(const uint64_t *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // 16-byte coherent load (buffer_load_dwordx4 with the sc1 policy, the same
 // policy as an agent-scope relaxed atomic load), coalesced across the wave.
@@ -118,8 +117,8 @@ struct FusedArgs {
   float *y;
   Ctrl *ctrl;
   FCtrl *fc;
-  uint64_t *tags;         // [kGroups][kMaxE]
-  float *hrep;            // [kGroups][K+1][I]
+  uint64_t *tags;         // [kGroups][kMaxE] tagged logits
+  uint64_t *htag;         // [kGroups][K+1][I] tagged activations
   int E, has_shared;
   int64_t off_gq, off_uq, off_dq, off_gsb, off_usb, off_dsb;
 };
@@ -177,6 +176,7 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
   using Gm = Geo<BITS, H, I, K>;
   constexpr int COLS = Gm::COLS, PAIRS = Gm::PAIRS, LSEG = Gm::LSEG;
   constexpr int NSL = K + 1;  // slot K is the shared expert
+  static_assert(NSL == kFusedSlots && I == kFusedI, "tagged activations are sized for these");
   __shared__ float s_red[kNR / 64][RR];
   __shared__ uint32_t s_xp[Gm::SEG_X][PAIRS];  // packed x pairs per segment
   __shared__ float2 s_cx[Gm::SEG_X];           // (1024 * sum of pairs, sum of x)
@@ -188,6 +188,7 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
   __shared__ uint32_t s_hready[NSL];           // s_hb[slot] filled
   __shared__ uint32_t s_epoch;
   __shared__ uint32_t s_ready;                 // routing selected
+  __shared__ uint32_t s_dissued;               // down waves that issued their routed loads
 
   const int b = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int grp = b % kGroups;
@@ -200,7 +201,10 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
     s_cnt[tid] = 0u;
     s_hready[tid] = 0u;
   }
-  if (tid == 0) s_ready = 0u;
+  if (tid == 0) {
+    s_ready = 0u;
+    s_dissued = 0u;
+  }
 
   // ---- router loads (waves 0..7) -------------------------------------------
   uint4 rw[RR * Gm::RXC], rx[Gm::RXC];
@@ -340,6 +344,10 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
     __syncthreads();  // (A) router partials in s_red, x pairs in s_xp, epoch in s_epoch
     if (a.has_shared) hand_over(K, gateup(K));
     wait_lds(&s_ready, 1u);
+    // the down waves' routed loads go first: they are needed last, and the
+    // activations of the last slot, exchanged at the end of the stream, then
+    // do not queue behind them
+    wait_lds(&s_dissued, (uint32_t)kDownWaves);
     int eid[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) {
@@ -412,6 +420,7 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
       const bool ok = eid[k] >= 0 && eid[k] < a.E;
       load_rows(k, a.experts + (size_t)(ok ? eid[k] : 0) * a.stride);
     }
+    if (lane == 0) atomicAdd(&s_dissued, 1u);
     if (a.has_shared) down(K, 1.f);
 #pragma unroll
     for (int k = 0; k < K; ++k) down(k, (eid[k] >= 0 && eid[k] < a.E) ? wk[k] : 0.f);
@@ -429,7 +438,6 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
     __syncthreads();  // (A)
     const uint32_t epoch = s_epoch;
     const uint64_t *tags_mine = a.tags + (size_t)grp * kMaxE;  // this group's copy
-    const float *hrep_mine = a.hrep + (size_t)grp * NSL * I;
     // 0. this workgroup's logits, one copy per reader group
     if (routing && lane < kGroups * rr) {
       const int rep = lane / rr, row = lane % rr, e = b * rr + row;
@@ -442,42 +450,34 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
                            __HIP_MEMORY_SCOPE_AGENT);
       }
     }
-    // publish this workgroup's h of `slot` (one copy per reader group), then
-    // count the workgroup in; the last workgroup of the group raises the
-    // group's flag in every reader group's flag line
+    // publish this workgroup's h of `slot`: one tagged copy per reader group
     auto publish = [&](int slot) {
       if (lane < kGroups * kGuWaves) {
         const int rep = lane / kGuWaves, row = lane % kGuWaves;
-        __hip_atomic_store(&a.hrep[((size_t)rep * NSL + slot) * I + b * Gm::GU_ROWS + row],
-                           s_h[slot][row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t v = ((uint64_t)epoch << 32) | (uint64_t)__float_as_uint(s_h[slot][row]);
+        __hip_atomic_store(&a.htag[((size_t)rep * NSL + slot) * I + b * Gm::GU_ROWS + row], v,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      wait_stores();
-      uint32_t last = 0;
-      if (lane == 0) {
-        const uint32_t old = __hip_atomic_fetch_add(&a.fc->cnt[slot][grp][0], 1u,
-                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        last = (old & (kG / kGroups - 1)) == kG / kGroups - 1;
-      }
-      last = __builtin_amdgcn_readfirstlane(last);
-      if (last && lane < kGroups)
-        __hip_atomic_store(&a.fc->rflag[lane][slot][grp], epoch, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
     };
-    // are all groups' flags of `slot` up (as seen in this group's flag line)?
-    auto slot_complete = [&](int slot) -> bool {
-      const uint32_t f = lane < kGroups ? ld_rlx(&a.fc->rflag[grp][slot][lane]) : epoch;
-      return __all((int32_t)(f - epoch) >= 0);
-    };
-    // copy h of `slot` from this group's copy into LDS for the down waves
-    auto consume = [&](int slot) {
-      const uint32_t base = (uint32_t)(slot * I * 4);
+    // read this group's copy of `slot`; if every entry carries the current
+    // epoch, move the values to LDS for the down waves and return true
+    auto try_consume = [&](int slot) -> bool {
+      constexpr int NLD = I / 128;  // 16-byte loads per lane (two entries each)
+      uint4 t[NLD];
+      const uint32_t base = (uint32_t)(((size_t)grp * NSL + slot) * I * 8);
 #pragma unroll
-      for (int t = 0; t < I / 256; ++t) {
-        const uint4 v = ld_coh16(hrep_mine, base + (uint32_t)(t * 256 + lane * 4) * 4);
-        *reinterpret_cast<uint4 *>(&s_hb[slot][t * 256 + lane * 4]) = v;
-      }
+      for (int i = 0; i < NLD; ++i) t[i] = ld_coh16(a.htag, base + (uint32_t)(128 * i + 2 * lane) * 8u);
+      bool ok = true;
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) ok &= t[i].y == epoch && t[i].w == epoch;
+      if (!__all(ok)) return false;
+#pragma unroll
+      for (int i = 0; i < NLD; ++i)
+        *reinterpret_cast<float2 *>(&s_hb[slot][128 * i + 2 * lane]) =
+            make_float2(__uint_as_float(t[i].x), __uint_as_float(t[i].z));
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
       if (lane == 0) s_hready[slot] = 1u;
+      return true;
     };
 
     // 1. the shared expert's h is ready first
@@ -485,6 +485,7 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
       wait_lds(&s_cnt[K], (uint32_t)kGuWaves);
       publish(K);
     }
+    const uint64_t *tags_copy = tags_mine;
     // 2. routing: wait for every workgroup's tagged logits in this group's
     //    copy, select the top-K.  Lane l holds experts 128 i + 2 l + {0, 1}.
     if (routing) {
@@ -497,7 +498,7 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
         for (int i = 0; i < NV / 2; ++i) {
           const int idx = 128 * i + 2 * lane;
           if (idx < a.E) {
-            const uint4 t = ld_coh16(tags_mine, (uint32_t)idx * 8u);
+            const uint4 t = ld_coh16(tags_copy, (uint32_t)idx * 8u);
             ok &= t.y == epoch && (idx + 1 >= a.E || t.w == epoch);
             v[2 * i] = __uint_as_float(t.x);
             v[2 * i + 1] = idx + 1 < a.E ? __uint_as_float(t.z) : __builtin_nanf("");
@@ -560,10 +561,10 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
     }
     if (lane == 0)
       __hip_atomic_store(&s_ready, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-    // 3. publish the routed slots as the gate/up waves finish them, and copy
-    //    every slot's complete h into LDS as soon as all groups published it.
+    // 3. publish the routed slots as the gate/up waves finish them, and move
+    //    every slot's complete h into LDS once all workgroups published it.
     //    Consumption order: shared, then routed slots 0..K-1; a slot is
-    //    consumed only after this workgroup has published it.
+    //    polled only after this workgroup has published it.
     const int nslots = K + a.has_shared;
     int p = 0, c = 0;
     long spins = 0;
@@ -576,8 +577,7 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
       }
       if (c < nslots) {
         const int slot = a.has_shared ? (c == 0 ? K : c - 1) : c;
-        if ((slot == K || slot < p) && slot_complete(slot)) {
-          consume(slot);
+        if ((slot == K || slot < p) && try_consume(slot)) {
           ++c;
           continue;
         }
@@ -628,7 +628,7 @@ int launch_layer_fused(const moe_dims &d, const moe_layer &L, const uint16_t *x,
   a.ctrl = reinterpret_cast<Ctrl *>(base + W.ctrl);
   a.fc = reinterpret_cast<FCtrl *>(base + W.fctrl);
   a.tags = reinterpret_cast<uint64_t *>(base + W.logits_tag);
-  a.hrep = reinterpret_cast<float *>(base + W.hrep);
+  a.htag = reinterpret_cast<uint64_t *>(base + W.h_tag);
   a.E = d.n_experts;
   a.has_shared = d.has_shared;
   a.off_gq = (int64_t)B.off[MOE_SEC_GATE_Q];

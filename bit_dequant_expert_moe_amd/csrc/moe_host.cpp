@@ -39,6 +39,7 @@ WsLayout ws_layout(const moe_dims &d, int T) {
   W.ctrl = kCtrlOff;
   W.fctrl = kFCtrlOff;
   W.logits_tag = kTagOff;
+  W.h_tag = kHTagOff;
   size_t o = align_up(kHeaderBytes, kAlign);
   W.logits = o;
   o = align_up(o + (size_t)T * d.n_experts * 4, kAlign);
@@ -48,8 +49,6 @@ WsLayout ws_layout(const moe_dims &d, int T) {
   o = align_up(o + (size_t)T * d.top_k * 4, kAlign);
   W.h = o;
   o = align_up(o + (size_t)T * slots * d.inter * 4, kAlign);
-  W.hrep = o;  // always K+1 slots: the single-token kernel indexes the shared slot as K
-  o = align_up(o + (size_t)kGroups * (d.top_k + 1) * d.inter * 4, kAlign);
   W.total = o;
   return W;
 }

@@ -26,14 +26,14 @@ BlobLayout blob_layout(const moe_dims &d);
 // Workspace map (byte offsets from the workspace base).  The first
 // kHeaderBytes hold control words and are zeroed by moe_workspace_init:
 //   ctrl       : Ctrl (256 bytes)
-//   fctrl      : FCtrl, synchronisation words of the fused single-token kernel
+//   fctrl      : FCtrl (epoch of the fused single-token kernel)
 //   logits_tag : uint64 [kGroups][kMaxE]  (fp32 logit bits | epoch << 32)
+//   h_tag      : uint64 [kGroups][5][1024] (fp32 h bits | epoch << 32)
 // then, not initialised:
 //   logits     : fp32 [T][E]
 //   ids        : int32 [T][K]
 //   w          : fp32 [T][K]
 //   h          : fp32 [T][K+1][I]   activations silu(g)*u per slot
-//   hrep       : fp32 [kGroups][K+1][I]   copies of h for the single-token kernel
 struct Ctrl {
   uint32_t route_counter;  // blocks of the routing kernel that finished
   uint32_t err;            // sticky device error flags
@@ -42,24 +42,29 @@ struct Ctrl {
 static_assert(sizeof(Ctrl) == 256, "control block is 256 bytes");
 
 constexpr int kGroups = 8;  // workgroup groups by blockIdx % 8 (one per XCD)
-// Every datum that all workgroups read is stored once per reader group, so
-// that each cache line has ~32 readers instead of 256 (coherent reads of one
-// line from every CU serialise at its memory channel).
+// Synchronisation state of the fused single-token kernel.  Every datum that
+// all workgroups read is stored once per reader group (kGroups copies), so
+// each cache line has ~32 coherent readers instead of 256 (coherent reads of
+// one line from every CU serialise at its memory channel).  Data words carry
+// the epoch of the call that wrote them in their upper 32 bits, so a reader
+// detects completion from the data itself.
 struct FCtrl {
-  uint32_t epoch;                                   // calls completed on this workspace
-  uint32_t pad0[31];
-  uint32_t cnt[kMaxK + 1][kGroups][32];             // arrivals per slot and group (own line)
-  uint32_t rflag[kGroups][kMaxK + 1][kGroups];      // [reader group][slot][source group] = epoch
+  uint32_t epoch;  // calls completed on this workspace
+  uint32_t pad[63];
 };
+constexpr int kFusedI = 1024;     // intermediate size the fused kernel covers
+constexpr int kFusedSlots = 5;    // top-4 + shared
 
 constexpr size_t kCtrlOff = 0;
 constexpr size_t kFCtrlOff = 256;
-constexpr size_t kTagOff = kFCtrlOff + ((sizeof(FCtrl) + 255) / 256) * 256;
-// tagged logits, one copy per reader group: uint64 [kGroups][kMaxE]
-constexpr size_t kHeaderBytes = kTagOff + (size_t)kGroups * kMaxE * 8;
+// tagged logits: uint64 [kGroups][kMaxE]
+constexpr size_t kTagOff = kFCtrlOff + 256;
+// tagged activations: uint64 [kGroups][kFusedSlots][kFusedI]
+constexpr size_t kHTagOff = kTagOff + (size_t)kGroups * kMaxE * 8;
+constexpr size_t kHeaderBytes = kHTagOff + (size_t)kGroups * kFusedSlots * kFusedI * 8;
 
 struct WsLayout {
-  size_t ctrl, fctrl, logits_tag, logits, ids, w, h, hrep, total;
+  size_t ctrl, fctrl, logits_tag, h_tag, logits, ids, w, h, total;
 };
 WsLayout ws_layout(const moe_dims &d, int T);
 

@@ -389,8 +389,9 @@ __global__ void __launch_bounds__(256) k_dequantize(DequantArgs a) {
   }
 }
 
-__global__ void k_ws_init(uint32_t *ctrl, int n) {
-  for (int i = threadIdx.x; i < n; i += blockDim.x) ctrl[i] = 0u;
+__global__ void k_ws_init(uint4 *ctrl, int n16) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += gridDim.x * blockDim.x)
+    ctrl[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 inline hipStream_t S(void *s) { return static_cast<hipStream_t>(s); }
@@ -412,8 +413,9 @@ int allow_lds(F f, size_t bytes) {
 // Launchers
 // ---------------------------------------------------------------------------
 int launch_ws_init(void *ws, size_t, void *stream) {
-  hipLaunchKernelGGL(k_ws_init, dim3(1), dim3(256), 0, S(stream), static_cast<uint32_t *>(ws),
-                     (int)(kHeaderBytes / 4));
+  static_assert(kHeaderBytes % 16 == 0, "header is a multiple of 16 bytes");
+  hipLaunchKernelGGL(k_ws_init, dim3(64), dim3(256), 0, S(stream), static_cast<uint4 *>(ws),
+                     (int)(kHeaderBytes / 16));
   return (int)hipGetLastError();
 }
 
