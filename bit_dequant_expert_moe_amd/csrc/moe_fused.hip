@@ -8,36 +8,36 @@
 // experts dequantised inside the FMA inner loop.
 //
 // Why one launch: a decode layer moves ~40 MB, about 6 us of HBM time on
-// MI355X, while a dependent kernel boundary costs ~1.7 us and a full
-// device-wide barrier across 256 workgroups ~2.3 us.  This kernel keeps every
-// workgroup resident (one per CU) and replaces the two data dependencies of
-// the layer with cheap one-way signals:
-//   * routing: each workgroup writes its logits as (value, epoch) 64-bit
-//     words; every workgroup polls the E words until all carry the current
-//     epoch, so the data arrives with the signal, then selects the top-K
-//     itself (the selection is deterministic, so all agree);
+// MI355X, while a dependent kernel boundary costs ~1.7 us and a device-wide
+// barrier across 256 workgroups ~2.3 us.  This kernel keeps every workgroup
+// resident (one per CU) and replaces the two data dependencies of the layer
+// with one-way exchanges:
+//   * routing: each workgroup writes its logits as 64-bit words (fp32 bits,
+//     epoch of the call); every workgroup reads the E words until all carry
+//     the current epoch -- the data arrives with the signal -- and selects
+//     the top-K itself (the selection is deterministic, so all agree);
 //   * activations h of slot k: the four gate/up waves of a workgroup hand
-//     their values to the comm wave in LDS; it stores them, adds the
-//     workgroup to a per-group counter (groups = blockIdx % 8, 32 workgroups
-//     each), and the last workgroup of a group raises the group's flag; every
-//     workgroup's comm wave waits for the eight flags of the slot and copies
-//     the slot's h into LDS for its down waves;
-//   * every datum that all workgroups read (logits, h, flags) is stored once
-//     per reader group, so each cache line has ~32 coherent readers: a line
-//     read coherently by all 256 CUs at once serialises at its memory channel
-//     for several microseconds.
-// Each workgroup has 9 waves: waves 0-3 compute gate/up rows (one row of
-// every slot each), waves 4-7 compute down rows (four output rows of every
-// slot each), wave 8 selects the top-K and publishes the workgroup's h
-// values.  The roles keep separate in-order load queues: the down waves'
-// weight loads are in flight while gate/up is still streaming, the
-// activations they wait for do not queue behind gate/up weights, and the
-// comm wave's wait for its own stores never waits for weight loads.
-// No agent-scope fence is used: a cache writeback/invalidate issued by every
-// CU at once costs tens of microseconds.
-// Every weight byte a workgroup needs is requested as soon as its address is
-// known: router, shared expert and x at launch; routed experts right after
-// the top-K.
+//     their values over in LDS; the workgroup writes them as tagged 64-bit
+//     words; every workgroup reads the slot's I words until all are current
+//     and copies them into LDS for its down waves.
+// Every word that all workgroups read is written once per reader group
+// (blockIdx % 8, one per XCD), so each cache line has ~32 coherent readers:
+// a line read coherently by all 256 CUs at once serialises at its memory
+// channel for several microseconds.  Exchanged words travel through
+// agent-scope relaxed atomics (coherent sc1 loads and stores); no cache
+// writeback or invalidate is issued (issued by every CU at once, those cost
+// tens of microseconds).
+//
+// Each workgroup has 8 waves (two per SIMD, so 256 VGPRs each): waves 0-3
+// compute gate/up rows (one row of every slot each), waves 4-7 compute down
+// rows (four output rows of every slot each).  Wave 4 also selects the top-K
+// and runs the activation exchange.  Weight bytes are requested as soon as
+// their addresses are known: router, shared expert and x at launch, routed
+// experts right after the top-K, down rows first -- a wave's memory requests
+// complete in order, so the exchange reads of wave 4 must not queue behind
+// the bulk of the gate/up stream.  Waits between waves of a workgroup read
+// LDS only (a global or flat load in a spin loop would wait for every weight
+// load the wave has in flight).
 //
 // Termination: every wait is bounded; a wait that times out sets bit 1 of
 // the sticky error word and the kernel runs to completion.
@@ -54,21 +54,34 @@ using namespace dev;
 
 constexpr int kG = 256;          // workgroups
 constexpr int kGuWaves = 4;      // gate/up waves 0..3
-constexpr int kDownWaves = 4;    // down waves 4..7
-constexpr int kCommWave = 8;     // routing selection and publication of h
-constexpr int kNT = 64 * (kGuWaves + kDownWaves + 1);
-constexpr int kNR = 64 * (kGuWaves + kDownWaves);  // threads that load the router
+constexpr int kDownWaves = 4;    // down waves 4..7 (wave 4 runs the exchange)
+constexpr int kNT = 64 * (kGuWaves + kDownWaves);
 constexpr long kSpinMax = 1L << 18;
 
-// Cross-workgroup data goes through agent-scope relaxed atomics, which the
-// gfx950 memory model implements as coherent (sc1) loads and stores; no
-// cache writeback or invalidate is issued.  Every exchanged word carries the
-// epoch of its call, so no separate signal (and no ordering between data and
-// signal) is needed.
-__device__ __forceinline__ uint32_t ld_rlx(const uint32_t *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+typedef __attribute__((address_space(3))) volatile uint32_t lds_u32;
+
+__device__ __forceinline__ lds_u32 *lds(uint32_t *p) { return (lds_u32 *)(p); }
+
+// Ordering of LDS accesses between waves of the workgroup only: these wait
+// for outstanding LDS operations, never for global loads.
+__device__ __forceinline__ void lds_release() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
 }
-__device__ __forceinline__ uint64_t ld_rlx64(const uint64_t *p) {
+__device__ __forceinline__ void lds_acquire() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Bounded wait until an LDS word written by another wave reaches `want`.
+__device__ __forceinline__ void wait_lds(uint32_t *p, uint32_t want) {
+  long spins = 0;
+  while (*lds(p) < want) {
+    if (++spins > (kSpinMax << 4)) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  lds_acquire();
+}
+
+__device__ __forceinline__ uint32_t ld_rlx(const uint32_t *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -89,7 +102,7 @@ struct Geo {
   static constexpr int LSEG = SEG_X / 64;           // segments per lane per gate/up row
   static constexpr int XLD = COLS * 2 / 16;         // 16-byte x loads per segment
   static constexpr int RCH = H / 8;                 // 16-byte chunks per router row
-  static constexpr int RXC = RCH / kNR;             // router x chunks per thread
+  static constexpr int RXC = RCH / kNT;             // router x chunks per thread
   static constexpr int GU_ROWS = I / kG;            // gate/up rows per workgroup and slot
   static constexpr int SEG_D = I * BITS / 128;      // segments per down row
   static constexpr int LPR = SEG_D < 64 ? SEG_D : 64;  // lanes per down row
@@ -102,7 +115,7 @@ struct Geo {
   static_assert(GU_ROWS == kGuWaves, "one gate/up row per gate/up wave and slot");
   static_assert(NSEGD == 1, "one down segment per lane");
   static_assert(DLD >= 1 && D_ROWS_W % RPL == 0, "down rows must tile the waves");
-  static_assert(RXC >= 1 && RCH % kNR == 0, "router row must span the loading threads");
+  static_assert(RXC >= 1 && RCH % kNT == 0, "router row must span the workgroup");
   static_assert(SEG_X <= 64 * kGuWaves, "one x segment per gate/up thread");
 };
 
@@ -151,8 +164,6 @@ __device__ __forceinline__ float seg_dot_f32(uint4 c, const float *h) {
   return acc;
 }
 
-__device__ __forceinline__ float wave_sum(float v) { return wave_sum64(v); }
-
 // Sum over aligned groups of LPR lanes (16, 32 or 64) without LDS traffic.
 template <int LPR>
 __device__ __forceinline__ float lane_group_sum(float v, int lane) {
@@ -162,22 +173,13 @@ __device__ __forceinline__ float lane_group_sum(float v, int lane) {
   return wave_sum64(v);
 }
 
-// Bounded wait on a workgroup-local flag written by another wave.
-__device__ __forceinline__ void wait_lds(volatile uint32_t *p, uint32_t want) {
-  long spins = 0;
-  while (*p < want) {
-    if (++spins > (kSpinMax << 4)) break;
-    __builtin_amdgcn_s_sleep(1);
-  }
-}
-
 template <int BITS, int H, int I, int K, int RR>
 __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
   using Gm = Geo<BITS, H, I, K>;
   constexpr int COLS = Gm::COLS, PAIRS = Gm::PAIRS, LSEG = Gm::LSEG;
   constexpr int NSL = K + 1;  // slot K is the shared expert
   static_assert(NSL == kFusedSlots && I == kFusedI, "tagged activations are sized for these");
-  __shared__ float s_red[kNR / 64][RR];
+  __shared__ float s_red[kNT / 64][RR];
   __shared__ uint32_t s_xp[Gm::SEG_X][PAIRS];  // packed x pairs per segment
   __shared__ float2 s_cx[Gm::SEG_X];           // (1024 * sum of pairs, sum of x)
   __shared__ float s_hb[NSL][I];               // h of every slot, for the down waves
@@ -195,8 +197,14 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
   const bool routing = a.ids_in == nullptr;
   constexpr int rr = RR;  // router rows per workgroup (E <= RR * kG)
 
-  // the epoch is read now and published to the workgroup at barrier (A)
-  const uint32_t epoch0 = tid == 0 ? ld_rlx(&a.fc->epoch) + 1u : 0u;
+  // the epoch of this call (calls completed + 1) is read first by the last
+  // wave, which needs nothing before barrier (A), and published there
+  constexpr int kEpochTid = kNT - 64;
+  // (the other threads' value is never used; a non-constant one keeps the
+  // compiler from folding the +1 into the branch, which would wait for the
+  // load right there)
+  uint32_t epoch_done = (uint32_t)a.E;
+  if (tid == kEpochTid) epoch_done = ld_rlx(&a.fc->epoch[grp][0]);
   if (tid < NSL) {
     s_cnt[tid] = 0u;
     s_hready[tid] = 0u;
@@ -206,16 +214,16 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
     s_dissued = 0u;
   }
 
-  // ---- router loads (waves 0..7) -------------------------------------------
+  // ---- router loads (all threads) -------------------------------------------
   uint4 rw[RR * Gm::RXC], rx[Gm::RXC];
-  if (routing && wave < kCommWave) {
+  if (routing) {
 #pragma unroll
     for (int j = 0; j < Gm::RXC; ++j)
-      rx[j] = *reinterpret_cast<const uint4 *>(a.x + (size_t)(tid + kNR * j) * 8);
+      rx[j] = *reinterpret_cast<const uint4 *>(a.x + (size_t)(tid + kNT * j) * 8);
 #pragma unroll
     for (int i = 0; i < RR * Gm::RXC; ++i) {
       const int row = i / Gm::RXC, e = b * rr + row;
-      const int ch = tid + kNR * (i % Gm::RXC);
+      const int ch = tid + kNT * (i % Gm::RXC);
       // rows past E read row E-1 and are never published (loads stay
       // unconditional so the load counter can be tracked statically)
       const int ec = e < a.E ? e : a.E - 1;
@@ -238,7 +246,7 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
     }
 #pragma unroll
     for (int row = 0; row < RR; ++row) {
-      const float v = wave_sum(part[row]);
+      const float v = wave_sum64(part[row]);
       if (lane == 0) s_red[wave][row] = v;
     }
   };
@@ -329,24 +337,22 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
         pg += bf16f(gsb[slot][j] & 0xFFFFu) * ag + bf16f(gsb[slot][j] >> 16) * cx.y;
         pu += bf16f(usb[slot][j] & 0xFFFFu) * au + bf16f(usb[slot][j] >> 16) * cx.y;
       }
-      pg = wave_sum(pg);
-      pu = wave_sum(pu);
+      pg = wave_sum64(pg);
+      pu = wave_sum64(pu);
       return pg / (1.f + expf(-pg)) * pu;
     };
-    // hand h of (slot, this row) to the comm wave through LDS
+    // hand h of (slot, this row) to the exchange through LDS
     auto hand_over = [&](int slot, float hv) {
       if (lane == 0) {
         s_h[slot][wave] = hv;
-        __hip_atomic_fetch_add(&s_cnt[slot], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        lds_release();
+        __hip_atomic_fetch_add(&s_cnt[slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
     };
-    if (tid == 0) s_epoch = epoch0;
     __syncthreads();  // (A) router partials in s_red, x pairs in s_xp, epoch in s_epoch
-    if (a.has_shared) hand_over(K, gateup(K));
+    hand_over(K, a.has_shared ? gateup(K) : 0.f);
     wait_lds(&s_ready, 1u);
-    // the down waves' routed loads go first: they are needed last, and the
-    // activations of the last slot, exchanged at the end of the stream, then
-    // do not queue behind them
+    // the down waves' routed loads go first (see the header)
     wait_lds(&s_dissued, (uint32_t)kDownWaves);
     int eid[K];
 #pragma unroll
@@ -361,9 +367,10 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
       const bool ok = eid[k] >= 0 && eid[k] < a.E;
       hand_over(k, ok ? gateup(k) : 0.f);
     }
-  } else if (wave < kCommWave) {
+  } else {
     // =========================== down waves =================================
     const int dw = wave - kGuWaves;
+    const bool xchg = dw == 0;  // this wave runs routing and the exchange
     const int seg = lane % Gm::LPR;
     const size_t rbytes = (size_t)I * BITS / 8;
     const int groups = I / kGroup;
@@ -383,73 +390,11 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
     };
     load_rows(K, a.has_shared ? a.shared : a.experts);
     if (routing) router_partials();
+    if (tid == kEpochTid) s_epoch = epoch_done + 1u;
     __syncthreads();  // (A)
     const uint32_t epoch = s_epoch;
 
-    float acc[Gm::DLD];
-#pragma unroll
-    for (int ld = 0; ld < Gm::DLD; ++ld) acc[ld] = 0.f;
-    auto down = [&](int slot, float wk) {
-      wait_lds(&s_hready[slot], 1u);
-      float hv[COLS];
-#pragma unroll
-      for (int t = 0; t < COLS / 4; ++t) {
-        const float4 v = *reinterpret_cast<const float4 *>(&s_hb[slot][seg * COLS + 4 * t]);
-        hv[4 * t] = v.x;
-        hv[4 * t + 1] = v.y;
-        hv[4 * t + 2] = v.z;
-        hv[4 * t + 3] = v.w;
-      }
-      float Hs = 0.f;
-#pragma unroll
-      for (int c = 0; c < COLS; ++c) Hs += hv[c];
-#pragma unroll
-      for (int ld = 0; ld < Gm::DLD; ++ld) {
-        const float q = seg_dot_f32<BITS>(dq[slot][ld], hv);
-        const uint32_t sb = dsb[slot][ld];
-        acc[ld] += wk * (bf16f(sb & 0xFFFFu) * q + bf16f(sb >> 16) * Hs);
-      }
-    };
-    wait_lds(&s_ready, 1u);
-    int eid[K];
-    float wk[K];
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      eid[k] = s_ids[k];
-      wk[k] = s_w[k];
-      const bool ok = eid[k] >= 0 && eid[k] < a.E;
-      load_rows(k, a.experts + (size_t)(ok ? eid[k] : 0) * a.stride);
-    }
-    if (lane == 0) atomicAdd(&s_dissued, 1u);
-    if (a.has_shared) down(K, 1.f);
-#pragma unroll
-    for (int k = 0; k < K; ++k) down(k, (eid[k] >= 0 && eid[k] < a.E) ? wk[k] : 0.f);
-#pragma unroll
-    for (int ld = 0; ld < Gm::DLD; ++ld) {
-      const float v = lane_group_sum<Gm::LPR>(acc[ld], lane);
-      if (seg == 0) a.y[rows[ld]] = v;
-    }
-    // every workgroup has published every slot, so all have passed barrier
-    // (A), where they read the epoch
-    if (b == 0 && dw == 0 && lane == 0)
-      __hip_atomic_store(&a.fc->epoch, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  } else {
-    // ============================ comm wave ==================================
-    __syncthreads();  // (A)
-    const uint32_t epoch = s_epoch;
-    const uint64_t *tags_mine = a.tags + (size_t)grp * kMaxE;  // this group's copy
-    // 0. this workgroup's logits, one copy per reader group
-    if (routing && lane < kGroups * rr) {
-      const int rep = lane / rr, row = lane % rr, e = b * rr + row;
-      if (e < a.E) {
-        float l = 0.f;
-#pragma unroll
-        for (int w = 0; w < kNR / 64; ++w) l += s_red[w][row];
-        const uint64_t v = ((uint64_t)epoch << 32) | (uint64_t)__float_as_uint(l);
-        __hip_atomic_store(&a.tags[(size_t)rep * kMaxE + e], v, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
+    // ---- the exchange (wave 4 only) ----
     // publish this workgroup's h of `slot`: one tagged copy per reader group
     auto publish = [&](int slot) {
       if (lane < kGroups * kGuWaves) {
@@ -475,119 +420,208 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
       for (int i = 0; i < NLD; ++i)
         *reinterpret_cast<float2 *>(&s_hb[slot][128 * i + 2 * lane]) =
             make_float2(__uint_as_float(t[i].x), __uint_as_float(t[i].z));
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      if (lane == 0) s_hready[slot] = 1u;
+      lds_release();
+      if (lane == 0) *lds(&s_hready[slot]) = 1u;
       return true;
     };
-
-    // 1. the shared expert's h is ready first
-    if (a.has_shared) {
-      wait_lds(&s_cnt[K], (uint32_t)kGuWaves);
-      publish(K);
-    }
-    const uint64_t *tags_copy = tags_mine;
-    // 2. routing: wait for every workgroup's tagged logits in this group's
-    //    copy, select the top-K.  Lane l holds experts 128 i + 2 l + {0, 1}.
-    if (routing) {
-      constexpr int NV = kMaxE / 64;
-      float v[NV];
-      long spins = 0;
+    // publish routed slots as the gate/up waves hand them over, until `slot`
+    // (published by this workgroup before it is polled) is complete everywhere
+    int published = 0;
+    long xspins = 0;
+    auto exchange_until = [&](int slot) {
       while (true) {
-        bool ok = true;
-#pragma unroll
-        for (int i = 0; i < NV / 2; ++i) {
-          const int idx = 128 * i + 2 * lane;
-          if (idx < a.E) {
-            const uint4 t = ld_coh16(tags_copy, (uint32_t)idx * 8u);
-            ok &= t.y == epoch && (idx + 1 >= a.E || t.w == epoch);
-            v[2 * i] = __uint_as_float(t.x);
-            v[2 * i + 1] = idx + 1 < a.E ? __uint_as_float(t.z) : __builtin_nanf("");
-          } else {
-            v[2 * i] = v[2 * i + 1] = __builtin_nanf("");
-          }
+        if (published < K && *lds(&s_cnt[published]) >= (uint32_t)kGuWaves) {
+          lds_acquire();
+          publish(published);
+          ++published;
+          continue;
         }
-        if (__all(ok)) break;
-        if (++spins > kSpinMax) {
+        if ((slot == K || slot < published) && try_consume(slot)) return;
+        if (++xspins > kSpinMax) {
           if (lane == 0) atomicOr(&a.ctrl->err, 2u);
-          break;
+          if (lane == 0) *lds(&s_hready[slot]) = 1u;
+          return;
         }
         __builtin_amdgcn_s_sleep(1);
       }
-      // key = (order-preserving logit bits, ~index): the largest key is the
-      // largest logit, and among equal logits the lowest index
-      uint64_t key[NV];
-#pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        const uint32_t idx = 128u * (j / 2) + 2u * lane + (j & 1);
-        key[j] = ((uint64_t)f32_order_key(v[j]) << 32) | (0xFFFFFFFFu - idx);
+    };
+
+    // the shared expert's h is published as soon as the gate/up waves hand
+    // it over, also while the routing poll runs
+    bool shared_out = false;
+    auto publish_shared = [&]() {
+      if (!shared_out && *lds(&s_cnt[K]) >= (uint32_t)kGuWaves) {
+        lds_acquire();
+        if (a.has_shared) publish(K);
+        shared_out = true;
       }
-      float sel_v[K];
-      int sel_i[K];
+    };
+
+    if (xchg) {
+      // 1. this workgroup's logits, one copy per reader group
+      if (routing && lane < kGroups * rr) {
+        const int rep = lane / rr, row = lane % rr, e = b * rr + row;
+        if (e < a.E) {
+          float l = 0.f;
 #pragma unroll
-      for (int k = 0; k < K; ++k) {
-        uint64_t best = 0;
-#pragma unroll
-        for (int j = 0; j < NV; ++j) best = key[j] > best ? key[j] : best;
-        const uint64_t m = wave_max_u64(best);
-        const uint32_t k32 = (uint32_t)(m >> 32);
-        sel_i[k] = (int)(0xFFFFFFFFu - (uint32_t)m);
-        sel_v[k] = __uint_as_float((k32 & 0x80000000u) ? (k32 & 0x7FFFFFFFu) : ~k32);
-        if (m == 0) sel_i[k] = -1;  // fewer than K finite logits
-#pragma unroll
-        for (int j = 0; j < NV; ++j) key[j] = key[j] == m ? 0 : key[j];
-      }
-      if (lane == 0) {
-        float den = 0.f, p[K];
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-          p[k] = expf(sel_v[k] - sel_v[0]);
-          den += p[k];
+          for (int w = 0; w < kNT / 64; ++w) l += s_red[w][row];
+          const uint64_t v = ((uint64_t)epoch << 32) | (uint64_t)__float_as_uint(l);
+          __hip_atomic_store(&a.tags[(size_t)rep * kMaxE + e], v, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
         }
+      }
+      // 2. routing: wait for every workgroup's tagged logits in this group's
+      //    copy, select the top-K.  Lane l holds experts 128 i + 2 l + {0, 1}.
+      if (routing) {
+        // entries E .. 256 RR - 1 of the copy (within its kMaxE words) are
+        // read but ignored, so every load is unconditional
+        const uint64_t *tags_mine = a.tags + (size_t)grp * kMaxE;
+        constexpr int NV = 4 * RR;
+        static_assert(256 * RR <= kMaxE, "tag copy holds 256 RR entries");
+        float v[NV];
+        long spins = 0;
+        while (true) {
+          uint4 t[NV / 2];
+#pragma unroll
+          for (int i = 0; i < NV / 2; ++i) t[i] = ld_coh16(tags_mine, (uint32_t)(128 * i + 2 * lane) * 8u);
+          bool ok = true;
+#pragma unroll
+          for (int i = 0; i < NV / 2; ++i) {
+            const int idx = 128 * i + 2 * lane;
+            ok &= (idx >= a.E || t[i].y == epoch) && (idx + 1 >= a.E || t[i].w == epoch);
+            v[2 * i] = idx < a.E ? __uint_as_float(t[i].x) : __builtin_nanf("");
+            v[2 * i + 1] = idx + 1 < a.E ? __uint_as_float(t[i].z) : __builtin_nanf("");
+          }
+          if (__all(ok)) break;
+          publish_shared();
+          if (++spins > kSpinMax) {
+            if (lane == 0) atomicOr(&a.ctrl->err, 2u);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+        // key = (order-preserving logit bits, ~index): the largest key is the
+        // largest logit, and among equal logits the lowest index
+        uint64_t key[NV];
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+          const uint32_t idx = 128u * (j / 2) + 2u * lane + (j & 1);
+          key[j] = ((uint64_t)f32_order_key(v[j]) << 32) | (0xFFFFFFFFu - idx);
+        }
+        float sel_v[K];
+        int sel_i[K];
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-          s_ids[k] = sel_i[k];
-          s_w[k] = p[k] / den;
-          if (b == 0 && a.ids_out) {
-            a.ids_out[k] = sel_i[k];
-            a.w_out[k] = p[k] / den;
+          uint64_t best = 0;
+#pragma unroll
+          for (int j = 0; j < NV; ++j) best = key[j] > best ? key[j] : best;
+          const uint64_t m = wave_max_u64(best);
+          const uint32_t k32 = (uint32_t)(m >> 32);
+          sel_i[k] = (int)(0xFFFFFFFFu - (uint32_t)m);
+          sel_v[k] = __uint_as_float((k32 & 0x80000000u) ? (k32 & 0x7FFFFFFFu) : ~k32);
+          if (m == 0) sel_i[k] = -1;  // fewer than K finite logits
+#pragma unroll
+          for (int j = 0; j < NV; ++j) key[j] = key[j] == m ? 0 : key[j];
+        }
+        if (lane == 0) {
+          float den = 0.f, p[K];
+#pragma unroll
+          for (int k = 0; k < K; ++k) {
+            p[k] = expf(sel_v[k] - sel_v[0]);
+            den += p[k];
+          }
+#pragma unroll
+          for (int k = 0; k < K; ++k) {
+            s_ids[k] = sel_i[k];
+            s_w[k] = p[k] / den;
+            if (b == 0 && a.ids_out) {
+              a.ids_out[k] = sel_i[k];
+              a.w_out[k] = p[k] / den;
+            }
           }
         }
+      } else if (lane < K) {
+        const int e = a.ids_in[lane];
+        s_ids[lane] = e;
+        s_w[lane] = a.w_in[lane];
+        if ((e < 0 || e >= a.E) && b == 0) atomicOr(&a.ctrl->err, 1u);
       }
-    } else if (lane < K) {
-      const int e = a.ids_in[lane];
-      s_ids[lane] = e;
-      s_w[lane] = a.w_in[lane];
-      if ((e < 0 || e >= a.E) && b == 0) atomicOr(&a.ctrl->err, 1u);
+      lds_release();
+      if (lane == 0) *lds(&s_ready) = 1u;
+    } else {
+      wait_lds(&s_ready, 1u);
+    }
+
+    // routed down rows: issued before the gate/up waves issue theirs
+    int eid[K];
+    float wk[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      eid[k] = s_ids[k];
+      wk[k] = s_w[k];
+      const bool ok = eid[k] >= 0 && eid[k] < a.E;
+      load_rows(k, a.experts + (size_t)(ok ? eid[k] : 0) * a.stride);
     }
     if (lane == 0)
-      __hip_atomic_store(&s_ready, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-    // 3. publish the routed slots as the gate/up waves finish them, and move
-    //    every slot's complete h into LDS once all workgroups published it.
-    //    Consumption order: shared, then routed slots 0..K-1; a slot is
-    //    polled only after this workgroup has published it.
-    const int nslots = K + a.has_shared;
-    int p = 0, c = 0;
-    long spins = 0;
-    volatile uint32_t *vcnt = s_cnt;
-    while (p < K || c < nslots) {
-      if (p < K && vcnt[p] >= (uint32_t)kGuWaves) {
-        publish(p);
-        ++p;
-        continue;
+      __hip_atomic_fetch_add(&s_dissued, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+
+    if (xchg && !shared_out) {
+      wait_lds(&s_cnt[K], (uint32_t)kGuWaves);
+      publish_shared();
+    }
+
+    float acc[Gm::DLD];
+#pragma unroll
+    for (int ld = 0; ld < Gm::DLD; ++ld) acc[ld] = 0.f;
+    auto down = [&](int slot, float wkk) {
+      if (xchg) exchange_until(slot);
+      else wait_lds(&s_hready[slot], 1u);
+      float hv[COLS];
+#pragma unroll
+      for (int t = 0; t < COLS / 4; ++t) {
+        const float4 v = *reinterpret_cast<const float4 *>(&s_hb[slot][seg * COLS + 4 * t]);
+        hv[4 * t] = v.x;
+        hv[4 * t + 1] = v.y;
+        hv[4 * t + 2] = v.z;
+        hv[4 * t + 3] = v.w;
       }
-      if (c < nslots) {
-        const int slot = a.has_shared ? (c == 0 ? K : c - 1) : c;
-        if ((slot == K || slot < p) && try_consume(slot)) {
-          ++c;
-          continue;
+      float Hs = 0.f;
+#pragma unroll
+      for (int c = 0; c < COLS; ++c) Hs += hv[c];
+#pragma unroll
+      for (int ld = 0; ld < Gm::DLD; ++ld) {
+        const float q = seg_dot_f32<BITS>(dq[slot][ld], hv);
+        const uint32_t sb = dsb[slot][ld];
+        acc[ld] += wkk * (bf16f(sb & 0xFFFFu) * q + bf16f(sb >> 16) * Hs);
+      }
+    };
+    if (a.has_shared) down(K, 1.f);
+#pragma unroll
+    for (int k = 0; k < K; ++k) down(k, (eid[k] >= 0 && eid[k] < a.E) ? wk[k] : 0.f);
+    // after a timed-out wait, publish what the gate/up waves still hand over
+    if (xchg) {
+      long spins = 0;
+      while (published < K) {
+        if (*lds(&s_cnt[published]) >= (uint32_t)kGuWaves) {
+          lds_acquire();
+          publish(published);
+          ++published;
+        } else if (++spins > kSpinMax) {
+          break;
+        } else {
+          __builtin_amdgcn_s_sleep(1);
         }
       }
-      if (++spins > kSpinMax) {
-        if (lane == 0) atomicOr(&a.ctrl->err, 2u);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
     }
+#pragma unroll
+    for (int ld = 0; ld < Gm::DLD; ++ld) {
+      const float v = lane_group_sum<Gm::LPR>(acc[ld], lane);
+      if (seg == 0) a.y[rows[ld]] = v;
+    }
+    // every workgroup has published every slot, so all have passed barrier
+    // (A), where they read the epoch
+    if (b == 0 && xchg && lane < kGroups)
+      __hip_atomic_store(&a.fc->epoch[lane][0], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

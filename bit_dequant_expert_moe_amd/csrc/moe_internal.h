@@ -49,16 +49,18 @@ constexpr int kGroups = 8;  // workgroup groups by blockIdx % 8 (one per XCD)
 // the epoch of the call that wrote them in their upper 32 bits, so a reader
 // detects completion from the data itself.
 struct FCtrl {
-  uint32_t epoch;  // calls completed on this workspace
-  uint32_t pad[63];
+  // calls completed on this workspace, one copy per reader group, each on a
+  // cache line of its own
+  uint32_t epoch[kGroups][32];
 };
+static_assert(sizeof(FCtrl) == 1024, "epoch copies are 128 bytes apart");
 constexpr int kFusedI = 1024;     // intermediate size the fused kernel covers
 constexpr int kFusedSlots = 5;    // top-4 + shared
 
 constexpr size_t kCtrlOff = 0;
 constexpr size_t kFCtrlOff = 256;
 // tagged logits: uint64 [kGroups][kMaxE]
-constexpr size_t kTagOff = kFCtrlOff + 256;
+constexpr size_t kTagOff = kFCtrlOff + sizeof(FCtrl);
 // tagged activations: uint64 [kGroups][kFusedSlots][kFusedI]
 constexpr size_t kHTagOff = kTagOff + (size_t)kGroups * kMaxE * 8;
 constexpr size_t kHeaderBytes = kHTagOff + (size_t)kGroups * kFusedSlots * kFusedI * 8;
