@@ -48,7 +48,15 @@ WsLayout ws_layout(const moe_dims &d, int T) {
   W.w = o;
   o = align_up(o + (size_t)T * d.top_k * 4, kAlign);
   W.h = o;
-  o = align_up(o + (size_t)T * slots * d.inter * 4, kAlign);
+  // indexed by pair code t (K + 1) + slot on every path
+  o = align_up(o + (size_t)T * (d.top_k + 1) * d.inter * 4, kAlign);
+  W.bk = o;
+  if (T >= 2) {
+    const size_t maxB = (size_t)grouped_max_buckets(d, T);
+    o = align_up(o + (2 + 2 * maxB + (size_t)T * slots) * 4, kAlign);
+  }
+  W.yd = o;
+  if (T >= 2) o = align_up(o + (size_t)T * (d.top_k + 1) * d.hidden * 4, kAlign);
   W.total = o;
   return W;
 }
@@ -93,6 +101,24 @@ static bool use_fused(const moe_dims &d, int T) {
     disabled = (e && e[0] == '1') ? 1 : 0;
   }
   return T == 1 && !disabled && fused_supported(d);
+}
+
+// Two or more tokens take the grouped path (pairs bucketed by expert, MFMA
+// GEMMs); MOE_DISABLE_GROUPED=1 selects the per-token kernels instead.
+static bool use_grouped(int T) {
+  static int disabled = -1;
+  if (disabled < 0) {
+    const char *e = getenv("MOE_DISABLE_GROUPED");
+    disabled = (e && e[0] == '1') ? 1 : 0;
+  }
+  return T >= 2 && !disabled;
+}
+
+static int expert_forward(const moe_dims &d, const moe_layer &L, const uint16_t *x, int T,
+                          const int32_t *ids, const float *w, float *y, void *ws,
+                          void *stream) {
+  if (use_grouped(T)) return launch_expert_forward_grouped(d, L, x, T, ids, w, y, ws, stream);
+  return launch_expert_forward(d, L, x, T, ids, w, y, ws, stream);
 }
 
 static moe_status check_T(int T) { return (T < 1 || T > kMaxT) ? MOE_ERR_SHAPE : MOE_OK; }
@@ -180,8 +206,7 @@ moe_status moe_expert_forward(const moe_dims *dims, const moe_layer *layer, cons
     return launch_layer_fused(*dims, *layer, x, ids, w, nullptr, nullptr, y, ws, stream) == 0
                ? MOE_OK
                : MOE_ERR_HIP;
-  return launch_expert_forward(*dims, *layer, x, T, ids, w, y, ws, stream) == 0 ? MOE_OK
-                                                                                : MOE_ERR_HIP;
+  return expert_forward(*dims, *layer, x, T, ids, w, y, ws, stream) == 0 ? MOE_OK : MOE_ERR_HIP;
 }
 
 moe_status moe_layer_decode(const moe_dims *dims, const moe_layer *layer, const uint16_t *x,
@@ -206,8 +231,7 @@ moe_status moe_layer_decode(const moe_dims *dims, const moe_layer *layer, const 
   float *w_d = w ? w : reinterpret_cast<float *>(base + W.w);
   if (launch_route(*dims, layer->router, x, T, ids_d, w_d, nullptr, ws, stream) != 0)
     return MOE_ERR_HIP;
-  if (launch_expert_forward(*dims, *layer, x, T, ids_d, w_d, y, ws, stream) != 0)
-    return MOE_ERR_HIP;
+  if (expert_forward(*dims, *layer, x, T, ids_d, w_d, y, ws, stream) != 0) return MOE_ERR_HIP;
   return MOE_OK;
 }
 

@@ -34,6 +34,8 @@ BlobLayout blob_layout(const moe_dims &d);
 //   ids        : int32 [T][K]
 //   w          : fp32 [T][K]
 //   h          : fp32 [T][K+1][I]   activations silu(g)*u per slot
+//   bk         : int32 buckets of the batched path (expert, offsets, pair codes)
+//   yd         : fp32 [T][K+1][H]   per-slot down projections of the batched path
 struct Ctrl {
   uint32_t route_counter;  // blocks of the routing kernel that finished
   uint32_t err;            // sticky device error flags
@@ -66,7 +68,7 @@ constexpr size_t kHTagOff = kTagOff + (size_t)kGroups * kMaxE * 8;
 constexpr size_t kHeaderBytes = kHTagOff + (size_t)kGroups * kFusedSlots * kFusedI * 8;
 
 struct WsLayout {
-  size_t ctrl, fctrl, logits_tag, h_tag, logits, ids, w, h, total;
+  size_t ctrl, fctrl, logits_tag, h_tag, logits, ids, w, h, bk, yd, total;
 };
 WsLayout ws_layout(const moe_dims &d, int T);
 
@@ -100,6 +102,11 @@ int launch_layer_fused(const moe_dims &d, const moe_layer &L, const uint16_t *x,
                        float *w_out, float *y, void *ws, void *stream);
 int launch_dequantize(const moe_dims &d, const uint8_t *blob, int which, float *out,
                       void *stream);
+// Batched path (moe_grouped.hip): pairs grouped by expert, MFMA GEMMs.
+int grouped_max_buckets(const moe_dims &d, int T);
+int launch_expert_forward_grouped(const moe_dims &d, const moe_layer &L, const uint16_t *x,
+                                  int T, const int32_t *ids, const float *w, float *y, void *ws,
+                                  void *stream);
 int read_device_error(void *ws, void *stream, int32_t *err);
 
 }  // namespace moe

@@ -111,4 +111,9 @@ def check_routing(od, ids_gpu, w_gpu, logits_or, gap_or, K):
 
 
 def max_rel_err(y_gpu, y_or):
-    return float(np.max(np.abs(y_gpu - y_or)) / np.max(np.abs(y_or)))
+    """max_i |y_gpu - y_or| / max_i |y_or| per token (last axis), worst token."""
+    y_gpu = np.atleast_2d(np.asarray(y_gpu, np.float64))
+    y_or = np.atleast_2d(np.asarray(y_or, np.float64))
+    num = np.max(np.abs(y_gpu - y_or), axis=-1)
+    den = np.max(np.abs(y_or), axis=-1)
+    return float(np.max(num / den))

@@ -126,6 +126,27 @@ def test_layer_decode_full_batch(full):
     _layer_check(full, x, "full T=4")
 
 
+def test_layer_decode_full_T64(full):
+    # the batched workload: 64 tokens, 512 experts; pairs grouped by expert
+    x = synth.tokens(1003, 0, 64, 4096)
+    _layer_check(full, x, "full T=64")
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_grouped_buckets_over_one_chunk(bits):
+    # E = K = 4: every token selects every expert, so each bucket holds all 64
+    # tokens (two 32-pair chunks), and the shared bucket too
+    L = gu.DeviceLayer(1024, 512, 4, 4, bits=bits, seed=77 + bits)
+    x = synth.tokens(77, 0, 64, 1024)
+    _layer_check(L, x, "E=K=4 T=64 %d-bit" % bits)
+
+
+def test_grouped_2bit_full_T16():
+    L = gu.DeviceLayer(4096, 1024, 512, 4, bits=2, seed=1001, blob_seed=1004)
+    x = synth.tokens(1001, 3, 16, 4096)
+    _layer_check(L, x, "2-bit full T=16")
+
+
 def test_layer_decode_2bit_tiny():
     L = gu.DeviceLayer(4096, 1024, 16, 4, bits=2, seed=1000, blob_seed=1004)
     x = synth.tokens(1000, 0, 2, 4096)
