@@ -12,9 +12,11 @@
 //   k_bucket     counting sort of the T*K (token, slot) pairs by expert:
 //                bucket list (routed experts in increasing id, then the shared
 //                expert with all T tokens), offsets and pair codes.
+//   k_xprep      x of the batch in the B-operand layout, with group sums.
 //   k_grouped    dequantising grouped GEMM on the matrix cores for one
-//                (bucket, 64-row tile, 32-pair chunk):
-//                  gate/up: h = silu(Gate x) * (Up x) for every pair;
+//                (bucket, 64-row tile, 16-pair chunk):
+//                  gate/up: h = silu(Gate x) * (Up x) for every pair, written
+//                           as the B operand of the down pass;
 //                  down:    yd = Down h for every pair.
 //   k_combine    y[t] = sum_k w[t][k] yd[t][k] + yd[t][shared], in that order.
 //
@@ -45,10 +47,11 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 constexpr int kRT = 64;         // weight rows per block (16 per wave)
-constexpr int kNC = 32;         // pairs per block (two 16-wide MFMA tiles)
+constexpr int kNC = 16;         // pairs per block (one 16-wide MFMA tile)
 constexpr int kKC = 256;        // columns per staged chunk
 constexpr int kGC = kKC / kGroup;  // groups per chunk (4)
 constexpr int kSl = kKC / 8;    // 8-column slices per chunk (32)
+static_assert(kRT == kGroup, "a gate/up row tile is one group of the down columns");
 
 // ---------------------------------------------------------------------------
 // Buckets.  Layout of the int32 array bk (maxB = min(E, T K) + has_shared):
@@ -144,16 +147,26 @@ __global__ void __launch_bounds__(1024) k_bucket(BucketArgs a) {
 
 // ---------------------------------------------------------------------------
 // Grouped dequantising GEMM.
+//
+// B operands are read straight from global memory (L2-resident: x and h of the
+// batch are a few MB) in the layout the matrix cores take, written by the
+// producers: k_xprep for x, the gate/up epilogue for h.  Per 8-column slice s
+// of a row of B: one 16-byte bf16x8 in the order (c0, c4, c1, c5, c2, c6, c3,
+// c7) (x), or two (h as bf16 hi, then bf16 lo); per group of 64 columns the
+// fp32 sum of the operand values (x, or hi + lo).  A block stages the codes,
+// the scales and its 16 B columns of each chunk in LDS.
 // ---------------------------------------------------------------------------
 struct GroupArgs {
-  const uint16_t *x;  // [T][H] bf16 (gate/up)
-  const float *hin;   // [T (K+1)][I] fp32 (down)
+  const uint4 *bop;    // B operand: [rows of B][C / 8][BV] uint4
+  const float *bsum;   // [rows of B][C / 64] group sums
   const uint8_t *experts, *shared;
   int64_t stride;
   const int32_t *bk;
-  float *out;         // gate/up: h [T (K+1)][I]; down: yd [T (K+1)][H]
-  int R, C;           // rows and columns of the matrices of this pass
-  int E, maxB, K1;    // K1 = K + 1 (pair code = token K1 + slot)
+  uint4 *hb;           // gate/up output: h as B operand of the down pass
+  float *hs;           //   and its group sums
+  float *yd;           // down output: [T (K+1)][H]
+  int R, C;            // rows and columns of the matrices of this pass
+  int E, maxB, K1;     // K1 = K + 1 (pair code = token K1 + slot)
   int64_t off_q0, off_q1, off_sb0, off_sb1;  // second matrix unused for down
 };
 
@@ -161,21 +174,28 @@ template <int BITS, bool DOWN>
 struct GL {  // LDS geometry
   static constexpr int NMAT = DOWN ? 1 : 2;
   static constexpr int RW = kKC * BITS / 32 + 2;  // words per staged row (+2 against bank conflicts)
-  static constexpr int BV = DOWN ? 8 : 4;         // u32 per (pair, slice): bf16x8 (x) or hi + lo
-  static constexpr int TS = kSl * BV + 4;         // u32 per staged pair (+4 against bank conflicts)
+  static constexpr int BV = DOWN ? 2 : 1;         // uint4 per (B row, slice)
+  static constexpr int BCS = kSl * BV + 1;        // uint4 per staged B column (+1 against bank conflicts)
+  static constexpr int BPT = kNC * kSl * BV / 256;  // B pieces per thread
   static constexpr int A_U32 = NMAT * kRT * RW;
-  static constexpr int B_U32 = kNC * TS;
   static constexpr int SB_U32 = NMAT * kRT * kGC;
-  static constexpr int XS_F32 = kNC * kGC;
-  static constexpr int BUF_U32 = A_U32 + B_U32 + SB_U32 + XS_F32;
+  static constexpr int B_U32 = kNC * BCS * 4;
+  static constexpr int XS_U32 = kNC * kGC;
+  static constexpr int BUF_U32 = A_U32 + SB_U32 + B_U32 + XS_U32;
   static constexpr size_t BYTES = 2 * (size_t)BUF_U32 * 4;
   static constexpr int PPR = kKC * BITS / 128;    // 16-byte pieces per staged row
-  static_assert((kRT * PPR) % 256 == 0 || kRT * PPR == 256, "A pieces tile the block");
+  static constexpr int APT = NMAT * kRT * PPR / 256;  // A pieces per thread
+  static_assert(APT >= 1 && (NMAT * kRT * PPR) % 256 == 0, "A pieces tile the block");
+  static_assert(BPT >= 1 && (kNC * kSl * BV) % 256 == 0, "B pieces tile the block");
+  static_assert((A_U32 + SB_U32) % 4 == 0, "B area 16-byte aligned");
 };
 
-// Two bf16 (hi half, lo half) of 128 + the fields selected by mask m.
+// Two bf16 (hi half, lo half) of 128 + the fields selected by mask m.  Plain
+// C (the compiler forms v_and_or_b32): an inline-asm producer is opaque to the
+// hazard checks that keep a VALU write from overtaking an MFMA still reading
+// the same register.
 __device__ __forceinline__ uint32_t magic_pair(uint32_t v, uint32_t m) {
-  return and_or(v, m, 0x43004300u);
+  return (v & m) | 0x43004300u;
 }
 
 // A operand of one 8-column slice: bf16 128 + q in the order
@@ -211,10 +231,36 @@ __device__ __forceinline__ uint4 b_order(uint4 q) {
   return r;
 }
 
+// x of the batch as B operand of the gate/up pass: one thread per slice.
+struct XPrepArgs {
+  const uint16_t *x;
+  uint4 *xb;
+  float *xs;
+  int T, H;
+};
+
+__global__ void __launch_bounds__(256) k_xprep(XPrepArgs a) {
+  const int ns = a.H / 8;
+  const int i = blockIdx.x * 256 + threadIdx.x;  // slice over all tokens
+  // (T H / 8 is a multiple of 8: whole groups are in or out of range)
+  const bool in = i < a.T * ns;
+  const uint4 v = in ? reinterpret_cast<const uint4 *>(a.x)[i] : make_uint4(0, 0, 0, 0);
+  float part = bf16f(v.x & 0xFFFFu) + bf16f(v.x >> 16) + bf16f(v.y & 0xFFFFu) +
+               bf16f(v.y >> 16) + bf16f(v.z & 0xFFFFu) + bf16f(v.z >> 16) +
+               bf16f(v.w & 0xFFFFu) + bf16f(v.w >> 16);
+  if (in) a.xb[i] = b_order(v);
+  // a group is 8 consecutive slices: 8 consecutive lanes
+  part += __shfl_xor(part, 1, 64);
+  part += __shfl_xor(part, 2, 64);
+  part += __shfl_xor(part, 4, 64);
+  if (in && (i & 7) == 0) a.xs[i >> 3] = part;
+}
+
 template <int BITS, bool DOWN>
 __global__ void __launch_bounds__(256) k_grouped(GroupArgs a) {
   using G = GL<BITS, DOWN>;
   extern __shared__ __align__(16) uint32_t lds[];
+  __shared__ float s_hsum[4][16];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int q = lane >> 4, col = lane & 15;
   const int nb = a.bk[0];
@@ -225,27 +271,26 @@ __global__ void __launch_bounds__(256) k_grouped(GroupArgs a) {
   const int pbase = p0 + kNC * (int)blockIdx.z;
   if (pbase >= p1) return;
   const int nn = min(kNC, p1 - pbase);
-  const int ntiles = (nn + 15) >> 4;
   const int32_t *pairs = a.bk + 2 + 2 * a.maxB + pbase;
   const uint8_t *blob = e == a.E ? a.shared : a.experts + (size_t)e * a.stride;
   const int row0 = kRT * (int)blockIdx.x;
   const size_t rbytes = (size_t)a.C * BITS / 8;
   const int groups = a.C / kGroup;
+  const int nslices = a.C / 8;
   const int nchunks = a.C / kKC;
+  // B columns of this block: the pair (down) or its token (gate/up) of each
+  // of the kNC columns; padding columns are staged as zeros
+  const int code = col < nn ? pairs[col] : 0;  // this lane's output column
+  const bool bvalid = col < nn;
 
-  // ---- staging of chunk c into buffer buf --------------------------------
-  constexpr int APT = G::NMAT * kRT * G::PPR / 256;  // 16-byte A pieces per thread
-  uint4 ra[APT > 0 ? APT : 1];
+  // ---- per chunk: A pieces, scales, B columns and their sums to LDS ---------
+  uint4 ra[G::APT];
   uint4 rsb = make_uint4(0, 0, 0, 0);
-  constexpr int BLD = DOWN ? 8 : 4;  // 16-byte B loads per thread
-  uint4 rb[BLD];
-  const int bj = tid >> 3, bs = (tid & 7) * 4;  // B: pair bj, slices bs .. bs+3
-  const int bcode = bj < nn ? pairs[bj] : 0;
-  const int brow = DOWN ? bcode : bcode / a.K1;  // row of hin (pair) or of x (token)
-
+  uint4 rb[G::BPT];
+  float rxs = 0.f;
   auto load_chunk = [&](int c) {
 #pragma unroll
-    for (int i = 0; i < APT; ++i) {
+    for (int i = 0; i < G::APT; ++i) {
       const int pc = tid + 256 * i;
       const int mat = pc / (kRT * G::PPR), rr = (pc / G::PPR) % kRT, c16 = pc % G::PPR;
       const int64_t off = mat ? a.off_q1 : a.off_q0;
@@ -258,30 +303,34 @@ __global__ void __launch_bounds__(256) k_grouped(GroupArgs a) {
       rsb = *reinterpret_cast<const uint4 *>(blob + off +
                                             ((size_t)(row0 + rr) * groups + (size_t)c * kGC) * 4);
     }
-    if (bj < nn) {
 #pragma unroll
-      for (int i = 0; i < BLD; ++i) {
-        if (DOWN) {
-          // 4 slices x 8 fp32 of h
-          rb[i] = *reinterpret_cast<const uint4 *>(a.hin + (size_t)brow * a.C + (size_t)c * kKC +
-                                                  (size_t)bs * 8 + 4 * i);
-        } else {
-          rb[i] = *reinterpret_cast<const uint4 *>(a.x + (size_t)brow * a.C + (size_t)c * kKC +
-                                                  (size_t)(bs + i) * 8);
-        }
+    for (int i = 0; i < G::BPT; ++i) {
+      const int pc = tid + 256 * i;
+      const int bc = pc / (kSl * G::BV), rest = pc % (kSl * G::BV);
+      rb[i] = make_uint4(0, 0, 0, 0);
+      if (bc < nn) {
+        const int pcode = pairs[bc];
+        const int brow = DOWN ? pcode : pcode / a.K1;
+        rb[i] = a.bop[((size_t)brow * nslices + (size_t)c * kSl) * G::BV + rest];
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < BLD; ++i) rb[i] = make_uint4(0, 0, 0, 0);
+    }
+    if (tid < kNC * kGC) {
+      const int bc = tid / kGC, gi = tid % kGC;
+      rxs = 0.f;
+      if (bc < nn) {
+        const int pcode = pairs[bc];
+        const int brow = DOWN ? pcode : pcode / a.K1;
+        rxs = a.bsum[(size_t)brow * groups + c * kGC + gi];
+      }
     }
   };
   auto store_chunk = [&](int buf) {
     uint32_t *A = lds + (size_t)buf * G::BUF_U32;
-    uint32_t *B = A + G::A_U32;
-    uint32_t *SB = B + G::B_U32;
-    float *XS = reinterpret_cast<float *>(SB + G::SB_U32);
+    uint32_t *SB = A + G::A_U32;
+    uint4 *Bq = reinterpret_cast<uint4 *>(SB + G::SB_U32);
+    float *XS = reinterpret_cast<float *>(SB + G::SB_U32 + G::B_U32);
 #pragma unroll
-    for (int i = 0; i < APT; ++i) {
+    for (int i = 0; i < G::APT; ++i) {
       const int pc = tid + 256 * i;
       const int mat = pc / (kRT * G::PPR), rr = (pc / G::PPR) % kRT, c16 = pc % G::PPR;
       uint32_t *dst = A + (mat * kRT + rr) * G::RW + c16 * 4;
@@ -291,100 +340,55 @@ __global__ void __launch_bounds__(256) k_grouped(GroupArgs a) {
       dst[3] = ra[i].w;
     }
     if (tid < G::NMAT * kRT) *reinterpret_cast<uint4 *>(SB + tid * kGC) = rsb;
-    float part = 0.f;
-    if (!DOWN) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint4 v = rb[i];
-        part += bf16f(v.x & 0xFFFFu) + bf16f(v.x >> 16) + bf16f(v.y & 0xFFFFu) + bf16f(v.y >> 16) +
-                bf16f(v.z & 0xFFFFu) + bf16f(v.z >> 16) + bf16f(v.w & 0xFFFFu) + bf16f(v.w >> 16);
-        *reinterpret_cast<uint4 *>(B + bj * G::TS + (bs + i) * G::BV) = b_order(v);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float f[8] = {__uint_as_float(rb[2 * i].x), __uint_as_float(rb[2 * i].y),
-                            __uint_as_float(rb[2 * i].z), __uint_as_float(rb[2 * i].w),
-                            __uint_as_float(rb[2 * i + 1].x), __uint_as_float(rb[2 * i + 1].y),
-                            __uint_as_float(rb[2 * i + 1].z), __uint_as_float(rb[2 * i + 1].w)};
-        uint32_t hi[8], lo[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          hi[k] = f2bf(f[k]);
-          const float r = f[k] - bf16f(hi[k]);
-          lo[k] = f2bf(r);
-          part += bf16f(hi[k]) + bf16f(lo[k]);
-        }
-        const uint4 vh = make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
-                                    hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16));
-        const uint4 vl = make_uint4(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16),
-                                    lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16));
-        uint32_t *dst = B + bj * G::TS + (bs + i) * G::BV;
-        *reinterpret_cast<uint4 *>(dst) = b_order(vh);
-        *reinterpret_cast<uint4 *>(dst + 4) = b_order(vl);
-      }
+    for (int i = 0; i < G::BPT; ++i) {
+      const int pc = tid + 256 * i;
+      const int bc = pc / (kSl * G::BV), rest = pc % (kSl * G::BV);
+      Bq[bc * G::BCS + rest] = rb[i];
     }
-    // a group is 8 slices = this thread's 4 and its neighbour's
-    part += __shfl_xor(part, 1, 64);
-    if ((tid & 1) == 0) XS[bj * kGC + (bs >> 3)] = part;
+    if (tid < kNC * kGC) XS[tid] = rxs;
   };
 
-  // ---- accumulators: [matrix][tile][4 rows] --------------------------------
-  f32x4 acc[G::NMAT][2];
+  f32x4 acc[G::NMAT];
 #pragma unroll
-  for (int m = 0; m < G::NMAT; ++m)
-#pragma unroll
-    for (int t = 0; t < 2; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
+  for (int m = 0; m < G::NMAT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int ar = wave * 16 + col;  // A row of this lane within the tile
+
   auto compute_chunk = [&](int buf) {
     const uint32_t *A = lds + (size_t)buf * G::BUF_U32;
-    const uint32_t *B = A + G::A_U32;
-    const uint32_t *SB = B + G::B_U32;
-    const float *XS = reinterpret_cast<const float *>(SB + G::SB_U32);
+    const uint32_t *SB = A + G::A_U32;
+    const uint4 *Bq = reinterpret_cast<const uint4 *>(SB + G::SB_U32);
+    const float *XS = reinterpret_cast<const float *>(SB + G::SB_U32 + G::B_U32);
 #pragma unroll
     for (int gi = 0; gi < kGC; ++gi) {
-      bf16x8 av[G::NMAT][2];
+      f32x4 P[G::NMAT];
+#pragma unroll
+      for (int m = 0; m < G::NMAT; ++m) P[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int sl = 8 * gi + 4 * h + q;  // slice of this lane
+        bf16x8 bv[G::BV];
+#pragma unroll
+        for (int u = 0; u < G::BV; ++u)
+          bv[u] = __builtin_bit_cast(bf16x8, Bq[col * G::BCS + sl * G::BV + u]);
+#pragma unroll
+        for (int m = 0; m < G::NMAT; ++m) {
+          const uint32_t w = A[(m * kRT + ar) * G::RW + (BITS == 4 ? sl : (sl >> 1))];
+          const bf16x8 av = a_slice<BITS>(w, sl & 1);
+#pragma unroll
+          for (int u = 0; u < G::BV; ++u)
+            P[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[u], P[m], 0, 0, 0);
+        }
+      }
+      // element v of this lane: row 4 q + v of the wave's 16, B column col
+      const float X = XS[col * kGC + gi];
 #pragma unroll
       for (int m = 0; m < G::NMAT; ++m)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int sl = 8 * gi + 4 * h + q;  // slice of this lane
-          const uint32_t w = A[(m * kRT + ar) * G::RW + (BITS == 4 ? sl : (sl >> 1))];
-          av[m][h] = a_slice<BITS>(w, sl & 1);
+        for (int v = 0; v < 4; ++v) {
+          const uint32_t sb = SB[(m * kRT + wave * 16 + 4 * q + v) * kGC + gi];
+          acc[m][v] += bf16f(sb & 0xFFFFu) * (P[m][v] - 128.f * X) + bf16f(sb >> 16) * X;
         }
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        if (t >= ntiles) break;
-        const int bp = 16 * t + col;  // pair of this lane's B column
-        f32x4 P[G::NMAT];
-#pragma unroll
-        for (int m = 0; m < G::NMAT; ++m) P[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int sl = 8 * gi + 4 * h + q;
-          const uint32_t *src = B + bp * G::TS + sl * G::BV;
-          const bf16x8 bv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(src));
-#pragma unroll
-          for (int m = 0; m < G::NMAT; ++m)
-            P[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[m][h], bv, P[m], 0, 0, 0);
-          if (DOWN) {
-            const bf16x8 bl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(src + 4));
-#pragma unroll
-            for (int m = 0; m < G::NMAT; ++m)
-              P[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[m][h], bl, P[m], 0, 0, 0);
-          }
-        }
-        // output element v of this lane: row 4 q + v of the wave's 16, pair bp
-        const float X = XS[bp * kGC + gi];
-#pragma unroll
-        for (int m = 0; m < G::NMAT; ++m)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const uint32_t sb = SB[(m * kRT + wave * 16 + 4 * q + v) * kGC + gi];
-            acc[m][t][v] += bf16f(sb & 0xFFFFu) * (P[m][v] - 128.f * X) + bf16f(sb >> 16) * X;
-          }
-      }
     }
   };
 
@@ -401,23 +405,42 @@ __global__ void __launch_bounds__(256) k_grouped(GroupArgs a) {
   }
 
   // ---- epilogue -------------------------------------------------------------
+  const int orow = row0 + wave * 16 + 4 * q;  // first of this lane's 4 rows
+  if (DOWN) {
+    if (bvalid) {
+      const float4 o = make_float4(acc[0][0], acc[0][1], acc[0][2], acc[0][3]);
+      *reinterpret_cast<float4 *>(a.yd + (size_t)code * a.R + orow) = o;
+    }
+  } else {
+    // h for 4 rows; with the neighbour's 4 (lane + 16) they form the 8-row
+    // slice that lanes with even q write as the B operand of the down pass
+    float hv[4], hsum = 0.f;
+    uint32_t hi[4], lo[4];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int bp = 16 * t + col;
-    if (t < ntiles && bp < nn) {
-      const int code = pairs[bp];
-      float4 o;
-      float *ov = reinterpret_cast<float *>(&o);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        if (DOWN) {
-          ov[v] = acc[0][t][v];
-        } else {
-          const float g = acc[0][t][v], u = acc[G::NMAT - 1][t][v];
-          ov[v] = g / (1.f + expf(-g)) * u;
-        }
-      }
-      *reinterpret_cast<float4 *>(a.out + (size_t)code * a.R + row0 + wave * 16 + 4 * q) = o;
+    for (int v = 0; v < 4; ++v) {
+      const float g = acc[0][v], u = acc[1][v];
+      hv[v] = g / (1.f + expf(-g)) * u;
+      hi[v] = f2bf(hv[v]);
+      lo[v] = f2bf(hv[v] - bf16f(hi[v]));
+      hsum += bf16f(hi[v]) + bf16f(lo[v]);
+    }
+    const uint32_t h01 = hi[0] | (hi[1] << 16), h23 = hi[2] | (hi[3] << 16);
+    const uint32_t l01 = lo[0] | (lo[1] << 16), l23 = lo[2] | (lo[3] << 16);
+    const uint32_t nh01 = __shfl_down(h01, 16, 64), nh23 = __shfl_down(h23, 16, 64);
+    const uint32_t nl01 = __shfl_down(l01, 16, 64), nl23 = __shfl_down(l23, 16, 64);
+    if (bvalid && (q & 1) == 0) {
+      uint4 *dst = a.hb + ((size_t)code * (a.R / 8) + orow / 8) * 2;
+      dst[0] = b_order(make_uint4(h01, h23, nh01, nh23));
+      dst[1] = b_order(make_uint4(l01, l23, nl01, nl23));
+    }
+    // group sum of the tile's 64 rows (= one group of the down columns)
+    hsum += __shfl_xor(hsum, 16, 64);
+    hsum += __shfl_xor(hsum, 32, 64);
+    if (q == 0) s_hsum[wave][col] = hsum;
+    __syncthreads();
+    if (tid < 16 && tid < nn) {
+      const float t4 = s_hsum[0][tid] + s_hsum[1][tid] + s_hsum[2][tid] + s_hsum[3][tid];
+      a.hs[(size_t)pairs[tid] * (a.R / kGroup) + blockIdx.x] = t4;
     }
   }
 }
@@ -493,7 +516,10 @@ int launch_expert_forward_grouped(const moe_dims &d, const moe_layer &L, const u
   uint8_t *base = static_cast<uint8_t *>(ws);
   Ctrl *ctrl = reinterpret_cast<Ctrl *>(base + W.ctrl);
   int32_t *bk = reinterpret_cast<int32_t *>(base + W.bk);
-  float *h = reinterpret_cast<float *>(base + W.h);
+  uint4 *xb = reinterpret_cast<uint4 *>(base + W.xb);
+  float *xs = reinterpret_cast<float *>(base + W.xs);
+  uint4 *hb = reinterpret_cast<uint4 *>(base + W.hb);
+  float *hs = reinterpret_cast<float *>(base + W.hs);
   float *yd = reinterpret_cast<float *>(base + W.yd);
   const int maxB = grouped_max_buckets(d, T);
   hipStream_t st = S(stream);
@@ -509,15 +535,26 @@ int launch_expert_forward_grouped(const moe_dims &d, const moe_layer &L, const u
   ba.maxB = maxB;
   hipLaunchKernelGGL(k_bucket, dim3(1), dim3(1024), 0, st, ba);
 
+  XPrepArgs xa;
+  xa.x = x;
+  xa.xb = xb;
+  xa.xs = xs;
+  xa.T = T;
+  xa.H = d.hidden;
+  hipLaunchKernelGGL(k_xprep, dim3((unsigned)(((size_t)T * d.hidden / 8 + 255) / 256)), dim3(256),
+                     0, st, xa);
+
   const int nchunk_pairs = (T + kNC - 1) / kNC;  // a bucket holds at most T pairs
   GroupArgs gu;
-  gu.x = x;
-  gu.hin = nullptr;
+  gu.bop = xb;
+  gu.bsum = xs;
   gu.experts = L.experts;
   gu.shared = L.shared;
   gu.stride = L.expert_stride;
   gu.bk = bk;
-  gu.out = h;
+  gu.hb = hb;
+  gu.hs = hs;
+  gu.yd = nullptr;
   gu.R = d.inter;
   gu.C = d.hidden;
   gu.E = d.n_experts;
@@ -528,9 +565,11 @@ int launch_expert_forward_grouped(const moe_dims &d, const moe_layer &L, const u
   gu.off_sb0 = (int64_t)B.off[MOE_SEC_GATE_SB];
   gu.off_sb1 = (int64_t)B.off[MOE_SEC_UP_SB];
   GroupArgs dn = gu;
-  dn.x = nullptr;
-  dn.hin = h;
-  dn.out = yd;
+  dn.bop = hb;
+  dn.bsum = hs;
+  dn.hb = nullptr;
+  dn.hs = nullptr;
+  dn.yd = yd;
   dn.R = d.hidden;
   dn.C = d.inter;
   dn.off_q0 = dn.off_q1 = (int64_t)B.off[MOE_SEC_DOWN_Q];

@@ -50,13 +50,22 @@ WsLayout ws_layout(const moe_dims &d, int T) {
   W.h = o;
   // indexed by pair code t (K + 1) + slot on every path
   o = align_up(o + (size_t)T * (d.top_k + 1) * d.inter * 4, kAlign);
-  W.bk = o;
+  W.bk = W.xb = W.xs = W.hb = W.hs = W.yd = o;
   if (T >= 2) {
     const size_t maxB = (size_t)grouped_max_buckets(d, T);
+    const size_t P = (size_t)T * (d.top_k + 1);  // pair codes
     o = align_up(o + (2 + 2 * maxB + (size_t)T * slots) * 4, kAlign);
+    W.xb = o;
+    o = align_up(o + (size_t)T * d.hidden * 2, kAlign);
+    W.xs = o;
+    o = align_up(o + (size_t)T * (d.hidden / kGroup) * 4, kAlign);
+    W.hb = o;
+    o = align_up(o + P * d.inter * 4, kAlign);
+    W.hs = o;
+    o = align_up(o + P * (d.inter / kGroup) * 4, kAlign);
+    W.yd = o;
+    o = align_up(o + P * d.hidden * 4, kAlign);
   }
-  W.yd = o;
-  if (T >= 2) o = align_up(o + (size_t)T * (d.top_k + 1) * d.hidden * 4, kAlign);
   W.total = o;
   return W;
 }

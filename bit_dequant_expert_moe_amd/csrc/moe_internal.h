@@ -34,10 +34,13 @@ BlobLayout blob_layout(const moe_dims &d);
 //   ids        : int32 [T][K]
 //   w          : fp32 [T][K]
 //   h          : fp32 [T][K+1][I]   activations silu(g)*u per slot
-//   bk         : int32 buckets of the batched path (expert, offsets, pair codes)
-//   yd         : fp32 [T][K+1][H]   per-slot down projections of the batched path
+//   batched path (T >= 2) only:
+//   bk         : int32 buckets (expert, offsets, pair codes)
+//   xb, xs     : x as matrix-core B operand [T][H/8] x 16 B, group sums [T][H/64]
+//   hb, hs     : h as B operand [T][K+1][I/8] x 32 B (bf16 hi, lo), sums [T][K+1][I/64]
+//   yd         : fp32 [T][K+1][H]   per-slot down projections
 struct Ctrl {
-  uint32_t route_counter;  // blocks of the routing kernel that finished
+  uint32_t reserved;       // unused
   uint32_t err;            // sticky device error flags
   uint32_t pad[62];
 };
@@ -68,7 +71,7 @@ constexpr size_t kHTagOff = kTagOff + (size_t)kGroups * kMaxE * 8;
 constexpr size_t kHeaderBytes = kHTagOff + (size_t)kGroups * kFusedSlots * kFusedI * 8;
 
 struct WsLayout {
-  size_t ctrl, fctrl, logits_tag, h_tag, logits, ids, w, h, bk, yd, total;
+  size_t ctrl, fctrl, logits_tag, h_tag, logits, ids, w, h, bk, xb, xs, hb, hs, yd, total;
 };
 WsLayout ws_layout(const moe_dims &d, int T);
 

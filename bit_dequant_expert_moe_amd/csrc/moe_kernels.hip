@@ -9,9 +9,9 @@
 // FMA inner loop of the matrix-vector product.
 //
 // Kernels
-//   k_route        router GEMV (bf16 x bf16 -> fp32, v_dot2_f32_bf16); the
-//                  last block to finish selects the top-K per token and
-//                  writes the renormalised weights.
+//   k_router       router logits for T tokens on the matrix cores (bf16 x
+//                  bf16 -> fp32, v_mfma_f32_16x16x32_bf16).
+//   k_topk         one wave per token: top-K and the renormalised weights.
 //   k_gateup       gate and up rows of the selected experts and the shared
 //                  expert, SwiGLU epilogue; activations h to the workspace.
 //   k_down         down rows of every slot, weighted combine into y.
@@ -97,102 +97,105 @@ __device__ __forceinline__ float seg_dot_h(uint4 c, const uint32_t *hp) {
 }
 
 // ---------------------------------------------------------------------------
-// Routing
+// Routing: logits = W_r x on the matrix cores (bf16 x bf16 products are exact
+// in fp32, sums in fp32), then one wave per token selects the top-K.
 // ---------------------------------------------------------------------------
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
 struct RouteArgs {
   const uint16_t *router, *x;
   int32_t *ids;
   float *w, *logits_out, *logits;
-  Ctrl *ctrl;
   int H, E, K, T;
 };
 
-__global__ void __launch_bounds__(256) k_route(RouteArgs a) {
+// Block = 16 experts x 16 tokens; the 4 waves split the hidden dimension and
+// their partial tiles are summed in a fixed order.
+__global__ void __launch_bounds__(256) k_router(RouteArgs a) {
+  __shared__ f32x4_t s_part[4][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int e = blockIdx.x * 4 + wave;
-  if (e < a.E) {
-    const uint4 *wr = reinterpret_cast<const uint4 *>(a.router + (size_t)e * a.H);
-    const int nq = a.H / 8;
-    for (int t = 0; t < a.T; ++t) {
-      const uint4 *xr = reinterpret_cast<const uint4 *>(a.x + (size_t)t * a.H);
-      float acc = 0.f;
-      for (int i = lane; i < nq; i += 64) {
-        const uint4 wv = wr[i], xv = xr[i];
-        acc = dot2b(wv.x, xv.x, acc);
-        acc = dot2b(wv.y, xv.y, acc);
-        acc = dot2b(wv.z, xv.z, acc);
-        acc = dot2b(wv.w, xv.w, acc);
-      }
-      acc = group_sum(acc, 64);
-      if (lane == 0) {
-        a.logits[(size_t)t * a.E + e] = acc;
-        if (a.logits_out) a.logits_out[(size_t)t * a.E + e] = acc;
-      }
-    }
+  const int row = lane & 15, q = lane >> 4;
+  const int e0 = 16 * blockIdx.x, t0 = 16 * blockIdx.y;
+  const int e = e0 + row, t = t0 + row;
+  const int kw = a.H / 4;  // columns per wave
+  const uint4 *wr = reinterpret_cast<const uint4 *>(a.router + (size_t)(e < a.E ? e : 0) * a.H +
+                                                    (size_t)wave * kw + 8 * q);
+  const uint4 *xr = reinterpret_cast<const uint4 *>(a.x + (size_t)(t < a.T ? t : 0) * a.H +
+                                                    (size_t)wave * kw + 8 * q);
+  const bool ev = e < a.E, tv = t < a.T;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+  for (int k = 0; k < kw / 32; ++k) {
+    uint4 av = wr[4 * k], bv = xr[4 * k];
+    if (!ev) av = make_uint4(0, 0, 0, 0);
+    if (!tv) bv = make_uint4(0, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                  __builtin_bit_cast(bf16x8_t, bv), acc, 0, 0, 0);
   }
-  // The last block to finish selects the experts of every token.
-  __shared__ int s_last;
+  s_part[wave][lane] = acc;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    __threadfence();
-    const uint32_t prev = __hip_atomic_fetch_add(&a.ctrl->route_counter, 1u, __ATOMIC_ACQ_REL,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    s_last = prev == gridDim.x - 1;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  for (int t = wave; t < a.T; t += 4) {
-    const float *lt = a.logits + (size_t)t * a.E;
-    float v[kMaxE / 64];
+  if (wave == 0) {
+    f32x4_t r = s_part[0][lane];
 #pragma unroll
-    for (int j = 0; j < kMaxE / 64; ++j) {
-      const int idx = lane + 64 * j;
-      v[j] = idx < a.E ? __hip_atomic_load(lt + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                       : __builtin_nanf("");
+    for (int w = 1; w < 4; ++w) {
+      const f32x4_t p = s_part[w][lane];
+      r[0] += p[0];
+      r[1] += p[1];
+      r[2] += p[2];
+      r[3] += p[3];
     }
-    float sel_v[kMaxK];
-    int sel_i[kMaxK];
+    // element v of lane: expert e0 + 4 q + v, token t0 + row
+    if (t0 + row < a.T) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int ee = e0 + 4 * q + v;
+        if (ee < a.E) {
+          a.logits[(size_t)(t0 + row) * a.E + ee] = r[v];
+          if (a.logits_out) a.logits_out[(size_t)(t0 + row) * a.E + ee] = r[v];
+        }
+      }
+    }
+  }
+}
+
+// One wave per token: top-K of the logits (largest first; equal logits ->
+// lower index), weights = softmax over the selected logits.
+__global__ void __launch_bounds__(64) k_topk(RouteArgs a) {
+  const int t = blockIdx.x, lane = threadIdx.x;
+  const float *lt = a.logits + (size_t)t * a.E;
+  constexpr int NV = kMaxE / 64;
+  uint64_t key[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int idx = lane + 64 * j;
+    const float v = idx < a.E ? lt[idx] : __builtin_nanf("");
+    key[j] = ((uint64_t)f32_order_key(v) << 32) | (0xFFFFFFFFu - (uint32_t)idx);
+  }
+  float sel_v[kMaxK];
+  int sel_i[kMaxK];
+  for (int k = 0; k < a.K; ++k) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) best = key[j] > best ? key[j] : best;
+    const uint64_t m = wave_max_u64(best);
+    const uint32_t k32 = (uint32_t)(m >> 32);
+    sel_i[k] = m == 0 ? -1 : (int)(0xFFFFFFFFu - (uint32_t)m);
+    sel_v[k] = __uint_as_float((k32 & 0x80000000u) ? (k32 & 0x7FFFFFFFu) : ~k32);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) key[j] = key[j] == m ? 0 : key[j];
+  }
+  if (lane == 0) {
+    float den = 0.f, p[kMaxK];
     for (int k = 0; k < a.K; ++k) {
-      // largest logit; equal logits -> lower index; removed entries are NaN
-      float bv = -__builtin_inff();
-      int bi = 0x7FFFFFFF;
-#pragma unroll
-      for (int j = 0; j < kMaxE / 64; ++j) {
-        const int idx = lane + 64 * j;
-        if (v[j] > bv || (v[j] == bv && idx < bi)) {
-          bv = v[j];
-          bi = idx;
-        }
-      }
-      for (int off = 32; off > 0; off >>= 1) {
-        const float ov = __shfl_xor(bv, off, 64);
-        const int oi = __shfl_xor(bi, off, 64);
-        if (ov > bv || (ov == bv && oi < bi)) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-      sel_v[k] = bv;
-      sel_i[k] = bi;
-#pragma unroll
-      for (int j = 0; j < kMaxE / 64; ++j)
-        if (lane + 64 * j == bi) v[j] = __builtin_nanf("");
+      p[k] = expf(sel_v[k] - sel_v[0]);
+      den += p[k];
     }
-    if (lane == 0) {
-      float den = 0.f, p[kMaxK];
-      for (int k = 0; k < a.K; ++k) {
-        p[k] = expf(sel_v[k] - sel_v[0]);
-        den += p[k];
-      }
-      for (int k = 0; k < a.K; ++k) {
-        a.ids[(size_t)t * a.K + k] = sel_i[k];
-        a.w[(size_t)t * a.K + k] = p[k] / den;
-      }
+    for (int k = 0; k < a.K; ++k) {
+      a.ids[(size_t)t * a.K + k] = sel_i[k];
+      a.w[(size_t)t * a.K + k] = p[k] / den;
     }
   }
-  if (threadIdx.x == 0)
-    __hip_atomic_store(&a.ctrl->route_counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -430,12 +433,13 @@ int launch_route(const moe_dims &d, const uint16_t *router, const uint16_t *x, i
   a.w = w;
   a.logits_out = logits;
   a.logits = reinterpret_cast<float *>(base + W.logits);
-  a.ctrl = reinterpret_cast<Ctrl *>(base + W.ctrl);
   a.H = d.hidden;
   a.E = d.n_experts;
   a.K = d.top_k;
   a.T = T;
-  hipLaunchKernelGGL(k_route, dim3((d.n_experts + 3) / 4), dim3(256), 0, S(stream), a);
+  hipLaunchKernelGGL(k_router, dim3((d.n_experts + 15) / 16, (T + 15) / 16), dim3(256), 0,
+                     S(stream), a);
+  hipLaunchKernelGGL(k_topk, dim3(T), dim3(64), 0, S(stream), a);
   return (int)hipGetLastError();
 }
 
