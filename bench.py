@@ -39,12 +39,60 @@ def parse():
     ap.add_argument("--workload", default="stack60", choices=["stack60", "stack60_2bit", "batch64"])
     ap.add_argument("--layers", type=int, default=None, help="override layer count (testing)")
     ap.add_argument("--tokens", type=int, default=None, help="override distinct tokens")
-    ap.add_argument("--cpu-layers", type=int, default=20,
+    ap.add_argument("--cpu-layers", type=int, default=60,
                     help="layers of the CPU oracle sample (one token)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--check-layers", type=int, default=3,
                     help="layers of token 0 checked against the oracle")
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="MB",
+                    help="only run a plain device copy of MB megabytes (calibrates the HBM "
+                         "byte counters of the profiler) and exit")
     return ap.parse_args()
+
+
+KERNEL_SOURCES = ["bit_dequant_expert_moe_amd/csrc/moe_fused.hip",
+                  "bit_dequant_expert_moe_amd/csrc/moe_device.h",
+                  "bit_dequant_expert_moe_amd/csrc/moe_internal.h"]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(name):
+    """HBM bytes per launch from the committed profiler counter summary
+    profiles/<name>_hbm_counters.txt (FETCH_SIZE and WRITE_SIZE, each scaled by
+    what the counter reads for a plain copy of known size).  None when the
+    summary is missing or was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", name + "_hbm_counters.txt")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        if line.startswith("traffic_json:"):
+            rec = json.loads(line.split(":", 1)[1])
+            if rec.get("kernel_source_sha256") == kernel_source_hash():
+                return rec
+    return None
+
+
+def calib_copy(mb):
+    """A plain copy kernel of known size: reads and writes mb * 2^20 bytes per
+    launch, so FETCH_SIZE / WRITE_SIZE of the profiler can be scaled to bytes."""
+    import torch
+    n = mb << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes": n, "launches": 4}), flush=True)
 
 
 def main():
@@ -53,6 +101,8 @@ def main():
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.calib_copy:
+        return calib_copy(args.calib_copy)
     import torch
     import bit_dequant_expert_moe_amd as moe
     import synth
@@ -152,11 +202,14 @@ def main():
                      for t in range(1, ntok) for l in range(nl)]) if ntok > 1 else float("nan")
     log("expert reuse between consecutive tokens: %.3f" % reuse)
 
-    # ---- per-launch duration of the layer call, with HIP events ---------------
-    # A spin kernel holds the stream while all launches are enqueued, so the
-    # event intervals measure back-to-back device execution.  On the
-    # single-token path one moe_layer_decode is one kernel (k_layer1).
+    # ---- per-launch duration of the layer call ---------------------------------
+    # On the single-token path one moe_layer_decode is one kernel (k_layer1) and
+    # a token graph is nl of them back to back, so the timed region above (HIP
+    # events on the replay stream) divided by the launches it holds is the
+    # average launch duration.  An isolated launch (events around each call)
+    # is reported beside it: the events themselves add a gap per launch.
     fused = os.environ.get("MOE_DISABLE_FUSED", "0") != "1"
+    layer_us = ms_per_step * 1e3 / nl
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(nl)]
     t_tok = 1 % ntok
@@ -167,11 +220,12 @@ def main():
                              wts[t_tok, l], ws, ws_bytes, sp)
         ev[l][1].record()
     torch.cuda.synchronize()
-    layer_us = float(np.mean([ev[l][0].elapsed_time(ev[l][1]) * 1e3 for l in range(nl)]))
+    iso_us = float(np.mean([ev[l][0].elapsed_time(ev[l][1]) * 1e3 for l in range(nl)]))
     launch_bytes = router_bytes_tok // nl + (wl.K + wl.has_shared) * blob
     achieved = launch_bytes / (layer_us * 1e-6) / 1e9
-    log("layer call %.2f us/launch -> %.0f GB/s of algorithmic bytes (%d B per launch)" % (
-        layer_us, achieved, launch_bytes))
+    log("layer call %.2f us/launch in the token graphs (%.2f us isolated) -> %.0f GB/s of "
+        "algorithmic bytes (%d B per launch)" % (layer_us, iso_us, achieved, launch_bytes))
+    traffic = measured_traffic("k_layer1_%s" % wl.name) if fused else None
     err = moe.moe_get_device_error(ws, sp)
     if err:
         log("device error flags: %d" % err)
@@ -251,8 +305,10 @@ def main():
                      "kernel": "k_layer1 (moe_layer_decode)" if fused else
                                "moe_layer_decode (k_route + k_gateup + k_down)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "avg_launch_us": layer_us, "bytes_per_launch": launch_bytes},
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic["traffic_bytes_per_launch"] if traffic else None,
+                     "avg_launch_us": layer_us, "isolated_launch_us": iso_us,
+                     "bytes_per_launch": launch_bytes},
         "device_error_flags": err,
         "oracle_check_max_rel_err": check,
         "cpu_baseline": cpu,
