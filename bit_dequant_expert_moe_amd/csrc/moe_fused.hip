@@ -94,6 +94,25 @@ __device__ __forceinline__ uint4 ld_coh16(const void *base, uint32_t byte_off) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// Weight loads through a buffer resource of the blob: the per-lane byte
+// offsets are the same 32-bit values for every expert, only the (scalar)
+// resource changes, which keeps 64-bit address arithmetic out of the vector
+// registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t blob_rsrc(const uint8_t *base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), 0, 0x7fffffff, 0x00020000);
+}
+__device__ __forceinline__ uint4 bld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint2 bld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+  return make_uint2(v[0], v[1]);
+}
+__device__ __forceinline__ uint32_t bld4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+
 template <int BITS, int H, int I, int K>
 struct Geo {
   static constexpr int COLS = 128 / BITS;           // columns per 16-byte segment
@@ -104,16 +123,17 @@ struct Geo {
   static constexpr int RCH = H / 8;                 // 16-byte chunks per router row
   static constexpr int RXC = RCH / kNT;             // router x chunks per thread
   static constexpr int GU_ROWS = I / kG;            // gate/up rows per workgroup and slot
-  static constexpr int SEG_D = I * BITS / 128;      // segments per down row
-  static constexpr int LPR = SEG_D < 64 ? SEG_D : 64;  // lanes per down row
+  static constexpr int DCOLS = 32;                  // down codes per lane (one load)
+  static constexpr int DWORDS = DCOLS * BITS / 32;  // their code words (4 or 2)
+  static constexpr int LPR = I / DCOLS;             // lanes per down row
   static constexpr int RPL = 64 / LPR;              // down rows per wave-wide load
-  static constexpr int NSEGD = SEG_D / LPR;         // segments per lane per down row
+  static constexpr int NSEGD = 1;
   static constexpr int D_ROWS = H / kG;             // down rows per workgroup
   static constexpr int D_ROWS_W = D_ROWS / kDownWaves;  // per down wave
   static constexpr int DLD = D_ROWS_W / RPL;        // down loads per lane per slot
   static_assert(LSEG >= 1 && SEG_X % 64 == 0, "gate/up row must span a wave");
   static_assert(GU_ROWS == kGuWaves, "one gate/up row per gate/up wave and slot");
-  static_assert(NSEGD == 1, "one down segment per lane");
+  static_assert(LPR <= 64 && 64 % LPR == 0, "a down row within one wave");
   static_assert(DLD >= 1 && D_ROWS_W % RPL == 0, "down rows must tile the waves");
   static_assert(RXC >= 1 && RCH % kNT == 0, "router row must span the workgroup");
   static_assert(SEG_X <= 64 * kGuWaves, "one x segment per gate/up thread");
@@ -136,29 +156,23 @@ struct FusedArgs {
   int64_t off_gq, off_uq, off_dq, off_gsb, off_usb, off_dsb;
 };
 
-// sum_c q_c h_c over one 16-byte segment of down codes, fp32.
+// sum_c q_c h_c over the codes of one 32-bit word (8 at 4 bits, 16 at 2 bits)
+// of a down row, fp32; hv holds the word's activations.
 template <int BITS>
-__device__ __forceinline__ float seg_dot_f32(uint4 c, const float *h) {
-  float acc = 0.f;
-  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+__device__ __forceinline__ float word_dot_f32(uint32_t u, const float *hv, float acc) {
+  if (BITS == 4) {
+    const uint32_t lo = u & 0x0F0F0F0Fu, hi = (u >> 4) & 0x0F0F0F0Fu;
 #pragma unroll
-  for (int wd = 0; wd < 4; ++wd) {
-    const uint32_t u = w[wd];
-    if (BITS == 4) {
-      const uint32_t lo = u & 0x0F0F0F0Fu, hi = (u >> 4) & 0x0F0F0F0Fu;
+    for (int j = 0; j < 4; ++j) {
+      acc = fmaf((float)((lo >> (8 * j)) & 0xFFu), hv[2 * j], acc);
+      acc = fmaf((float)((hi >> (8 * j)) & 0xFFu), hv[2 * j + 1], acc);
+    }
+  } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc = fmaf((float)((lo >> (8 * j)) & 0xFFu), h[8 * wd + 2 * j], acc);
-        acc = fmaf((float)((hi >> (8 * j)) & 0xFFu), h[8 * wd + 2 * j + 1], acc);
-      }
-    } else {
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t m = (u >> (2 * k)) & 0x03030303u;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t m = (u >> (2 * k)) & 0x03030303u;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc = fmaf((float)((m >> (8 * j)) & 0xFFu), h[16 * wd + 4 * j + k], acc);
-      }
+      for (int j = 0; j < 4; ++j) acc = fmaf((float)((m >> (8 * j)) & 0xFFu), hv[4 * j + k], acc);
     }
   }
   return acc;
@@ -264,14 +278,24 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
       xr[t] = *reinterpret_cast<const uint4 *>(a.x + (size_t)(xs % Gm::SEG_X) * COLS + 8 * t);
     uint4 gq[NSL][LSEG], uq[NSL][LSEG];
     uint32_t gsb[NSL][LSEG], usb[NSL][LSEG];
+    // byte offsets inside a blob, the same for every expert
+    uint32_t o_gq[LSEG], o_uq[LSEG], o_gsb[LSEG], o_usb[LSEG];
+#pragma unroll
+    for (int j = 0; j < LSEG; ++j) {
+      const int sg = lane + 64 * j;
+      o_gq[j] = (uint32_t)(a.off_gq + (int64_t)r * rbytes + sg * 16);
+      o_uq[j] = (uint32_t)(a.off_uq + (int64_t)r * rbytes + sg * 16);
+      o_gsb[j] = (uint32_t)(a.off_gsb + ((int64_t)r * groups + sg * COLS / kGroup) * 4);
+      o_usb[j] = (uint32_t)(a.off_usb + ((int64_t)r * groups + sg * COLS / kGroup) * 4);
+    }
     auto load_rows = [&](int slot, const uint8_t *bl) {
+      const __amdgpu_buffer_rsrc_t rs = blob_rsrc(bl);
 #pragma unroll
       for (int j = 0; j < LSEG; ++j) {
-        const int sg = lane + 64 * j;
-        gq[slot][j] = ldg16(bl + a.off_gq + r * rbytes + (size_t)sg * 16);
-        uq[slot][j] = ldg16(bl + a.off_uq + r * rbytes + (size_t)sg * 16);
-        gsb[slot][j] = reinterpret_cast<const uint32_t *>(bl + a.off_gsb)[(size_t)r * groups + sg * COLS / kGroup];
-        usb[slot][j] = reinterpret_cast<const uint32_t *>(bl + a.off_usb)[(size_t)r * groups + sg * COLS / kGroup];
+        gq[slot][j] = bld16(rs, o_gq[j]);
+        uq[slot][j] = bld16(rs, o_uq[j]);
+        gsb[slot][j] = bld4(rs, o_gsb[j]);
+        usb[slot][j] = bld4(rs, o_usb[j]);
       }
       // keep the slots' loads in issue order = consumption order (the load
       // counter completes in order)
@@ -357,7 +381,7 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
     int eid[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      eid[k] = s_ids[k];
+      eid[k] = __builtin_amdgcn_readfirstlane(s_ids[k]);
       const bool ok = eid[k] >= 0 && eid[k] < a.E;
       // an invalid id reads expert 0 and contributes 0
       load_rows(k, a.experts + (size_t)(ok ? eid[k] : 0) * a.stride);
@@ -380,11 +404,23 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
       rows[ld] = b * Gm::D_ROWS + dw * Gm::D_ROWS_W + ld * Gm::RPL + lane / Gm::LPR;
     uint4 dq[NSL][Gm::DLD];
     uint32_t dsb[NSL][Gm::DLD];
+    uint32_t o_dq[Gm::DLD], o_dsb[Gm::DLD];
+#pragma unroll
+    for (int ld = 0; ld < Gm::DLD; ++ld) {
+      o_dq[ld] = (uint32_t)(a.off_dq + (int64_t)rows[ld] * rbytes + seg * Gm::DWORDS * 4);
+      o_dsb[ld] = (uint32_t)(a.off_dsb + ((int64_t)rows[ld] * groups + seg * Gm::DCOLS / kGroup) * 4);
+    }
     auto load_rows = [&](int slot, const uint8_t *bl) {
+      const __amdgpu_buffer_rsrc_t rs = blob_rsrc(bl);
 #pragma unroll
       for (int ld = 0; ld < Gm::DLD; ++ld) {
-        dq[slot][ld] = ldg16(bl + a.off_dq + rows[ld] * rbytes + (size_t)seg * 16);
-        dsb[slot][ld] = reinterpret_cast<const uint32_t *>(bl + a.off_dsb)[(size_t)rows[ld] * groups + seg * COLS / kGroup];
+        if (Gm::DWORDS == 4) {
+          dq[slot][ld] = bld16(rs, o_dq[ld]);
+        } else {
+          const uint2 v = bld8(rs, o_dq[ld]);
+          dq[slot][ld] = make_uint4(v.x, v.y, 0u, 0u);
+        }
+        dsb[slot][ld] = bld4(rs, o_dsb[ld]);
       }
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -557,7 +593,7 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
     float wk[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      eid[k] = s_ids[k];
+      eid[k] = __builtin_amdgcn_readfirstlane(s_ids[k]);
       wk[k] = s_w[k];
       const bool ok = eid[k] >= 0 && eid[k] < a.E;
       load_rows(k, a.experts + (size_t)(ok ? eid[k] : 0) * a.stride);
@@ -576,23 +612,37 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
     auto down = [&](int slot, float wkk) {
       if (xchg) exchange_until(slot);
       else wait_lds(&s_hready[slot], 1u);
-      float hv[COLS];
+      // one code word's activations are read from LDS at a time
+      constexpr int CPW = 32 / BITS;
+      float q[Gm::DLD];
 #pragma unroll
-      for (int t = 0; t < COLS / 4; ++t) {
-        const float4 v = *reinterpret_cast<const float4 *>(&s_hb[slot][seg * COLS + 4 * t]);
-        hv[4 * t] = v.x;
-        hv[4 * t + 1] = v.y;
-        hv[4 * t + 2] = v.z;
-        hv[4 * t + 3] = v.w;
-      }
+      for (int ld = 0; ld < Gm::DLD; ++ld) q[ld] = 0.f;
       float Hs = 0.f;
 #pragma unroll
-      for (int c = 0; c < COLS; ++c) Hs += hv[c];
+      for (int wd = 0; wd < Gm::DWORDS; ++wd) {
+        float hv[CPW];
+#pragma unroll
+        for (int t = 0; t < CPW / 4; ++t) {
+          const float4 v = *reinterpret_cast<const float4 *>(&s_hb[slot][seg * Gm::DCOLS + CPW * wd + 4 * t]);
+          hv[4 * t] = v.x;
+          hv[4 * t + 1] = v.y;
+          hv[4 * t + 2] = v.z;
+          hv[4 * t + 3] = v.w;
+        }
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) Hs += hv[c];
+#pragma unroll
+        for (int ld = 0; ld < Gm::DLD; ++ld) {
+          const uint4 c4 = dq[slot][ld];
+          const uint32_t u = wd == 0 ? c4.x : wd == 1 ? c4.y : wd == 2 ? c4.z : c4.w;
+          q[ld] = word_dot_f32<BITS>(u, hv, q[ld]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
       for (int ld = 0; ld < Gm::DLD; ++ld) {
-        const float q = seg_dot_f32<BITS>(dq[slot][ld], hv);
         const uint32_t sb = dsb[slot][ld];
-        acc[ld] += wkk * (bf16f(sb & 0xFFFFu) * q + bf16f(sb >> 16) * Hs);
+        acc[ld] += wkk * (bf16f(sb & 0xFFFFu) * q[ld] + bf16f(sb >> 16) * Hs);
       }
     };
     if (a.has_shared) down(K, 1.f);
