@@ -349,13 +349,24 @@ def bench_batch(args, wl):
     for b in range(nb):
         moe.moe_layer_decode(dims, L, xs[b], wl.T, y, ids[b], wts[b], ws, wsb, sp)
     torch.cuda.synchronize()
+    # one graph per batch (route, bucket, x staging, grouped GEMMs, combine)
+    graphs = []
+    cs = torch.cuda.Stream()
+    with torch.cuda.stream(cs):
+        for b in range(nb):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cs):
+                moe.moe_layer_decode(dims, L, xs[b], wl.T, y, ids[b], wts[b], ws, wsb,
+                                     torch.cuda.current_stream().cuda_stream)
+            graphs.append(g)
+    torch.cuda.synchronize()
     for i in range(args.warmup):
-        moe.moe_layer_decode(dims, L, xs[i % nb], wl.T, y, ids[i % nb], wts[i % nb], ws, wsb, sp)
+        graphs[i % nb].replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(args.steps):
-        moe.moe_layer_decode(dims, L, xs[i % nb], wl.T, y, ids[i % nb], wts[i % nb], ws, wsb, sp)
+        graphs[i % nb].replay()
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps

@@ -284,47 +284,58 @@ __global__ void __launch_bounds__(256) k_grouped(GroupArgs a) {
   const bool bvalid = col < nn;
 
   // ---- per chunk: A pieces, scales, B columns and their sums to LDS ---------
-  uint4 ra[G::APT];
-  uint4 rsb = make_uint4(0, 0, 0, 0);
-  uint4 rb[G::BPT];
-  float rxs = 0.f;
-  auto load_chunk = [&](int c) {
+  // Two register sets hold the next two chunks in flight while the current
+  // one is computed from LDS (the pass is bound by bytes in flight).
+  struct Regs {
+    uint4 ra[G::APT];
+    uint4 rsb;
+    uint4 rb[G::BPT];
+    float rxs;
+  };
+  // B rows of this thread's pieces, resolved once: a load whose address
+  // depends on another load inside the pipeline would wait for every load
+  // issued before it (loads complete in order)
+  int brow_b[G::BPT], brow_s = -1;
+#pragma unroll
+  for (int i = 0; i < G::BPT; ++i) {
+    const int bc = (tid + 256 * i) / (kSl * G::BV);
+    brow_b[i] = -1;
+    if (bc < nn) {
+      const int pcode = pairs[bc];
+      brow_b[i] = DOWN ? pcode : pcode / a.K1;
+    }
+  }
+  if (tid < kNC * kGC && tid / kGC < nn) {
+    const int pcode = pairs[tid / kGC];
+    brow_s = DOWN ? pcode : pcode / a.K1;
+  }
+  auto load_chunk = [&](int c, Regs &R) {
 #pragma unroll
     for (int i = 0; i < G::APT; ++i) {
       const int pc = tid + 256 * i;
       const int mat = pc / (kRT * G::PPR), rr = (pc / G::PPR) % kRT, c16 = pc % G::PPR;
       const int64_t off = mat ? a.off_q1 : a.off_q0;
-      ra[i] = *reinterpret_cast<const uint4 *>(blob + off + (size_t)(row0 + rr) * rbytes +
-                                              (size_t)c * (kKC * BITS / 8) + c16 * 16);
+      R.ra[i] = *reinterpret_cast<const uint4 *>(blob + off + (size_t)(row0 + rr) * rbytes +
+                                                (size_t)c * (kKC * BITS / 8) + c16 * 16);
     }
+    R.rsb = make_uint4(0, 0, 0, 0);
     if (tid < G::NMAT * kRT) {
       const int mat = tid / kRT, rr = tid % kRT;
       const int64_t off = mat ? a.off_sb1 : a.off_sb0;
-      rsb = *reinterpret_cast<const uint4 *>(blob + off +
-                                            ((size_t)(row0 + rr) * groups + (size_t)c * kGC) * 4);
+      R.rsb = *reinterpret_cast<const uint4 *>(blob + off +
+                                              ((size_t)(row0 + rr) * groups + (size_t)c * kGC) * 4);
     }
 #pragma unroll
     for (int i = 0; i < G::BPT; ++i) {
-      const int pc = tid + 256 * i;
-      const int bc = pc / (kSl * G::BV), rest = pc % (kSl * G::BV);
-      rb[i] = make_uint4(0, 0, 0, 0);
-      if (bc < nn) {
-        const int pcode = pairs[bc];
-        const int brow = DOWN ? pcode : pcode / a.K1;
-        rb[i] = a.bop[((size_t)brow * nslices + (size_t)c * kSl) * G::BV + rest];
-      }
+      const int rest = (tid + 256 * i) % (kSl * G::BV);
+      R.rb[i] = make_uint4(0, 0, 0, 0);
+      if (brow_b[i] >= 0)
+        R.rb[i] = a.bop[((size_t)brow_b[i] * nslices + (size_t)c * kSl) * G::BV + rest];
     }
-    if (tid < kNC * kGC) {
-      const int bc = tid / kGC, gi = tid % kGC;
-      rxs = 0.f;
-      if (bc < nn) {
-        const int pcode = pairs[bc];
-        const int brow = DOWN ? pcode : pcode / a.K1;
-        rxs = a.bsum[(size_t)brow * groups + c * kGC + gi];
-      }
-    }
+    R.rxs = 0.f;
+    if (brow_s >= 0) R.rxs = a.bsum[(size_t)brow_s * groups + c * kGC + tid % kGC];
   };
-  auto store_chunk = [&](int buf) {
+  auto store_chunk = [&](int buf, const Regs &R) {
     uint32_t *A = lds + (size_t)buf * G::BUF_U32;
     uint32_t *SB = A + G::A_U32;
     uint4 *Bq = reinterpret_cast<uint4 *>(SB + G::SB_U32);
@@ -334,19 +345,19 @@ __global__ void __launch_bounds__(256) k_grouped(GroupArgs a) {
       const int pc = tid + 256 * i;
       const int mat = pc / (kRT * G::PPR), rr = (pc / G::PPR) % kRT, c16 = pc % G::PPR;
       uint32_t *dst = A + (mat * kRT + rr) * G::RW + c16 * 4;
-      dst[0] = ra[i].x;
-      dst[1] = ra[i].y;
-      dst[2] = ra[i].z;
-      dst[3] = ra[i].w;
+      dst[0] = R.ra[i].x;
+      dst[1] = R.ra[i].y;
+      dst[2] = R.ra[i].z;
+      dst[3] = R.ra[i].w;
     }
-    if (tid < G::NMAT * kRT) *reinterpret_cast<uint4 *>(SB + tid * kGC) = rsb;
+    if (tid < G::NMAT * kRT) *reinterpret_cast<uint4 *>(SB + tid * kGC) = R.rsb;
 #pragma unroll
     for (int i = 0; i < G::BPT; ++i) {
       const int pc = tid + 256 * i;
       const int bc = pc / (kSl * G::BV), rest = pc % (kSl * G::BV);
-      Bq[bc * G::BCS + rest] = rb[i];
+      Bq[bc * G::BCS + rest] = R.rb[i];
     }
-    if (tid < kNC * kGC) XS[tid] = rxs;
+    if (tid < kNC * kGC) XS[tid] = R.rxs;
   };
 
   f32x4 acc[G::NMAT];
@@ -393,15 +404,24 @@ __global__ void __launch_bounds__(256) k_grouped(GroupArgs a) {
   };
 
   // ---- software pipeline over the column chunks ----------------------------
-  load_chunk(0);
-  store_chunk(0);
+  // chunk c is computed from LDS buffer c & 1 while chunks c + 1 and c + 2
+  // are in flight in the register sets (nchunks is even)
+  Regs R0, R1;
+  load_chunk(0, R0);
+  if (nchunks > 1) load_chunk(1, R1);
+  store_chunk(0, R0);
   __syncthreads();
-  for (int c = 0; c < nchunks; ++c) {
-    const int buf = c & 1;
-    if (c + 1 < nchunks) load_chunk(c + 1);
-    compute_chunk(buf);
-    if (c + 1 < nchunks) store_chunk(buf ^ 1);
+  for (int c = 0; c < nchunks; c += 2) {
+    if (c + 2 < nchunks) load_chunk(c + 2, R0);
+    compute_chunk(0);
+    if (c + 1 < nchunks) store_chunk(1, R1);
     __syncthreads();
+    if (c + 1 < nchunks) {
+      if (c + 3 < nchunks) load_chunk(c + 3, R1);
+      compute_chunk(1);
+      if (c + 2 < nchunks) store_chunk(0, R0);
+      __syncthreads();
+    }
   }
 
   // ---- epilogue -------------------------------------------------------------
@@ -483,8 +503,11 @@ __global__ void __launch_bounds__(256) k_combine(CombineArgs a) {
 
 inline hipStream_t S(void *s) { return static_cast<hipStream_t>(s); }
 
+// Allows `bytes` of dynamic LDS for kernel f; the default cap (64 KB) needs
+// no attribute call (a runtime call per launch that the common sizes skip).
 template <typename F>
 int allow_lds(F *f, size_t bytes) {
+  if (bytes <= 64 * 1024) return 0;
   return (int)hipFuncSetAttribute(reinterpret_cast<const void *>(f),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
