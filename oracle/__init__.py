@@ -105,6 +105,14 @@ def lib():
         L.or_expert_forward.restype = None
         L.or_expert_forward.argtypes = [dp, ctypes.POINTER(_u8p), _u8p, _u16p, ctypes.c_int32,
                                         _i32p, _f64p, _f64p]
+        L.or_f64_to_bf16.restype = ctypes.c_uint16
+        L.or_f64_to_bf16.argtypes = [ctypes.c_double]
+        L.or_rmsnorm_bf16.restype = None
+        L.or_rmsnorm_bf16.argtypes = [ctypes.c_int64, _f32p, ctypes.c_double, _u16p]
+        L.or_residual_layer.restype = None
+        L.or_residual_layer.argtypes = [dp, _u16p, ctypes.POINTER(_u8p), _u8p, _f32p,
+                                        ctypes.c_int32, _f64p, _u16p, _f64p, _i32p, _f64p,
+                                        _f64p, _f64p]
         _lib = L
     return _lib
 
@@ -268,3 +276,49 @@ def expert_forward(d: Dims, blobs, shared, x: np.ndarray, ids: np.ndarray, w: np
                             _p(x, _u16p), T, _p(ids, _i32p), _p(w, _f64p), _p(y, _f64p))
     del keep
     return y
+
+
+RMS_EPS = 1e-6
+
+
+def f64_to_bf16(v: float) -> int:
+    """Nearest bf16 bit pattern of a double (via float, ties to even)."""
+    return int(lib().or_f64_to_bf16(float(v)))
+
+
+def rmsnorm_bf16(r: np.ndarray, eps: float = RMS_EPS) -> np.ndarray:
+    """x = bf16(r / sqrt(mean(r^2) + eps)) per row of an fp32 [T][n] array."""
+    r = _c(r, np.float32)
+    r2 = r.reshape(-1, r.shape[-1])
+    x = np.empty(r2.shape, dtype=np.uint16)
+    for t in range(r2.shape[0]):
+        lib().or_rmsnorm_bf16(r2.shape[1], _p(r2[t], _f32p), eps, _p(x[t], _u16p))
+    return x.reshape(r.shape)
+
+
+def residual_layer(d: Dims, router: np.ndarray, blobs, shared, r: np.ndarray):
+    """One MoE layer on the fp32 residual stream r [T][H]: x = rmsnorm(r)
+    (bf16), y = layer(x), r_out = r + y.  blobs as in layer().  Returns
+    r_out (float64), x (bf16 bits), y, ids, w, logits, gap."""
+    router = _c(router, np.uint16)
+    r = _c(r, np.float32).reshape(-1, d.H)
+    T = r.shape[0]
+    x = rmsnorm_bf16(r)
+    ids0, _, _, _ = route(d, router, x)
+    if callable(blobs):
+        blobs = {int(e): blobs(int(e)) for e in np.unique(ids0)}
+    arr, keep = _blob_table(d, blobs)
+    sh = _c(shared, np.uint8) if d.has_shared else None
+    r_out = np.empty((T, d.H), dtype=np.float64)
+    xo = np.empty((T, d.H), dtype=np.uint16)
+    y = np.empty((T, d.H), dtype=np.float64)
+    ids = np.empty((T, d.K), dtype=np.int32)
+    w = np.empty((T, d.K), dtype=np.float64)
+    logits = np.empty((T, d.E), dtype=np.float64)
+    gap = np.empty(T, dtype=np.float64)
+    lib().or_residual_layer(ctypes.byref(d.c()), _p(router, _u16p), arr,
+                            _p(sh, _u8p) if sh is not None else None, _p(r, _f32p), T,
+                            _p(r_out, _f64p), _p(xo, _u16p), _p(y, _f64p), _p(ids, _i32p),
+                            _p(w, _f64p), _p(logits, _f64p), _p(gap, _f64p))
+    del keep
+    return r_out, xo, y, ids, w, logits, gap

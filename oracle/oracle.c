@@ -336,3 +336,44 @@ void or_expert_forward(const or_dims *d, const uint8_t *const *blobs, const uint
   free(xd);
   free(ye);
 }
+
+/* ---- residual stream and pre-MoE norm --------------------------------------
+ * "Flash-MoE: Running a 397B Parameter Model on a Laptop" (hysenlabs.com),
+ * section "How the SSD expert streaming pipeline works": the layer's last
+ * command does the expert forward "plus combine and norm".  Reading taken:
+ * the MoE output is added to an fp32 residual stream r, and the next MoE
+ * input is its RMS normalisation without a gain,
+ *     x_c = r_c / sqrt(mean_c r_c^2 + 1e-6),
+ * rounded to bf16 (the MoE input format). */
+
+/* Round a double to the nearest bf16 (ties to even), via float: the double
+ * -> float conversion rounds to nearest, then the float's upper half is
+ * rounded to nearest even. */
+uint16_t or_f64_to_bf16(double v) {
+  float f = (float)v;
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+/* x = bf16(r / sqrt(mean(r^2) + eps)) for one token of n values. */
+void or_rmsnorm_bf16(int64_t n, const float *r, double eps, uint16_t *x) {
+  double ss = 0.0;
+  for (int64_t c = 0; c < n; ++c) ss += (double)r[c] * (double)r[c];
+  const double inv = 1.0 / sqrt(ss / (double)n + eps);
+  for (int64_t c = 0; c < n; ++c) x[c] = or_f64_to_bf16((double)r[c] * inv);
+}
+
+/* One layer on the residual stream for T tokens: x = rmsnorm(r) (bf16),
+ * y = layer(x), r_out = r + y.  Outputs as or_layer, plus x [T][H] and
+ * r_out [T][H] (double). */
+void or_residual_layer(const or_dims *d, const uint16_t *router, const uint8_t *const *blobs,
+                       const uint8_t *shared, const float *r, int32_t T, double *r_out,
+                       uint16_t *x, double *y, int32_t *ids, double *w, double *logits,
+                       double *gap) {
+  const int64_t H = d->H;
+  for (int32_t t = 0; t < T; ++t) or_rmsnorm_bf16(H, r + (int64_t)t * H, 1e-6, x + (int64_t)t * H);
+  or_layer(d, router, blobs, shared, x, T, y, ids, w, logits, gap);
+  for (int64_t i = 0; i < (int64_t)T * H; ++i) r_out[i] = (double)r[i] + y[i];
+}

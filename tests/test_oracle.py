@@ -389,3 +389,64 @@ def test_generated_blob_ranges_through_oracle_parser(bits):
     chi2 = float(np.sum((hist - expect) ** 2 / expect))
     assert chi2 < 60  # dof 15 (or 3): far below this for a uniform source
     assert np.isfinite(W).all() and np.isfinite(G).all()
+
+
+# ---- residual stream and pre-MoE norm -------------------------------------------
+
+def test_f64_to_bf16_rounds_to_nearest_even():
+    # bf16 keeps 8 significant bits: around 1.0 the spacing is 2^-7
+    assert oracle.f64_to_bf16(1.0) == 0x3F80
+    assert oracle.f64_to_bf16(1.0 + 2.0 ** -8) == 0x3F80        # tie -> even (1.0)
+    assert oracle.f64_to_bf16(1.0 + 3 * 2.0 ** -8) == 0x3F82    # tie -> even (1 + 2^-6)
+    assert oracle.f64_to_bf16(1.0 + 2.0 ** -8 + 2.0 ** -20) == 0x3F81  # above the tie
+    assert oracle.f64_to_bf16(-2.5) == 0xC020
+
+
+def test_rmsnorm_hand_worked():
+    # r = (3, 4, 0, 0): mean r^2 = 25/4, rms = 2.5, x = (1.2, 1.6, 0, 0);
+    # bf16(1.2) = 1.203125 (0x3F9A), bf16(1.6) = 1.6015625 (0x3FCD) by hand
+    x = oracle.rmsnorm_bf16(np.array([3.0, 4.0, 0.0, 0.0], np.float32))
+    assert x.tolist() == [0x3F9A, 0x3FCD, 0, 0]
+
+
+def test_rmsnorm_constant_and_sign():
+    # a constant vector c has rms |c|: x = sign(c) / sqrt(1 + eps / c^2) -> +-1.0 in bf16
+    for c in (2.5, -0.75, 1000.0):
+        x = oracle.rmsnorm_bf16(np.full(256, c, np.float32))
+        assert set(x.tolist()) == {0x3F80 if c > 0 else 0xBF80}
+
+
+def test_rmsnorm_unit_rms_and_scale_invariance():
+    rng = np.random.default_rng(7)
+    r = (rng.standard_normal(4096) * 37.0).astype(np.float32)
+    x = synth.bf16_to_f32(oracle.rmsnorm_bf16(r)).astype(np.float64)
+    # mean of x^2 is 1 up to the bf16 rounding of each element (< 2^-8 relative)
+    assert abs(np.mean(x * x) - 1.0) < 2.0 ** -8
+    # the norm removes a positive scale (up to eps and ties: at most one bf16 ulp)
+    x8 = synth.bf16_to_f32(oracle.rmsnorm_bf16(r * np.float32(8.0))).astype(np.float64)
+    assert np.all(np.abs(x8 - x) <= np.abs(x) * 2.0 ** -7 + 1e-30)
+    # and equals the direct definition, element by element, before rounding
+    ref = r.astype(np.float64) / math.sqrt(np.mean(r.astype(np.float64) ** 2) + oracle.RMS_EPS)
+    assert np.all(np.abs(x - ref) <= np.abs(ref) * 2.0 ** -8)
+
+
+def test_residual_layer_is_norm_then_layer_then_add():
+    d, router, blobs, shared, _ = _layer_inputs(E=8, K=4, T=2)
+    rng = np.random.default_rng(3)
+    r = (rng.standard_normal((2, 256)) * 5.0).astype(np.float32)
+    r_out, x, y, ids, w, _, _ = oracle.residual_layer(d, router, blobs, shared, r)
+    np.testing.assert_array_equal(x, oracle.rmsnorm_bf16(r))
+    y2, ids2, _, _, _ = oracle.layer(d, router, blobs, shared, x)
+    np.testing.assert_array_equal(ids, ids2)
+    np.testing.assert_array_equal(y, y2)
+    np.testing.assert_array_equal(r_out, r.astype(np.float64) + y2)
+
+
+def test_residual_layer_with_zero_experts_keeps_the_residual():
+    # s = z = 0 in every matrix: every expert outputs 0, so r_out = r exactly
+    d, router, _, _, _ = _layer_inputs(E=8, K=4, T=1)
+    zero = blobkit.constant_blob(256, 256, 4, 9, 0.0, 0.0)
+    r = np.linspace(-3, 3, 256, dtype=np.float32)[None]
+    r_out, _, y, _, _, _, _ = oracle.residual_layer(d, router, {e: zero for e in range(8)}, zero, r)
+    assert np.all(y == 0.0)
+    np.testing.assert_array_equal(r_out, r.astype(np.float64))
