@@ -22,7 +22,8 @@ SEC_GATE_Q, SEC_UP_Q, SEC_DOWN_Q, SEC_GATE_SB, SEC_UP_SB, SEC_DOWN_SB = range(6)
 # Entry points that libmoe.so exports (one per declaration in include/moe.h).
 EXPORTS = ("moe_abi_version", "moe_status_str", "moe_check_dims", "moe_expert_bytes",
            "moe_blob_layout", "moe_workspace_bytes", "moe_workspace_init", "moe_route",
-           "moe_expert_forward", "moe_layer_decode", "moe_dequantize", "moe_get_device_error")
+           "moe_expert_forward", "moe_layer_decode", "moe_layer_decode_residual",
+           "moe_dequantize", "moe_get_device_error")
 
 
 class MoeError(RuntimeError):
@@ -79,6 +80,7 @@ def lib() -> ctypes.CDLL:
             "moe_route": (i32, [dp, vp, vp, i32, vp, vp, vp, vp, sz, vp]),
             "moe_expert_forward": (i32, [dp, lp, vp, i32, vp, vp, vp, vp, sz, vp]),
             "moe_layer_decode": (i32, [dp, lp, vp, i32, vp, vp, vp, vp, sz, vp]),
+            "moe_layer_decode_residual": (i32, [dp, lp, vp, i32, vp, vp, vp, vp, vp, sz, vp]),
             "moe_dequantize": (i32, [dp, vp, i32, vp, vp]),
             "moe_get_device_error": (i32, [vp, vp, ctypes.POINTER(i32)]),
         }
@@ -187,6 +189,15 @@ def moe_layer_decode(d: Dims, layer: moe_layer, x, T: int, y, ids=None, w=None, 
                                 ws_bytes if ws_bytes is not None else ws.numel(),
                                 _stream(stream))
     _check(rc, "moe_layer_decode")
+
+
+def moe_layer_decode_residual(d: Dims, layer: moe_layer, resid, T: int, x_out=None, y=None,
+                              ids=None, w=None, ws=None, ws_bytes=None, stream=None):
+    rc = lib().moe_layer_decode_residual(ctypes.byref(d.c()), ctypes.byref(layer), _ptr(resid),
+                                         T, _ptr(x_out), _ptr(y), _ptr(ids), _ptr(w), _ptr(ws),
+                                         ws_bytes if ws_bytes is not None else ws.numel(),
+                                         _stream(stream))
+    _check(rc, "moe_layer_decode_residual")
 
 
 def moe_dequantize(d: Dims, blob, which: int, out, stream=None):

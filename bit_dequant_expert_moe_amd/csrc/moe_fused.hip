@@ -46,6 +46,14 @@
 // waves or more copies, and splitting stores and polls into separate waves
 // all measured slower than this layout.
 //
+// Residual mode (RES): the layer also runs the two steps around it on the
+// residual stream r (fp32, updated in place): x = bf16(r / rms(r)) before the
+// router, r += y after the combine.  Every workgroup normalises the whole
+// vector itself (16 KB from L2; no extra exchange), and writes its own rows of
+// r only after it has received every workgroup's activations, which every
+// workgroup publishes only after it has read all of r: reads of r in any
+// workgroup precede writes of r in every workgroup.
+//
 // Termination: every wait is bounded; a wait that times out sets bit 1 of
 // the sticky error word and the kernel runs to completion.
 #include <hip/hip_runtime.h>
@@ -64,6 +72,7 @@ constexpr int kGuWaves = 4;      // gate/up waves 0..3
 constexpr int kDownWaves = 4;    // down waves 4..7 (wave 4 runs the exchange)
 constexpr int kNT = 64 * (kGuWaves + kDownWaves);
 constexpr long kSpinMax = 1L << 18;
+constexpr float kRmsEps = 1e-6f;  // epsilon of the pre-MoE RMS norm
 
 typedef __attribute__((address_space(3))) volatile uint32_t lds_u32;
 
@@ -159,6 +168,8 @@ struct FusedArgs {
   FCtrl *fc;
   uint64_t *tags;         // [kGroups][kMaxE] tagged logits
   uint64_t *htag;         // [kGroups][K+1][I] tagged activations
+  float *resid;           // residual mode: r, fp32 [H], read and updated in place
+  uint16_t *x_out;        // residual mode: the normalised x, bf16 [H], or null
   int E, has_shared;
   int64_t off_gq, off_uq, off_dq, off_gsb, off_usb, off_dsb;
 };
@@ -194,7 +205,7 @@ __device__ __forceinline__ float lane_group_sum(float v, int lane) {
   return wave_sum64(v);
 }
 
-template <int BITS, int H, int I, int K, int RR>
+template <int BITS, int H, int I, int K, int RR, bool RES>
 __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
   using Gm = Geo<BITS, H, I, K>;
   constexpr int COLS = Gm::COLS, PAIRS = Gm::PAIRS, LSEG = Gm::LSEG;
@@ -212,6 +223,8 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
   __shared__ uint32_t s_epoch;
   __shared__ uint32_t s_ready;                 // routing selected
   __shared__ uint32_t s_dissued;               // gate/up waves that issued their routed loads
+  __shared__ float s_ss[kNT / 64];             // residual mode: sum of r^2 per wave
+  __shared__ uint4 s_xn[RES ? H / 8 : 1];      // residual mode: normalised x, bf16
 
   const int b = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int grp = b % kGroups;
@@ -236,11 +249,24 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
   }
 
   // ---- router loads (all threads) -------------------------------------------
+  // thread tid owns x chunk tid + kNT j (8 columns); in residual mode it loads
+  // the fp32 r of those columns instead and x is formed by norm_x below
   uint4 rw[RR * Gm::RXC], rx[Gm::RXC];
-  if (routing) {
+  float4 rf[RES ? 2 * Gm::RXC : 1];
+  if (RES) {
 #pragma unroll
-    for (int j = 0; j < Gm::RXC; ++j)
-      rx[j] = *reinterpret_cast<const uint4 *>(a.x + (size_t)(tid + kNT * j) * 8);
+    for (int j = 0; j < Gm::RXC; ++j) {
+      const float4 *p = reinterpret_cast<const float4 *>(a.resid + (size_t)(tid + kNT * j) * 8);
+      rf[2 * j] = p[0];
+      rf[2 * j + 1] = p[1];
+    }
+  }
+  if (routing) {
+    if (!RES) {
+#pragma unroll
+      for (int j = 0; j < Gm::RXC; ++j)
+        rx[j] = *reinterpret_cast<const uint4 *>(a.x + (size_t)(tid + kNT * j) * 8);
+    }
 #pragma unroll
     for (int i = 0; i < RR * Gm::RXC; ++i) {
       const int row = i / Gm::RXC, e = b * rr + row;
@@ -251,6 +277,42 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
       rw[i] = *reinterpret_cast<const uint4 *>(a.router + (size_t)ec * H + (size_t)ch * 8);
     }
   }
+  // Residual mode, all waves, once: x = bf16(r / sqrt(mean(r^2) + eps)) into
+  // rx and s_xn.  The per-wave sums are added in wave order, so every thread
+  // of every workgroup uses the same scale.  The two barriers order LDS only.
+  auto norm_x = [&]() {
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < 2 * Gm::RXC; ++j) {
+      ss = fmaf(rf[j].x, rf[j].x, ss);
+      ss = fmaf(rf[j].y, rf[j].y, ss);
+      ss = fmaf(rf[j].z, rf[j].z, ss);
+      ss = fmaf(rf[j].w, rf[j].w, ss);
+    }
+    ss = wave_sum64(ss);
+    if (lane == 0) s_ss[wave] = ss;
+    lds_release();
+    __builtin_amdgcn_s_barrier();
+    lds_acquire();
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < kNT / 64; ++w) tot += s_ss[w];
+    const float inv = 1.f / sqrtf(tot * (1.f / (float)H) + kRmsEps);
+#pragma unroll
+    for (int j = 0; j < Gm::RXC; ++j) {
+      const float4 lo = rf[2 * j], hi = rf[2 * j + 1];
+      rx[j] = make_uint4(f2bf(lo.x * inv) | (f2bf(lo.y * inv) << 16),
+                         f2bf(lo.z * inv) | (f2bf(lo.w * inv) << 16),
+                         f2bf(hi.x * inv) | (f2bf(hi.y * inv) << 16),
+                         f2bf(hi.z * inv) | (f2bf(hi.w * inv) << 16));
+      s_xn[tid + kNT * j] = rx[j];
+      if (b == 0 && a.x_out)
+        *reinterpret_cast<uint4 *>(a.x_out + (size_t)(tid + kNT * j) * 8) = rx[j];
+    }
+    lds_release();
+    __builtin_amdgcn_s_barrier();
+    lds_acquire();
+  };
   auto router_partials = [&]() {
     float part[RR];
 #pragma unroll
@@ -280,9 +342,11 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
     // x segments to stage (one per thread of the gate/up waves)
     const int xs = tid;
     uint4 xr[Gm::XLD];
+    if (!RES) {
 #pragma unroll
-    for (int t = 0; t < Gm::XLD; ++t)
-      xr[t] = *reinterpret_cast<const uint4 *>(a.x + (size_t)(xs % Gm::SEG_X) * COLS + 8 * t);
+      for (int t = 0; t < Gm::XLD; ++t)
+        xr[t] = *reinterpret_cast<const uint4 *>(a.x + (size_t)(xs % Gm::SEG_X) * COLS + 8 * t);
+    }
     uint4 gq[NSL][LSEG], uq[NSL][LSEG];
     uint32_t gsb[NSL][LSEG], usb[NSL][LSEG];
     // byte offsets inside a blob, the same for every expert
@@ -310,6 +374,11 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
     };
     // without a shared expert slot K reads expert 0 and is never used
     load_rows(K, a.has_shared ? a.shared : a.experts);
+    if (RES) {
+      norm_x();
+#pragma unroll
+      for (int t = 0; t < Gm::XLD; ++t) xr[t] = s_xn[(xs % Gm::SEG_X) * (COLS / 8) + t];
+    }
     if (routing) router_partials();
     // x pairs and per-segment corrections, one code word at a time, to LDS
     if (xs < Gm::SEG_X) {
@@ -409,6 +478,13 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
 #pragma unroll
     for (int ld = 0; ld < Gm::DLD; ++ld)
       rows[ld] = b * Gm::D_ROWS + dw * Gm::D_ROWS_W + ld * Gm::RPL + lane / Gm::LPR;
+    // residual mode: r of this lane's output rows, read before any workgroup
+    // can write r
+    float rres[RES ? Gm::DLD : 1];
+    if (RES) {
+#pragma unroll
+      for (int ld = 0; ld < Gm::DLD; ++ld) rres[ld] = a.resid[rows[ld]];
+    }
     uint4 dq[NSL][Gm::DLD];
     uint32_t dsb[NSL][Gm::DLD];
     uint32_t o_dq[Gm::DLD], o_dsb[Gm::DLD];
@@ -432,6 +508,7 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     };
     load_rows(K, a.has_shared ? a.shared : a.experts);
+    if (RES) norm_x();
     if (routing) router_partials();
     if (tid == kEpochTid) s_epoch = epoch_done + 1u;
     __syncthreads();  // (A)
@@ -672,7 +749,10 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
 #pragma unroll
     for (int ld = 0; ld < Gm::DLD; ++ld) {
       const float v = lane_group_sum<Gm::LPR>(acc[ld], lane);
-      if (seg == 0) a.y[rows[ld]] = v;
+      if (seg == 0) {
+        if (!RES || a.y) a.y[rows[ld]] = v;
+        if (RES) a.resid[rows[ld]] = rres[ld] + v;
+      }
     }
     // every workgroup has published every slot, so all have passed barrier
     // (A), where they read the epoch
@@ -700,7 +780,8 @@ bool fused_supported(const moe_dims &d) {
 
 int launch_layer_fused(const moe_dims &d, const moe_layer &L, const uint16_t *x,
                        const int32_t *ids_in, const float *w_in, int32_t *ids_out,
-                       float *w_out, float *y, void *ws, void *stream) {
+                       float *w_out, float *y, float *resid, uint16_t *x_out, void *ws,
+                       void *stream) {
   const WsLayout W = ws_layout(d, 1);
   const BlobLayout B = blob_layout(d);
   uint8_t *base = static_cast<uint8_t *>(ws);
@@ -715,6 +796,8 @@ int launch_layer_fused(const moe_dims &d, const moe_layer &L, const uint16_t *x,
   a.ids_out = ids_out;
   a.w_out = w_out;
   a.y = y;
+  a.resid = resid;
+  a.x_out = x_out;
   a.ctrl = reinterpret_cast<Ctrl *>(base + W.ctrl);
   a.fc = reinterpret_cast<FCtrl *>(base + W.fctrl);
   a.tags = reinterpret_cast<uint64_t *>(base + W.logits_tag);
@@ -728,17 +811,20 @@ int launch_layer_fused(const moe_dims &d, const moe_layer &L, const uint16_t *x,
   a.off_usb = (int64_t)B.off[MOE_SEC_UP_SB];
   a.off_dsb = (int64_t)B.off[MOE_SEC_DOWN_SB];
   const int rr = (d.n_experts + kG - 1) / kG;
-#define MOE_LAUNCH_L1(B, R) \
-  hipLaunchKernelGGL((k_layer1<B, 4096, 1024, 4, R>), dim3(kG), dim3(kNT), 0, S(stream), a)
+  // the residual mode always routes
+  if (resid && ids_in) return (int)hipErrorInvalidValue;
+#define MOE_LAUNCH_L1(B, R, RS) \
+  hipLaunchKernelGGL((k_layer1<B, 4096, 1024, 4, R, RS>), dim3(kG), dim3(kNT), 0, S(stream), a)
+#define MOE_LAUNCH_RR(B, RS)        \
+  if (rr == 1) MOE_LAUNCH_L1(B, 1, RS); \
+  else if (rr == 2) MOE_LAUNCH_L1(B, 2, RS); \
+  else MOE_LAUNCH_L1(B, 4, RS)
   if (d.bits == 4) {
-    if (rr == 1) MOE_LAUNCH_L1(4, 1);
-    else if (rr == 2) MOE_LAUNCH_L1(4, 2);
-    else MOE_LAUNCH_L1(4, 4);
+    if (resid) { MOE_LAUNCH_RR(4, true); } else { MOE_LAUNCH_RR(4, false); }
   } else {
-    if (rr == 1) MOE_LAUNCH_L1(2, 1);
-    else if (rr == 2) MOE_LAUNCH_L1(2, 2);
-    else MOE_LAUNCH_L1(2, 4);
+    if (resid) { MOE_LAUNCH_RR(2, true); } else { MOE_LAUNCH_RR(2, false); }
   }
+#undef MOE_LAUNCH_RR
 #undef MOE_LAUNCH_L1
   return (int)hipGetLastError();
 }

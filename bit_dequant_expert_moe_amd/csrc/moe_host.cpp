@@ -66,6 +66,10 @@ WsLayout ws_layout(const moe_dims &d, int T) {
     W.yd = o;
     o = align_up(o + P * d.hidden * 4, kAlign);
   }
+  W.xn = o;
+  o = align_up(o + (size_t)T * d.hidden * 2, kAlign);
+  W.yr = o;
+  o = align_up(o + (size_t)T * d.hidden * 4, kAlign);
   W.total = o;
   return W;
 }
@@ -212,7 +216,8 @@ moe_status moe_expert_forward(const moe_dims *dims, const moe_layer *layer, cons
     return MOE_ERR_ALIGN;
   MOE_TRY(check_ws(dims, T, ws, ws_bytes));
   if (use_fused(*dims, T))
-    return launch_layer_fused(*dims, *layer, x, ids, w, nullptr, nullptr, y, ws, stream) == 0
+    return launch_layer_fused(*dims, *layer, x, ids, w, nullptr, nullptr, y, nullptr,
+                              nullptr, ws, stream) == 0
                ? MOE_OK
                : MOE_ERR_HIP;
   return expert_forward(*dims, *layer, x, T, ids, w, y, ws, stream) == 0 ? MOE_OK : MOE_ERR_HIP;
@@ -231,7 +236,8 @@ moe_status moe_layer_decode(const moe_dims *dims, const moe_layer *layer, const 
   if (!layer->router) return MOE_ERR_NULL;
   if (!aligned(layer->router, 16)) return MOE_ERR_ALIGN;
   if (use_fused(*dims, T))
-    return launch_layer_fused(*dims, *layer, x, nullptr, nullptr, ids, w, y, ws, stream) == 0
+    return launch_layer_fused(*dims, *layer, x, nullptr, nullptr, ids, w, y, nullptr,
+                              nullptr, ws, stream) == 0
                ? MOE_OK
                : MOE_ERR_HIP;
   const WsLayout W = ws_layout(*dims, T);
@@ -241,6 +247,36 @@ moe_status moe_layer_decode(const moe_dims *dims, const moe_layer *layer, const 
   if (launch_route(*dims, layer->router, x, T, ids_d, w_d, nullptr, ws, stream) != 0)
     return MOE_ERR_HIP;
   if (expert_forward(*dims, *layer, x, T, ids_d, w_d, y, ws, stream) != 0) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+moe_status moe_layer_decode_residual(const moe_dims *dims, const moe_layer *layer, float *resid,
+                                     int32_t T, uint16_t *x_out, float *y, int32_t *ids,
+                                     float *w, void *ws, size_t ws_bytes, void *stream) {
+  MOE_TRY(check_dims(dims));
+  MOE_TRY(check_T(T));
+  MOE_TRY(check_layer(dims, layer));
+  if (!resid || !layer->router) return MOE_ERR_NULL;
+  if (!aligned(resid, 16) || (x_out && !aligned(x_out, 16)) || (y && !aligned(y, 16)) ||
+      (ids && !aligned(ids, 4)) || (w && !aligned(w, 4)) || !aligned(layer->router, 16))
+    return MOE_ERR_ALIGN;
+  MOE_TRY(check_ws(dims, T, ws, ws_bytes));
+  if (use_fused(*dims, T))
+    return launch_layer_fused(*dims, *layer, nullptr, nullptr, nullptr, ids, w, y, resid, x_out,
+                              ws, stream) == 0
+               ? MOE_OK
+               : MOE_ERR_HIP;
+  const WsLayout W = ws_layout(*dims, T);
+  uint8_t *base = static_cast<uint8_t *>(ws);
+  uint16_t *x_d = x_out ? x_out : reinterpret_cast<uint16_t *>(base + W.xn);
+  float *y_d = y ? y : reinterpret_cast<float *>(base + W.yr);
+  int32_t *ids_d = ids ? ids : reinterpret_cast<int32_t *>(base + W.ids);
+  float *w_d = w ? w : reinterpret_cast<float *>(base + W.w);
+  if (launch_rmsnorm(*dims, resid, T, x_d, stream) != 0) return MOE_ERR_HIP;
+  if (launch_route(*dims, layer->router, x_d, T, ids_d, w_d, nullptr, ws, stream) != 0)
+    return MOE_ERR_HIP;
+  if (expert_forward(*dims, *layer, x_d, T, ids_d, w_d, y_d, ws, stream) != 0) return MOE_ERR_HIP;
+  if (launch_resid_add(*dims, resid, y_d, T, stream) != 0) return MOE_ERR_HIP;
   return MOE_OK;
 }
 

@@ -39,6 +39,9 @@ BlobLayout blob_layout(const moe_dims &d);
 //   xb, xs     : x as matrix-core B operand [T][H/8] x 16 B, group sums [T][H/64]
 //   hb, hs     : h as B operand [T][K+1][I/8] x 32 B (bf16 hi, lo), sums [T][K+1][I/64]
 //   yd         : fp32 [T][K+1][H]   per-slot down projections
+//   residual entry point, unfused path only:
+//   xn         : bf16 [T][H]   normalised x (when the caller passes no x_out)
+//   yr         : fp32 [T][H]   layer output (when the caller passes no y)
 struct Ctrl {
   uint32_t reserved;       // unused
   uint32_t err;            // sticky device error flags
@@ -71,7 +74,8 @@ constexpr size_t kHTagOff = kTagOff + (size_t)kGroups * kMaxE * 8;
 constexpr size_t kHeaderBytes = kHTagOff + (size_t)kGroups * kFusedSlots * kFusedI * 8;
 
 struct WsLayout {
-  size_t ctrl, fctrl, logits_tag, h_tag, logits, ids, w, h, bk, xb, xs, hb, hs, yd, total;
+  size_t ctrl, fctrl, logits_tag, h_tag, logits, ids, w, h, bk, xb, xs, hb, hs, yd, xn, yr,
+      total;
 };
 WsLayout ws_layout(const moe_dims &d, int T);
 
@@ -100,9 +104,15 @@ int launch_expert_forward(const moe_dims &d, const moe_layer &L, const uint16_t 
                           const int32_t *ids, const float *w, float *y, void *ws,
                           void *stream);
 bool fused_supported(const moe_dims &d);
+// With resid != null the kernel runs in residual mode: x is formed from resid
+// (written to x_out if given), resid += y in place, y is optional.
 int launch_layer_fused(const moe_dims &d, const moe_layer &L, const uint16_t *x,
                        const int32_t *ids_in, const float *w_in, int32_t *ids_out,
-                       float *w_out, float *y, void *ws, void *stream);
+                       float *w_out, float *y, float *resid, uint16_t *x_out, void *ws,
+                       void *stream);
+// Residual stream steps of the unfused path.
+int launch_rmsnorm(const moe_dims &d, const float *r, int T, uint16_t *x, void *stream);
+int launch_resid_add(const moe_dims &d, float *r, const float *y, int T, void *stream);
 int launch_dequantize(const moe_dims &d, const uint8_t *blob, int which, float *out,
                       void *stream);
 // Batched path (moe_grouped.hip): pairs grouped by expert, MFMA GEMMs.

@@ -392,6 +392,54 @@ __global__ void __launch_bounds__(256) k_dequantize(DequantArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Residual stream around the layer, for the multi-token and unfused paths.
+// x[t] = bf16(r[t] / sqrt(mean_c r[t][c]^2 + eps)), one workgroup per token;
+// the sum of squares is reduced in a fixed order (deterministic).
+// ---------------------------------------------------------------------------
+constexpr float kRmsEps = 1e-6f;
+
+__global__ void __launch_bounds__(256) k_rmsnorm(const float *__restrict__ r, int H,
+                                                 uint16_t *__restrict__ x) {
+  __shared__ float s_part[4];
+  const float *rt = r + (size_t)blockIdx.x * H;
+  uint16_t *xt = x + (size_t)blockIdx.x * H;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float ss = 0.f;
+  for (int c = 4 * threadIdx.x; c < H; c += 1024) {
+    const float4 v = *reinterpret_cast<const float4 *>(rt + c);
+    ss = fmaf(v.x, v.x, ss);
+    ss = fmaf(v.y, v.y, ss);
+    ss = fmaf(v.z, v.z, ss);
+    ss = fmaf(v.w, v.w, ss);
+  }
+  ss = wave_sum64(ss);
+  if (lane == 0) s_part[wave] = ss;
+  __syncthreads();
+  const float tot = ((s_part[0] + s_part[1]) + s_part[2]) + s_part[3];
+  const float inv = 1.f / sqrtf(tot * (1.f / (float)H) + kRmsEps);
+  for (int c = 4 * threadIdx.x; c < H; c += 1024) {
+    const float4 v = *reinterpret_cast<const float4 *>(rt + c);
+    *reinterpret_cast<uint2 *>(xt + c) =
+        make_uint2(f2bf(v.x * inv) | (f2bf(v.y * inv) << 16), f2bf(v.z * inv) | (f2bf(v.w * inv) << 16));
+  }
+}
+
+// r += y over n floats (n a multiple of 4).
+__global__ void __launch_bounds__(256) k_resid_add(float *__restrict__ r,
+                                                   const float *__restrict__ y, size_t n4) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
+       i += (size_t)gridDim.x * blockDim.x) {
+    float4 a = reinterpret_cast<float4 *>(r)[i];
+    const float4 b = reinterpret_cast<const float4 *>(y)[i];
+    a.x += b.x;
+    a.y += b.y;
+    a.z += b.z;
+    a.w += b.w;
+    reinterpret_cast<float4 *>(r)[i] = a;
+  }
+}
+
 __global__ void k_ws_init(uint4 *ctrl, int n16) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += gridDim.x * blockDim.x)
     ctrl[i] = make_uint4(0u, 0u, 0u, 0u);
@@ -514,6 +562,19 @@ int launch_expert_forward(const moe_dims &d, const moe_layer &L, const uint16_t 
     hipLaunchKernelGGL(k_gateup<2>, grid_gu, dim3(256), lds_gu, S(stream), g);
     hipLaunchKernelGGL(k_down<2>, grid_dn, dim3(256), lds_dn, S(stream), dn);
   }
+  return (int)hipGetLastError();
+}
+
+int launch_rmsnorm(const moe_dims &d, const float *r, int T, uint16_t *x, void *stream) {
+  hipLaunchKernelGGL(k_rmsnorm, dim3(T), dim3(256), 0, S(stream), r, d.hidden, x);
+  return (int)hipGetLastError();
+}
+
+int launch_resid_add(const moe_dims &d, float *r, const float *y, int T, void *stream) {
+  const size_t n4 = (size_t)T * d.hidden / 4;
+  size_t blocks = (n4 + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(k_resid_add, dim3((unsigned)blocks), dim3(256), 0, S(stream), r, y, n4);
   return (int)hipGetLastError();
 }
 

@@ -8,6 +8,7 @@
  *   for the K routed experts plus one shared expert -> weighted combine
  *                                                               (moe_expert_forward)
  *   both, back to back on one stream                            (moe_layer_decode)
+ *   RMS norm of the residual, the layer, residual add   (moe_layer_decode_residual)
  *
  * Sources for the method (web pages; cited by title and section):
  *   [HL] "Flash-MoE: Running a 397B Parameter Model on a Laptop" (hysenlabs.com),
@@ -66,7 +67,8 @@
  *   error nothing is enqueued and the status says why.
  * - bf16 tensors are passed as uint16_t bit patterns.
  * - x is bf16 [T][H], row-major, and is expected to be RMS-normalised by the
- *   caller (the pages place a norm before routing, [HL]).
+ *   caller (the pages place a norm before routing, [HL]);
+ *   moe_layer_decode_residual forms it from the residual itself.
  * - y is fp32 [T][H] row-major.  ids int32 [T][K], w fp32 [T][K], per token
  *   in descending-logit order.
  * - Results are deterministic: identical inputs give bitwise-identical
@@ -194,6 +196,28 @@ moe_status moe_layer_decode(const moe_dims *dims, const moe_layer *layer,
                             const uint16_t *x, int32_t T, float *y,
                             int32_t *ids, float *w, void *ws, size_t ws_bytes,
                             void *stream);
+
+/* One MoE block on the residual stream ([HL], "How the SSD expert streaming
+ * pipeline works": each layer ends with the combine and a norm, so the next
+ * layer's router sees the normalised sum).  For each token t:
+ *   x[t] = bf16( r[t] / sqrt(mean_c r[t][c]^2 + 1e-6) )   (RMS norm)
+ *   y[t] = the MoE layer of x[t], exactly as moe_layer_decode
+ *   r[t] = r[t] + y[t]                                   (fp32, in place)
+ * Readings (the pages name the norm but not its form): RMS norm without a
+ * learned gain (a gain folds into the next matrices), epsilon 1e-6, the
+ * residual kept in fp32, the sum of squares accumulated in fp32 and x
+ * rounded to bf16 to nearest-even.  Calling this once per layer with the
+ * same r chains layers: x of layer l+1 = norm(r after layer l).
+ * Arguments: resid fp32 [T][H], 16-byte aligned, read and written (the
+ * caller owns it; it must not alias any other argument).  x_out bf16 [T][H]
+ * (16-byte aligned) receives x, or NULL.  y fp32 [T][H] (16-byte aligned)
+ * receives the layer output, or NULL.  ids/w as in moe_layer_decode.
+ * After a call that leaves a device error (moe_get_device_error) resid is
+ * undefined. */
+moe_status moe_layer_decode_residual(const moe_dims *dims, const moe_layer *layer,
+                                     float *resid, int32_t T, uint16_t *x_out, float *y,
+                                     int32_t *ids, float *w, void *ws, size_t ws_bytes,
+                                     void *stream);
 
 /* Test hook: writes the dequantised fp32 matrix `which` (0 Gate [I][H],
  * 1 Up [I][H], 2 Down [H][I]) of one blob to out (row-major).  Each element

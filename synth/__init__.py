@@ -158,7 +158,7 @@ def bf16_to_f32(b) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-_TAG_ROUTER, _TAG_X, _TAG_NOISE = 1, 2, 3
+_TAG_ROUTER, _TAG_X, _TAG_NOISE, _TAG_RESID = 1, 2, 3, 4
 
 
 def router_weights(seed: int, layer: int, E: int, H: int, std: float = 0.02) -> np.ndarray:
@@ -191,6 +191,24 @@ def tokens_ar1(seed: int, layer: int, T: int, H: int, rho: float) -> np.ndarray:
     for t in range(1, T):
         z[t] = rho * z[t - 1] + c * g.standard_normal(H)
     return f32_to_bf16(rms_normalise(z))
+
+
+def residual(seed: int, T: int, H: int, rho: float = 0.0, outliers: int = 4,
+             outlier_scale: float = 20.0) -> np.ndarray:
+    """T consecutive residual-stream vectors, fp32 [T][H]: N(0,1) per channel,
+    AR(1)-correlated with coefficient rho from token to token, with
+    `outliers` fixed channels scaled by `outlier_scale` (residual streams of
+    large transformers carry a few channels far above the rest; the value is
+    a stand-in, not a measurement).  Not normalised."""
+    g = np.random.default_rng([seed, _TAG_RESID, 0])
+    big = g.choice(H, size=outliers, replace=False) if outliers else np.zeros(0, np.int64)
+    z = np.empty((T, H), dtype=np.float64)
+    z[0] = g.standard_normal(H)
+    c = np.sqrt(1.0 - rho * rho)
+    for t in range(1, T):
+        z[t] = rho * z[t - 1] + c * g.standard_normal(H)
+    z[:, big] *= outlier_scale
+    return z.astype(np.float32)
 
 
 from .workloads import WORKLOADS, Workload  # noqa: E402,F401

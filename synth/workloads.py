@@ -29,6 +29,9 @@ class Workload:
     rho: float = 0.0   # AR(1) token-to-token correlation of activations (0: i.i.d.)
     has_shared: int = 1
     group: int = 64
+    chain: bool = False  # layers chained through the residual stream (x = norm(r), r += y)
+    z_lo: float = -0.08  # bias range of the expert blobs
+    z_hi: float = 0.08
     description: str = ""
 
 
@@ -38,6 +41,15 @@ class Workload:
 # routers, the benchmark reports the reuse it actually sees.
 STACK_RHO = 0.97
 
+# Bias range centred on -(2^4 - 1)/2 * mean scale (7.5 * 0.0125), so that each
+# 4-bit weight matrix has zero mean, as a trained model's do.  With the
+# uncentred range every weight has mean ~0.094: the first layer's output is
+# then a near-constant vector that dominates the residual, and from the second
+# layer on every gate sum is ~ -0.094 * 4096 and SwiGLU underflows -- the
+# chained stack degenerates.  Per-layer (teacher-forced) workloads keep the
+# uncentred range.
+CENTRED_Z = (-0.08 - 7.5 * 0.0125, 0.08 - 7.5 * 0.0125)
+
 WORKLOADS = {
     "tiny": Workload("tiny", 4096, 1024, 16, 4, 4, 1, 1, 1, 1000, 1000,
                      description="one layer, 16 experts, 1 token"),
@@ -46,6 +58,11 @@ WORKLOADS = {
     "stack60": Workload("stack60", 4096, 1024, 512, 4, 4, 60, 1, 128, 1002, 1002, rho=STACK_RHO,
                         description="60 HBM-resident layers x 512 4-bit experts, "
                                     "128 consecutive decode tokens"),
+    "stack60_chain": Workload("stack60_chain", 4096, 1024, 512, 4, 4, 60, 1, 128, 1002, 1002,
+                              rho=STACK_RHO, chain=True, z_lo=CENTRED_Z[0], z_hi=CENTRED_Z[1],
+                              description="the 60-layer stack chained through the residual "
+                                          "stream: per layer x = norm(r), the MoE layer, "
+                                          "r += y; 128 consecutive decode tokens"),
     "batch64": Workload("batch64", 4096, 1024, 512, 4, 4, 1, 64, 1, 1003, 1003,
                         description="one full layer, 64 tokens routed independently"),
     "stack60_2bit": Workload("stack60_2bit", 4096, 1024, 512, 4, 2, 60, 1, 128, 1002, 1004,

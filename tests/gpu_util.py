@@ -23,7 +23,7 @@ class DeviceLayer:
     """One synthetic layer resident on the GPU."""
 
     def __init__(self, H, I, E, K, bits=4, has_shared=1, seed=1000, blob_seed=None, layer=0,
-                 stride=None):
+                 stride=None, z_range=None):
         import torch
         self.torch = torch
         self.dims = moe.Dims(hidden=H, inter=I, n_experts=E, top_k=K, bits=bits,
@@ -33,6 +33,8 @@ class DeviceLayer:
         self.stride = stride or self.nbytes
         self.params = synth.BlobParams(seed=blob_seed if blob_seed is not None else seed,
                                        H=H, I=I, bits=bits)
+        if z_range is not None:
+            self.params = synth.replace(self.params, z_lo=z_range[0], z_hi=z_range[1])
         self.layer = layer
         self.seed = seed
         self.experts = torch.empty(E * self.stride, dtype=torch.uint8, device="cuda")
@@ -84,6 +86,46 @@ class DeviceLayer:
         if want_logits:
             out["logits"] = logits.cpu().numpy()
         return out
+
+    def decode_residual(self, r_f32, ws=None, outputs=True):
+        """moe_layer_decode_residual on a copy of r; returns host arrays
+        (x, y, ids, w only when outputs=True)."""
+        torch = self.torch
+        r_f32 = np.ascontiguousarray(r_f32, dtype=np.float32).reshape(-1, self.dims.hidden)
+        T = r_f32.shape[0]
+        rd = torch.from_numpy(r_f32.copy()).cuda()
+        ws = ws if ws is not None else moe.alloc_workspace(self.dims, T)
+        out = {}
+        if outputs:
+            x = torch.empty((T, self.dims.hidden), dtype=torch.int16, device="cuda")
+            y = torch.empty((T, self.dims.hidden), dtype=torch.float32, device="cuda")
+            ids = torch.empty((T, self.dims.top_k), dtype=torch.int32, device="cuda")
+            w = torch.empty((T, self.dims.top_k), dtype=torch.float32, device="cuda")
+            moe.moe_layer_decode_residual(self.dims, self.L, rd, T, x, y, ids, w, ws)
+        else:
+            moe.moe_layer_decode_residual(self.dims, self.L, rd, T, ws=ws)
+        torch.cuda.synchronize()
+        out["err"] = moe.moe_get_device_error(ws)
+        out["r"] = rd.cpu().numpy()
+        if outputs:
+            out.update(x=x.cpu().numpy().view(np.uint16), y=y.cpu().numpy(),
+                       ids=ids.cpu().numpy(), w=w.cpu().numpy())
+        return out
+# The device sums r^2 in fp32 and scales in fp32, the oracle in float64: a
+# value within ~1e-7 relative of a bf16 rounding boundary may round the other
+# way (expected well under one element per 4096-vector).  Allowed: at most
+# this many elements per vector, each one bf16 step away.
+X_MISMATCH_MAX = 8
+
+
+def check_norm(x_gpu, r):
+    """x_gpu (bf16 bits [H]) against the oracle's RMS norm of r."""
+    x_o = oracle.rmsnorm_bf16(np.asarray(r, np.float32))
+    d = x_gpu.astype(np.int32) - x_o.astype(np.int32)
+    bad = np.nonzero(d)[0]
+    assert bad.size <= X_MISMATCH_MAX, "x differs from the oracle in %d elements" % bad.size
+    assert np.all(np.abs(d) <= 1) and np.all((x_gpu[bad] ^ x_o[bad]) & 0x8000 == 0)
+    return int(bad.size)
 
 
 def check_routing(od, ids_gpu, w_gpu, logits_or, gap_or, K):

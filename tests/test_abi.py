@@ -145,3 +145,18 @@ def test_dequantize_and_misc_validation():
     assert _status(moe.moe_workspace_init, ws=None, ws_bytes=256, stream=0) == -1
     assert _status(moe.moe_workspace_init, ws=WS, ws_bytes=16, stream=0) == -5
     assert moe.lib().moe_get_device_error(None, None, ctypes.byref(ctypes.c_int32())) == -1
+
+
+def test_layer_decode_residual_validation():
+    f = moe.moe_layer_decode_residual
+    args = dict(d=D, layer=L_OK, resid=A, T=1, x_out=None, y=None, ids=None, w=None, ws=WS,
+                ws_bytes=moe.moe_workspace_bytes(D, 1), stream=0)
+    assert _status(f, **{**args, "resid": None}) == -1
+    assert _status(f, **{**args, "layer": moe.make_layer(None, A, 7_077_888, A)}) == -1
+    assert _status(f, **{**args, "resid": A + 4}) == -4
+    assert _status(f, **{**args, "x_out": A + 8}) == -4
+    assert _status(f, **{**args, "y": A + 4}) == -4
+    assert _status(f, **{**args, "T": 0}) == -2
+    assert _status(f, **{**args, "d": moe.Dims(bits=3)}) == -3
+    assert _status(f, **{**args, "ws_bytes": 256}) == -5
+    assert _status(f, **{**args, "T": 4}) == -5   # workspace sized for T=1
