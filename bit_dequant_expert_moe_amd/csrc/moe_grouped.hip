@@ -47,7 +47,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 constexpr int kRT = 64;         // weight rows per block (16 per wave)
-constexpr int kNC = 16;         // pairs per block (one 16-wide MFMA tile)
+constexpr int kNC = 16;         // pairs per block (one 16-wide MFMA tile; one work item)
 constexpr int kKC = 256;        // columns per staged chunk
 constexpr int kGC = kKC / kGroup;  // groups per chunk (4)
 constexpr int kSl = kKC / 8;    // 8-column slices per chunk (32)
@@ -58,13 +58,25 @@ static_assert(kRT == kGroup, "a gate/up row tile is one group of the down column
 //   bk[0]                       number of buckets nb
 //   bk[1 + j]                   expert of bucket j (E = the shared expert)
 //   bk[1 + maxB + j], j <= nb   first pair of bucket j; bk[1 + maxB + nb] = total
-//   bk[2 + 2 maxB + p]          pair code t (K + 1) + slot (slot K = shared)
+//   bk[2 + 2 maxB + p]          pair code t (K + 1) + slot (slot K = shared),
+//                               p < T (K + 1) = pair_cap
+//   bk[2 + 2 maxB + pair_cap]   number of work items
+//   bk[3 + 2 maxB + pair_cap + i]  work item i = bucket << 8 | chunk: the pairs
+//                               kNC chunk .. kNC chunk + kNC - 1 of the bucket
+// One GEMM block per (row tile, work item): no block is launched for an
+// empty chunk of a bucket.
+// ---------------------------------------------------------------------------
+
+// Upper bound of the number of work items for T tokens.
+__host__ __device__ constexpr int max_items(int E, int T, int K, int has_shared) {
+  return (E < T * K ? E : T * K) + (T * K + kNC - 1) / kNC + (has_shared ? (T + kNC - 1) / kNC : 0);
+}
 // ---------------------------------------------------------------------------
 struct BucketArgs {
   const int32_t *ids;
   int32_t *bk;
   Ctrl *ctrl;
-  int T, K, E, has_shared, maxB;
+  int T, K, E, has_shared, maxB, pair_cap;
 };
 
 // Exclusive prefix sum over the 1024 threads of the block; returns the sum of
@@ -133,6 +145,20 @@ __global__ void __launch_bounds__(1024) k_bucket(BucketArgs a) {
   }
   if (a.has_shared)
     for (int t = tid; t < a.T; t += 1024) pairs[total + t] = t * (a.K + 1) + a.K;
+  // work items: routed buckets in bucket order, then the shared bucket
+  const int nz = (c + kNC - 1) / kNC;
+  int nitems;
+  const int ioff = block_exscan(nz, s_wtot, &nitems);
+  int32_t *items = a.bk + 3 + 2 * a.maxB + a.pair_cap;
+  for (int z = 0; z < nz; ++z) items[ioff + z] = (j << 8) | z;
+  if (tid == 0) {
+    if (a.has_shared) {
+      const int nzs = (a.T + kNC - 1) / kNC;
+      for (int z = 0; z < nzs; ++z) items[nitems + z] = (nrb << 8) | z;
+      nitems += nzs;
+    }
+    a.bk[2 + 2 * a.maxB + a.pair_cap] = nitems;
+  }
   __syncthreads();
   // the order of pairs inside a bucket does not change any result: each
   // pair's column of the MFMA tiles is computed independently
@@ -167,6 +193,7 @@ struct GroupArgs {
   float *yd;           // down output: [T (K+1)][H]
   int R, C;            // rows and columns of the matrices of this pass
   int E, maxB, K1;     // K1 = K + 1 (pair code = token K1 + slot)
+  int pair_cap;        // T (K + 1): size of the pair-code list
   int64_t off_q0, off_q1, off_sb0, off_sb1;  // second matrix unused for down
 };
 
@@ -263,12 +290,13 @@ __global__ void __launch_bounds__(256) k_grouped(GroupArgs a) {
   __shared__ float s_hsum[4][16];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int q = lane >> 4, col = lane & 15;
-  const int nb = a.bk[0];
-  const int j = blockIdx.y;
-  if (j >= nb) return;
+  const int32_t *items = a.bk + 2 + 2 * a.maxB + a.pair_cap;
+  if ((int)blockIdx.y >= items[0]) return;
+  const int item = items[1 + blockIdx.y];
+  const int j = item >> 8;
   const int e = a.bk[1 + j];
   const int p0 = a.bk[1 + a.maxB + j], p1 = a.bk[2 + a.maxB + j];
-  const int pbase = p0 + kNC * (int)blockIdx.z;
+  const int pbase = p0 + kNC * (item & 255);
   if (pbase >= p1) return;
   const int nn = min(kNC, p1 - pbase);
   const int32_t *pairs = a.bk + 2 + 2 * a.maxB + pbase;
@@ -531,6 +559,11 @@ int grouped_max_buckets(const moe_dims &d, int T) {
   return routed + d.has_shared;
 }
 
+int grouped_bucket_words(const moe_dims &d, int T) {
+  return 3 + 2 * grouped_max_buckets(d, T) + T * (d.top_k + 1) +
+         max_items(d.n_experts, T, d.top_k, d.has_shared);
+}
+
 int launch_expert_forward_grouped(const moe_dims &d, const moe_layer &L, const uint16_t *x,
                                   int T, const int32_t *ids, const float *w, float *y, void *ws,
                                   void *stream) {
@@ -556,6 +589,7 @@ int launch_expert_forward_grouped(const moe_dims &d, const moe_layer &L, const u
   ba.E = d.n_experts;
   ba.has_shared = d.has_shared;
   ba.maxB = maxB;
+  ba.pair_cap = T * (d.top_k + 1);
   hipLaunchKernelGGL(k_bucket, dim3(1), dim3(1024), 0, st, ba);
 
   XPrepArgs xa;
@@ -567,7 +601,7 @@ int launch_expert_forward_grouped(const moe_dims &d, const moe_layer &L, const u
   hipLaunchKernelGGL(k_xprep, dim3((unsigned)(((size_t)T * d.hidden / 8 + 255) / 256)), dim3(256),
                      0, st, xa);
 
-  const int nchunk_pairs = (T + kNC - 1) / kNC;  // a bucket holds at most T pairs
+  const int nitems = max_items(d.n_experts, T, d.top_k, d.has_shared);
   GroupArgs gu;
   gu.bop = xb;
   gu.bsum = xs;
@@ -583,6 +617,7 @@ int launch_expert_forward_grouped(const moe_dims &d, const moe_layer &L, const u
   gu.E = d.n_experts;
   gu.maxB = maxB;
   gu.K1 = d.top_k + 1;
+  gu.pair_cap = T * (d.top_k + 1);
   gu.off_q0 = (int64_t)B.off[MOE_SEC_GATE_Q];
   gu.off_q1 = (int64_t)B.off[MOE_SEC_UP_Q];
   gu.off_sb0 = (int64_t)B.off[MOE_SEC_GATE_SB];
@@ -597,8 +632,8 @@ int launch_expert_forward_grouped(const moe_dims &d, const moe_layer &L, const u
   dn.C = d.inter;
   dn.off_q0 = dn.off_q1 = (int64_t)B.off[MOE_SEC_DOWN_Q];
   dn.off_sb0 = dn.off_sb1 = (int64_t)B.off[MOE_SEC_DOWN_SB];
-  const dim3 grid_gu((unsigned)(d.inter / kRT), (unsigned)maxB, (unsigned)nchunk_pairs);
-  const dim3 grid_dn((unsigned)(d.hidden / kRT), (unsigned)maxB, (unsigned)nchunk_pairs);
+  const dim3 grid_gu((unsigned)(d.inter / kRT), (unsigned)nitems);
+  const dim3 grid_dn((unsigned)(d.hidden / kRT), (unsigned)nitems);
   int rc = d.bits == 4 ? launch_gemms<4>(gu, dn, grid_gu, grid_dn, st)
                        : launch_gemms<2>(gu, dn, grid_gu, grid_dn, st);
   if (rc) return rc;

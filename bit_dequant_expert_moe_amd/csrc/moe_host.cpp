@@ -35,7 +35,6 @@ BlobLayout blob_layout(const moe_dims &d) {
 
 WsLayout ws_layout(const moe_dims &d, int T) {
   WsLayout W;
-  const size_t slots = (size_t)d.top_k + (size_t)d.has_shared;
   W.ctrl = kCtrlOff;
   W.fctrl = kFCtrlOff;
   W.logits_tag = kTagOff;
@@ -52,9 +51,8 @@ WsLayout ws_layout(const moe_dims &d, int T) {
   o = align_up(o + (size_t)T * (d.top_k + 1) * d.inter * 4, kAlign);
   W.bk = W.xb = W.xs = W.hb = W.hs = W.yd = o;
   if (T >= 2) {
-    const size_t maxB = (size_t)grouped_max_buckets(d, T);
     const size_t P = (size_t)T * (d.top_k + 1);  // pair codes
-    o = align_up(o + (2 + 2 * maxB + (size_t)T * slots) * 4, kAlign);
+    o = align_up(o + (size_t)grouped_bucket_words(d, T) * 4, kAlign);
     W.xb = o;
     o = align_up(o + (size_t)T * d.hidden * 2, kAlign);
     W.xs = o;

@@ -35,7 +35,7 @@ BlobLayout blob_layout(const moe_dims &d);
 //   w          : fp32 [T][K]
 //   h          : fp32 [T][K+1][I]   activations silu(g)*u per slot
 //   batched path (T >= 2) only:
-//   bk         : int32 buckets (expert, offsets, pair codes)
+//   bk         : int32 buckets (expert, offsets, pair codes, work items)
 //   xb, xs     : x as matrix-core B operand [T][H/8] x 16 B, group sums [T][H/64]
 //   hb, hs     : h as B operand [T][K+1][I/8] x 32 B (bf16 hi, lo), sums [T][K+1][I/64]
 //   yd         : fp32 [T][K+1][H]   per-slot down projections
@@ -117,6 +117,7 @@ int launch_dequantize(const moe_dims &d, const uint8_t *blob, int which, float *
                       void *stream);
 // Batched path (moe_grouped.hip): pairs grouped by expert, MFMA GEMMs.
 int grouped_max_buckets(const moe_dims &d, int T);
+int grouped_bucket_words(const moe_dims &d, int T);  // int32 words of the bucket area
 int launch_expert_forward_grouped(const moe_dims &d, const moe_layer &L, const uint16_t *x,
                                   int T, const int32_t *ids, const float *w, float *y, void *ws,
                                   void *stream);
