@@ -36,7 +36,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=128, help="timed decode tokens")
     ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--workload", default="stack60", choices=["stack60", "stack60_chain", "stack60_2bit", "batch64"])
+    ap.add_argument("--workload", default="stack60", choices=["stack60", "stack60_chain", "stack60_2bit", "batch64", "stack8_tier"])
     ap.add_argument("--layers", type=int, default=None, help="override layer count (testing)")
     ap.add_argument("--tokens", type=int, default=None, help="override distinct tokens")
     ap.add_argument("--cpu-layers", type=int, default=60,
@@ -111,6 +111,8 @@ def main():
     wl = WORKLOADS[args.workload]
     if wl.T > 1:
         return bench_batch(args, wl)
+    if wl.tier_slots:
+        return bench_tier(args, wl)
     nl = args.layers or wl.layers
     ntok = args.tokens or wl.tokens
     dims = moe.Dims(hidden=wl.H, inter=wl.I, n_experts=wl.E, top_k=wl.K, bits=wl.bits,
@@ -360,6 +362,116 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def bench_tier(args, wl):
+    """Decode through the off-HBM expert tier: every layer's experts in pinned
+    host memory, wl.tier_slots device slots shared by all layers (LRU), router
+    and shared expert resident.  A step is one token through all layers
+    (moe_tier_decode per layer: route, host waits for the ids, copies of the
+    missing experts over PCIe, expert forward).  The cache is warmed with
+    `warmup` tokens first.  No graph: the host takes part in every layer."""
+    import torch
+    import bit_dequant_expert_moe_amd as moe
+    import synth
+    nl = args.layers or wl.layers
+    ntok = args.tokens or wl.tokens
+    dims = moe.Dims(hidden=wl.H, inter=wl.I, n_experts=wl.E, top_k=wl.K, bits=wl.bits,
+                    has_shared=wl.has_shared)
+    blob = moe.moe_expert_bytes(dims)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    sp = torch.cuda.current_stream().cuda_stream
+    params = synth.BlobParams(seed=wl.blob_seed, H=wl.H, I=wl.I, bits=wl.bits, z_lo=wl.z_lo,
+                              z_hi=wl.z_hi)
+
+    def aligned(n, pin=False, device=None):
+        t = (torch.empty(n + 256, dtype=torch.uint8, pin_memory=True) if pin else
+             torch.empty(n + 256, dtype=torch.uint8, device=device))
+        off = (-t.data_ptr()) % 256
+        return t[off:off + n]
+
+    t0 = time.time()
+    host, shared, routers = [], [], []
+    stage = torch.empty(wl.E * blob, dtype=torch.uint8, device=dev)
+    for l in range(nl):
+        synth.gen_blobs_dev(params, l, 0, wl.E, stage.data_ptr(), blob, sp)
+        h = aligned(wl.E * blob, pin=True)
+        h.copy_(stage)
+        host.append(h)
+        sh = torch.empty(blob, dtype=torch.uint8, device=dev)
+        synth.gen_blobs_dev(params, l, 0xFFFF, 1, sh.data_ptr(), blob, sp)
+        shared.append(sh)
+        routers.append(torch.from_numpy(synth.router_weights(wl.seed, l, wl.E, wl.H)
+                                        .view(np.int16)).to(dev))
+    del stage
+    torch.cuda.synchronize()
+    log("host tier: %d layers x %d experts (%.1f GB pinned) in %.1fs" % (
+        nl, wl.E, nl * wl.E * blob / 1e9, time.time() - t0))
+    n_slots = wl.tier_slots
+    slots = aligned(n_slots * blob, device=dev)
+    staging = aligned(moe.moe_tier_staging_bytes(dims, 1), pin=True)
+    scratch = aligned(moe.moe_tier_device_bytes(dims, 1), device=dev)
+    copy_stream = torch.cuda.Stream()
+    tier = moe.Tier(dims, [h.data_ptr() for h in host], blob, slots, blob, n_slots, staging,
+                    scratch, t_max=1, copy_stream=copy_stream)
+    wsb = moe.moe_tier_workspace_bytes(dims, n_slots, 1)
+    ws = aligned(wsb, device=dev)
+    moe.moe_workspace_init(ws, wsb)
+    x_h = np.stack([synth.tokens_ar1(wl.seed, l, ntok, wl.H, wl.rho) for l in range(nl)], axis=1)
+    x = torch.from_numpy(x_h.view(np.int16)).to(dev)
+    y = torch.empty((ntok, nl, wl.H), dtype=torch.float32, device=dev)
+    ids = torch.empty((ntok, nl, wl.K), dtype=torch.int32, device=dev)
+
+    def token(t):
+        for l in range(nl):
+            tier.decode(l, routers[l], shared[l], x[t, l], 1, y[t, l], ids[t, l], None, ws, wsb,
+                        sp)
+
+    for i in range(args.warmup):
+        token(i % ntok)
+    torch.cuda.synchronize()
+    st0 = tier.stats()
+    tc = time.perf_counter()
+    for i in range(args.steps):
+        token((args.warmup + i) % ntok)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - tc
+    st1 = tier.stats()
+    hits, misses = st1["hits"] - st0["hits"], st1["misses"] - st0["misses"]
+    copied = st1["bytes"] - st0["bytes"]
+    ms_per_step = dt * 1e3 / args.steps
+    tok_s = args.steps / dt
+    hit_rate = hits / max(1, hits + misses)
+    log("tier decode: %.3f ms/token (%d layers), %.1f tok/s, %.1f us/layer, hit rate %.3f, "
+        "%.2f MB copied per token, %.1f GB/s over PCIe" % (
+            ms_per_step, nl, tok_s, ms_per_step * 1e3 / nl, hit_rate, copied / args.steps / 1e6,
+            copied / dt / 1e9))
+    err = moe.moe_get_device_error(ws, sp)
+    out = {
+        "metric": "MoE decode tokens/s through the host-memory expert tier (%d layers, batch 1)"
+                  % nl,
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u%d" % wl.bits + "+bf16/fp32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "layers": nl, "experts": wl.E, "top_k": wl.K,
+                   "bits": wl.bits, "device_slots": n_slots, "tokens": ntok},
+        "hit_rate": hit_rate,
+        "copied_bytes_per_token": copied / args.steps,
+        "pcie_GBps": copied / dt / 1e9,
+        "us_per_layer": ms_per_step * 1e3 / nl,
+        "device_error_flags": err,
+    }
+    print(json.dumps(out), flush=True)
+    tier.close()
 
 
 def bench_batch(args, wl):

@@ -23,7 +23,9 @@ SEC_GATE_Q, SEC_UP_Q, SEC_DOWN_Q, SEC_GATE_SB, SEC_UP_SB, SEC_DOWN_SB = range(6)
 EXPORTS = ("moe_abi_version", "moe_status_str", "moe_check_dims", "moe_expert_bytes",
            "moe_blob_layout", "moe_workspace_bytes", "moe_workspace_init", "moe_route",
            "moe_expert_forward", "moe_layer_decode", "moe_layer_decode_residual",
-           "moe_dequantize", "moe_get_device_error")
+           "moe_dequantize", "moe_get_device_error", "moe_tier_staging_bytes",
+           "moe_tier_device_bytes", "moe_tier_workspace_bytes", "moe_tier_create",
+           "moe_tier_decode", "moe_tier_plan", "moe_tier_stats", "moe_tier_destroy")
 
 
 class MoeError(RuntimeError):
@@ -40,6 +42,14 @@ class moe_dims(ctypes.Structure):
 class moe_layer(ctypes.Structure):
     _fields_ = [("router", ctypes.c_void_p), ("experts", ctypes.c_void_p),
                 ("expert_stride", ctypes.c_int64), ("shared", ctypes.c_void_p)]
+
+
+class moe_tier_config(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("t_max", ctypes.c_int32),
+                ("host_experts", ctypes.POINTER(ctypes.c_void_p)), ("host_stride", ctypes.c_int64),
+                ("slots", ctypes.c_void_p), ("slot_stride", ctypes.c_int64),
+                ("n_slots", ctypes.c_int32), ("copy_stream", ctypes.c_void_p),
+                ("staging", ctypes.c_void_p), ("dev_scratch", ctypes.c_void_p)]
 
 
 @dataclass(frozen=True)
@@ -83,6 +93,14 @@ def lib() -> ctypes.CDLL:
             "moe_layer_decode_residual": (i32, [dp, lp, vp, i32, vp, vp, vp, vp, vp, sz, vp]),
             "moe_dequantize": (i32, [dp, vp, i32, vp, vp]),
             "moe_get_device_error": (i32, [vp, vp, ctypes.POINTER(i32)]),
+            "moe_tier_staging_bytes": (sz, [dp, i32]),
+            "moe_tier_device_bytes": (sz, [dp, i32]),
+            "moe_tier_workspace_bytes": (sz, [dp, i32, i32]),
+            "moe_tier_create": (i32, [dp, ctypes.POINTER(moe_tier_config), ctypes.POINTER(vp)]),
+            "moe_tier_decode": (i32, [vp, i32, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]),
+            "moe_tier_plan": (i32, [vp, i32, vp, i32, vp, vp]),
+            "moe_tier_stats": (i32, [vp, ctypes.POINTER(ctypes.c_int64)]),
+            "moe_tier_destroy": (None, [vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -211,3 +229,80 @@ def moe_get_device_error(ws, stream=None) -> int:
     if rc not in (MOE_OK, -7):
         raise MoeError(rc, "moe_get_device_error")
     return int(err.value)
+
+
+# ---- off-HBM expert tier ----------------------------------------------------------
+
+class Tier:
+    """moe_tier_* over caller-owned buffers.  host_ptrs: one host address per
+    layer (pinned memory for asynchronous copies); slots, staging and
+    dev_scratch are addresses (or tensors) the caller keeps alive."""
+
+    def __init__(self, d: Dims, host_ptrs, host_stride: int, slots, slot_stride: int,
+                 n_slots: int, staging, dev_scratch, t_max: int = 1, copy_stream=None):
+        self.d = d
+        self._hosts = (ctypes.c_void_p * len(host_ptrs))(*[int(p) for p in host_ptrs])
+        cfg = moe_tier_config(len(host_ptrs), t_max, ctypes.cast(self._hosts,
+                              ctypes.POINTER(ctypes.c_void_p)), int(host_stride), _ptr(slots),
+                              int(slot_stride), n_slots, _ptr_stream(copy_stream), _ptr(staging),
+                              _ptr(dev_scratch))
+        self._cfg = cfg
+        h = ctypes.c_void_p()
+        _check(lib().moe_tier_create(ctypes.byref(d.c()), ctypes.byref(cfg), ctypes.byref(h)),
+               "moe_tier_create")
+        self.h = h
+        self.n_slots = n_slots
+
+    def plan(self, layer: int, ids, T: int):
+        """Host-only slot plan for int32 host ids [T][K]; returns (slots, copies)."""
+        import numpy as np
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        slots = np.empty(ids.size, dtype=np.int32)
+        copies = np.empty(ids.size, dtype=np.int32)
+        _check(lib().moe_tier_plan(self.h, layer, ids.ctypes.data, T, slots.ctypes.data,
+                                   copies.ctypes.data), "moe_tier_plan")
+        return slots, copies
+
+    def decode(self, layer: int, router, shared, x, T: int, y, ids=None, w=None, ws=None,
+               ws_bytes=None, stream=None):
+        rc = lib().moe_tier_decode(self.h, layer, _ptr(router), _ptr(shared), _ptr(x), T, _ptr(y),
+                                   _ptr(ids), _ptr(w), _ptr(ws),
+                                   ws_bytes if ws_bytes is not None else ws.numel(),
+                                   _stream(stream))
+        _check(rc, "moe_tier_decode")
+
+    def stats(self):
+        out = (ctypes.c_int64 * 4)()
+        _check(lib().moe_tier_stats(self.h, out), "moe_tier_stats")
+        return dict(hits=out[0], misses=out[1], bytes=out[2], evictions=out[3])
+
+    def close(self):
+        if getattr(self, "h", None):
+            lib().moe_tier_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _ptr_stream(stream):
+    if stream is None:
+        return None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def moe_tier_staging_bytes(d: Dims, t_max: int) -> int:
+    return int(lib().moe_tier_staging_bytes(ctypes.byref(d.c()), t_max))
+
+
+def moe_tier_device_bytes(d: Dims, t_max: int) -> int:
+    return int(lib().moe_tier_device_bytes(ctypes.byref(d.c()), t_max))
+
+
+def moe_tier_workspace_bytes(d: Dims, n_slots: int, T: int) -> int:
+    return int(lib().moe_tier_workspace_bytes(ctypes.byref(d.c()), n_slots, T))

@@ -6,7 +6,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe.so")
 SOURCES = [os.path.join(CSRC, "moe_host.cpp"), os.path.join(CSRC, "moe_kernels.hip"),
-           os.path.join(CSRC, "moe_fused.hip"), os.path.join(CSRC, "moe_grouped.hip")]
+           os.path.join(CSRC, "moe_fused.hip"), os.path.join(CSRC, "moe_grouped.hip"),
+           os.path.join(CSRC, "moe_tier.cpp")]
 HEADERS = [os.path.join(CSRC, "moe_internal.h"), os.path.join(CSRC, "moe_device.h"),
            os.path.join(os.path.dirname(HERE), "include", "moe.h")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

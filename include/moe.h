@@ -9,6 +9,7 @@
  *                                                               (moe_expert_forward)
  *   both, back to back on one stream                            (moe_layer_decode)
  *   RMS norm of the residual, the layer, residual add   (moe_layer_decode_residual)
+ *   experts held in host memory behind a device cache            (moe_tier_*)
  *
  * Sources for the method (web pages; cited by title and section):
  *   [HL] "Flash-MoE: Running a 397B Parameter Model on a Laptop" (hysenlabs.com),
@@ -59,7 +60,8 @@
  * ---------------------------------------------------------------------------
  * - All tensor pointers are DEVICE pointers (hipMalloc / torch allocations on
  *   the current device) unless stated otherwise; the caller owns them.  The
- *   library never allocates device or pinned memory.
+ *   library never allocates device or pinned memory (a tier object holds
+ *   host heap memory and two HIP events).
  * - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *   Every compute call only enqueues work on `stream` and returns; none of
  *   them synchronises the host, except moe_get_device_error.
@@ -218,6 +220,75 @@ moe_status moe_layer_decode_residual(const moe_dims *dims, const moe_layer *laye
                                      float *resid, int32_t T, uint16_t *x_out, float *y,
                                      int32_t *ids, float *w, void *ws, size_t ws_bytes,
                                      void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Off-HBM expert tier ([HL], "How the SSD expert streaming pipeline works":
+ * per token only the K routed experts of a layer are read from the slow tier,
+ * once the routing of that layer is known, and a least-recently-used page
+ * cache absorbs the reuse between tokens).  Here the slow tier is host memory
+ * (pinned, so that copies are asynchronous) and the cache is n_slots expert
+ * blobs in device memory, shared by all layers with least-recently-used
+ * replacement.  For GPUs, or expert sets, whose experts do not all fit in
+ * device memory; results are identical to moe_route + moe_expert_forward on
+ * resident experts (the same kernels run over the slots).
+ * A tier object holds host-side state only (allocated with the C++ heap); it
+ * is not thread-safe.
+ * ------------------------------------------------------------------------- */
+typedef struct moe_tier moe_tier;
+
+typedef struct {
+  int32_t n_layers;                   /* layers served by this tier */
+  int32_t t_max;                      /* most tokens per call, 1..256 */
+  const uint8_t *const *host_experts; /* host array of n_layers host pointers:
+                                         layer l's expert e at
+                                         host_experts[l] + e * host_stride */
+  int64_t host_stride;                /* bytes, >= moe_expert_bytes */
+  void *slots;                        /* device: n_slots blobs, 256-byte aligned */
+  int64_t slot_stride;                /* bytes, >= moe_expert_bytes, multiple of 256 */
+  int32_t n_slots;                    /* t_max * K <= n_slots <= 1024 */
+  void *copy_stream;                  /* hipStream_t of the host-to-device copies */
+  void *staging;                      /* pinned host, moe_tier_staging_bytes, 16-byte aligned */
+  void *dev_scratch;                  /* device, moe_tier_device_bytes, 256-byte aligned */
+} moe_tier_config;
+
+/* Sizes of the caller-owned buffers of a tier (0 if invalid).  Host only. */
+size_t moe_tier_staging_bytes(const moe_dims *dims, int32_t t_max);
+size_t moe_tier_device_bytes(const moe_dims *dims, int32_t t_max);
+/* Workspace bytes for tier calls of T tokens (covers the routing with E
+ * experts and the expert forward over n_slots slots).  Host only. */
+size_t moe_tier_workspace_bytes(const moe_dims *dims, int32_t n_slots, int32_t T);
+
+/* Creates a tier with every slot empty.  Validates the configuration; makes
+ * no HIP call.  *out receives the object (NULL on error). */
+moe_status moe_tier_create(const moe_dims *dims, const moe_tier_config *cfg, moe_tier **out);
+
+/* One layer for T tokens through the tier: moe_route on `stream` (router,
+ * x as in moe_route), the host waits for the ids (this call synchronises
+ * with `stream` once), missing experts are copied into least-recently-used
+ * slots on the copy stream, then the expert forward over the slots runs on
+ * `stream` after the copies.  shared: the layer's shared expert blob in
+ * device memory (NULL iff has_shared == 0).  y as in moe_layer_decode;
+ * ids/w (device, optional) receive the routing (real expert ids).  ws: at
+ * least moe_tier_workspace_bytes. */
+moe_status moe_tier_decode(moe_tier *tier, int32_t layer, const uint16_t *router,
+                           const uint8_t *shared, const uint16_t *x, int32_t T, float *y,
+                           int32_t *ids, float *w, void *ws, size_t ws_bytes, void *stream);
+
+/* Host-only test hook: the slot plan of one call for host expert ids
+ * [T][K] of `layer`, applied to the tier's state as moe_tier_decode would
+ * (no copy is made).  slot_ids (host) receive the slot of each id (-1 for an
+ * id outside [0, E)); copy_expert (host, optional) the expert copied into
+ * that slot by this call, or -1 for a hit. */
+moe_status moe_tier_plan(moe_tier *tier, int32_t layer, const int32_t *ids, int32_t T,
+                         int32_t *slot_ids, int32_t *copy_expert);
+
+/* Counters since creation: out[0] hits, out[1] misses (copies), out[2] bytes
+ * copied, out[3] evictions.  A repeat of an expert inside one call counts
+ * once.  Host only. */
+moe_status moe_tier_stats(const moe_tier *tier, int64_t out[4]);
+
+/* Frees the tier object (not the caller's buffers).  NULL is ignored. */
+void moe_tier_destroy(moe_tier *tier);
 
 /* Test hook: writes the dequantised fp32 matrix `which` (0 Gate [I][H],
  * 1 Up [I][H], 2 Down [H][I]) of one blob to out (row-major).  Each element

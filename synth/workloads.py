@@ -32,6 +32,7 @@ class Workload:
     chain: bool = False  # layers chained through the residual stream (x = norm(r), r += y)
     z_lo: float = -0.08  # bias range of the expert blobs
     z_hi: float = 0.08
+    tier_slots: int = 0  # > 0: experts in host memory behind this many device slots
     description: str = ""
 
 
@@ -63,6 +64,11 @@ WORKLOADS = {
                               description="the 60-layer stack chained through the residual "
                                           "stream: per layer x = norm(r), the MoE layer, "
                                           "r += y; 128 consecutive decode tokens"),
+    "stack8_tier": Workload("stack8_tier", 4096, 1024, 512, 4, 4, 8, 1, 128, 1002, 1002,
+                            rho=STACK_RHO, tier_slots=1024,
+                            description="8 layers x 512 4-bit experts in pinned host memory "
+                                        "behind 1024 device expert slots (LRU), 128 "
+                                        "consecutive decode tokens"),
     "batch64": Workload("batch64", 4096, 1024, 512, 4, 4, 1, 64, 1, 1003, 1003,
                         description="one full layer, 64 tokens routed independently"),
     "stack60_2bit": Workload("stack60_2bit", 4096, 1024, 512, 4, 2, 60, 1, 128, 1002, 1004,
