@@ -41,7 +41,7 @@ WsLayout ws_layout(const moe_dims &d, int T) {
   W.h_tag = kHTagOff;
   size_t o = align_up(kHeaderBytes, kAlign);
   W.logits = o;
-  o = align_up(o + (size_t)T * d.n_experts * 4, kAlign);
+  o = align_up(o + (size_t)route_splits(d, T) * T * d.n_experts * 4, kAlign);
   W.ids = o;
   o = align_up(o + (size_t)T * d.top_k * 4, kAlign);
   W.w = o;

@@ -14,6 +14,7 @@ constexpr int kMaxT = 256;
 constexpr int kMaxK = 8;
 constexpr int kMaxE = 1024;
 constexpr size_t kAlign = 256;
+constexpr int kMaxRouteSplits = 8;
 
 inline size_t align_up(size_t n, size_t a) { return (n + a - 1) / a * a; }
 
@@ -30,7 +31,7 @@ BlobLayout blob_layout(const moe_dims &d);
 //   logits_tag : uint64 [kGroups][kMaxE]  (fp32 logit bits | epoch << 32)
 //   h_tag      : uint64 [kGroups][5][1024] (fp32 h bits | epoch << 32)
 // then, not initialised:
-//   logits     : fp32 [T][E]
+//   logits     : fp32 [S][T][E] partial router sums (S <= kMaxRouteSplits)
 //   ids        : int32 [T][K]
 //   w          : fp32 [T][K]
 //   h          : fp32 [T][K+1][I]   activations silu(g)*u per slot
@@ -93,6 +94,16 @@ inline RowGeo row_geo(int cols, int bits) {
   g.rpl = 64 / g.lpr;
   g.nseg = g.seg_per_row / g.lpr;
   return g;
+}
+
+// Column splits of the router for T tokens: blocks of 16 experts x 16 tokens
+// are split along the hidden dimension until about 256 blocks stream the
+// router (each wave keeps whole 32-column steps).
+inline int route_splits(const moe_dims &d, int T) {
+  const int blocks = ((d.n_experts + 15) / 16) * ((T + 15) / 16);
+  int s = 1;
+  while (s < kMaxRouteSplits && blocks * s < 256 && d.hidden % (128 * 2 * s) == 0) s *= 2;
+  return s;
 }
 
 // Kernel launchers (moe_kernels.hip).  Each returns hipSuccess (0) or the

@@ -108,21 +108,26 @@ struct RouteArgs {
   int32_t *ids;
   float *w, *logits_out, *logits;
   int H, E, K, T;
+  int S;  // splits of the hidden dimension over blocks (partial logits [S][T][E])
 };
 
-// Block = 16 experts x 16 tokens; the 4 waves split the hidden dimension and
-// their partial tiles are summed in a fixed order.
+// Block = 16 experts x 16 tokens x one of S column ranges; the 4 waves split
+// the block's columns and their partial tiles are summed in a fixed order.
+// With few tokens the columns are split over S blocks as well, so that the
+// router matrix streams through enough workgroups to fill the chip; k_topk
+// adds the S partials in order.
 __global__ void __launch_bounds__(256) k_router(RouteArgs a) {
   __shared__ f32x4_t s_part[4][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row = lane & 15, q = lane >> 4;
   const int e0 = 16 * blockIdx.x, t0 = 16 * blockIdx.y;
   const int e = e0 + row, t = t0 + row;
-  const int kw = a.H / 4;  // columns per wave
+  const int kw = a.H / (4 * a.S);  // columns per wave
+  const size_t c0 = (size_t)blockIdx.z * (a.H / a.S) + (size_t)wave * kw;
   const uint4 *wr = reinterpret_cast<const uint4 *>(a.router + (size_t)(e < a.E ? e : 0) * a.H +
-                                                    (size_t)wave * kw + 8 * q);
+                                                    c0 + 8 * q);
   const uint4 *xr = reinterpret_cast<const uint4 *>(a.x + (size_t)(t < a.T ? t : 0) * a.H +
-                                                    (size_t)wave * kw + 8 * q);
+                                                    c0 + 8 * q);
   const bool ev = e < a.E, tv = t < a.T;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
@@ -147,29 +152,53 @@ __global__ void __launch_bounds__(256) k_router(RouteArgs a) {
     }
     // element v of lane: expert e0 + 4 q + v, token t0 + row
     if (t0 + row < a.T) {
+      float *lp = a.logits + ((size_t)blockIdx.z * a.T + t0 + row) * a.E;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int ee = e0 + 4 * q + v;
-        if (ee < a.E) {
-          a.logits[(size_t)(t0 + row) * a.E + ee] = r[v];
-          if (a.logits_out) a.logits_out[(size_t)(t0 + row) * a.E + ee] = r[v];
-        }
+        if (ee < a.E) lp[ee] = r[v];
       }
     }
   }
 }
 
-// One wave per token: top-K of the logits (largest first; equal logits ->
-// lower index), weights = softmax over the selected logits.
-__global__ void __launch_bounds__(64) k_topk(RouteArgs a) {
-  const int t = blockIdx.x, lane = threadIdx.x;
+// One block per token: the 4 waves add the S partial logits in order (all
+// loads in flight at once) into LDS, then wave 0 selects the top-K (largest
+// first; equal logits -> lower index) and the weights = softmax over the
+// selected logits.
+__global__ void __launch_bounds__(256) k_topk(RouteArgs a) {
+  __shared__ float s_l[kMaxE];
+  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const float *lt = a.logits + (size_t)t * a.E;
+  constexpr int NI = kMaxE / 256;
+  float p[NI][kMaxRouteSplits];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int idx = tid + 256 * i;
+#pragma unroll
+    for (int sp = 0; sp < kMaxRouteSplits; ++sp)
+      p[i][sp] = (idx < a.E && sp < a.S) ? lt[(size_t)sp * a.T * a.E + idx] : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int idx = tid + 256 * i;
+    if (idx < a.E) {
+      float v = p[i][0];
+#pragma unroll
+      for (int sp = 1; sp < kMaxRouteSplits; ++sp)
+        if (sp < a.S) v += p[i][sp];
+      s_l[idx] = v;
+      if (a.logits_out) a.logits_out[(size_t)t * a.E + idx] = v;
+    }
+  }
+  __syncthreads();
+  if (tid >= 64) return;
   constexpr int NV = kMaxE / 64;
   uint64_t key[NV];
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int idx = lane + 64 * j;
-    const float v = idx < a.E ? lt[idx] : __builtin_nanf("");
+    const float v = idx < a.E ? s_l[idx] : __builtin_nanf("");
     key[j] = ((uint64_t)f32_order_key(v) << 32) | (0xFFFFFFFFu - (uint32_t)idx);
   }
   float sel_v[kMaxK];
@@ -186,14 +215,14 @@ __global__ void __launch_bounds__(64) k_topk(RouteArgs a) {
     for (int j = 0; j < NV; ++j) key[j] = key[j] == m ? 0 : key[j];
   }
   if (lane == 0) {
-    float den = 0.f, p[kMaxK];
+    float den = 0.f, pk[kMaxK];
     for (int k = 0; k < a.K; ++k) {
-      p[k] = expf(sel_v[k] - sel_v[0]);
-      den += p[k];
+      pk[k] = expf(sel_v[k] - sel_v[0]);
+      den += pk[k];
     }
     for (int k = 0; k < a.K; ++k) {
       a.ids[(size_t)t * a.K + k] = sel_i[k];
-      a.w[(size_t)t * a.K + k] = p[k] / den;
+      a.w[(size_t)t * a.K + k] = pk[k] / den;
     }
   }
 }
@@ -485,9 +514,10 @@ int launch_route(const moe_dims &d, const uint16_t *router, const uint16_t *x, i
   a.E = d.n_experts;
   a.K = d.top_k;
   a.T = T;
-  hipLaunchKernelGGL(k_router, dim3((d.n_experts + 15) / 16, (T + 15) / 16), dim3(256), 0,
+  a.S = route_splits(d, T);
+  hipLaunchKernelGGL(k_router, dim3((d.n_experts + 15) / 16, (T + 15) / 16, a.S), dim3(256), 0,
                      S(stream), a);
-  hipLaunchKernelGGL(k_topk, dim3(T), dim3(64), 0, S(stream), a);
+  hipLaunchKernelGGL(k_topk, dim3(T), dim3(256), 0, S(stream), a);
   return (int)hipGetLastError();
 }
 
