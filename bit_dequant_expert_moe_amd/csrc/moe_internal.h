@@ -10,7 +10,7 @@
 namespace moe {
 
 constexpr int kGroup = 64;
-constexpr int kMaxT = 256;
+constexpr int kMaxT = 4096;  // tokens per call (a prefill chunk)
 constexpr int kMaxK = 8;
 constexpr int kMaxE = 1024;
 constexpr size_t kAlign = 256;

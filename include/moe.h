@@ -169,7 +169,7 @@ moe_status moe_workspace_init(void *ws, size_t ws_bytes, void *stream);
  *             to sum to 1 (a reading: the pages do not say whether they
  *             renormalise; here they do).
  * Arguments: x bf16 [T][H] (16-byte aligned); ids int32 [T][K]; w fp32 [T][K];
- * logits fp32 [T][E] or NULL.  1 <= T <= 256. */
+ * logits fp32 [T][E] or NULL.  1 <= T <= 4096 (every entry point). */
 moe_status moe_route(const moe_dims *dims, const uint16_t *router,
                      const uint16_t *x, int32_t T, int32_t *ids, float *w,
                      float *logits, void *ws, size_t ws_bytes, void *stream);
@@ -238,7 +238,7 @@ typedef struct moe_tier moe_tier;
 
 typedef struct {
   int32_t n_layers;                   /* layers served by this tier */
-  int32_t t_max;                      /* most tokens per call, 1..256 */
+  int32_t t_max;                      /* most tokens per call (t_max K <= n_slots) */
   const uint8_t *const *host_experts; /* host array of n_layers host pointers:
                                          layer l's expert e at
                                          host_experts[l] + e * host_stride */

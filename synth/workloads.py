@@ -71,6 +71,9 @@ WORKLOADS = {
                                         "consecutive decode tokens"),
     "batch64": Workload("batch64", 4096, 1024, 512, 4, 4, 1, 64, 1, 1003, 1003,
                         description="one full layer, 64 tokens routed independently"),
+    "prefill4096": Workload("prefill4096", 4096, 1024, 512, 4, 4, 1, 4096, 1, 1006, 1006,
+                            description="one full layer, a prefill chunk of 4096 tokens "
+                                        "routed independently"),
     "stack60_2bit": Workload("stack60_2bit", 4096, 1024, 512, 4, 2, 60, 1, 128, 1002, 1004,
                              rho=STACK_RHO,
                              description="the 60-layer stack with 2-bit codes, same routers "

@@ -71,7 +71,8 @@ def test_workspace_bytes():
     # h [T][K+1][I] fp32 dominates
     assert n64 >= 64 * 5 * 1024 * 4
     assert moe.moe_workspace_bytes(D, 0) == 0
-    assert moe.moe_workspace_bytes(D, 257) == 0
+    assert moe.moe_workspace_bytes(D, 4097) == 0
+    assert moe.moe_workspace_bytes(D, 4096) > moe.moe_workspace_bytes(D, 256)
     assert n1 % 256 == 0
 
 
@@ -100,7 +101,7 @@ def test_route_validation():
     assert _status(moe.moe_route, **_route(ids=None)) == -1
     assert _status(moe.moe_route, **_route(ws=None)) == -1
     assert _status(moe.moe_route, **_route(T=0)) == -2
-    assert _status(moe.moe_route, **_route(T=300)) == -2
+    assert _status(moe.moe_route, **_route(T=4097)) == -2
     assert _status(moe.moe_route, **_route(x=A + 8)) == -4
     assert _status(moe.moe_route, **_route(ws=WS + 16)) == -4
     assert _status(moe.moe_route, **_route(ws_bytes=100)) == -5

@@ -304,3 +304,30 @@ def test_fused_no_shared_expert():
     for t in range(3):
         x = synth.tokens(777, 10 + t, 1, 4096)
         _layer_check(L, x, "fused, no shared expert, token %d" % t)
+
+
+# ---- prefill chunks: many tokens per call ----------------------------------------
+
+@pytest.mark.parametrize("T", [1024, 4096])
+def test_prefill_chunk_sampled(full, T):
+    # all 512 experts in play, the shared expert's bucket holds T pairs
+    # (T / 16 work items); sampled tokens against the oracle, teacher-forced
+    x = synth.tokens(1001, 40 + T, T, 4096)
+    out = full.decode(x)
+    assert out["err"] == 0
+    sample = sorted({0, 1, T // 3, T // 2, T - 2, T - 1})
+    _, _, logits_o, gap_o = oracle.route(full.od, full.router_h, x[sample])
+    gu.check_routing(full.od, out["ids"][sample], out["w"][sample], logits_o, gap_o, 4)
+    wf = np.empty((len(sample), 4))
+    for i, t in enumerate(sample):
+        sel = logits_o[i][out["ids"][t]]
+        e = np.exp(sel - sel.max())
+        wf[i] = e / e.sum()
+    y_o = oracle.expert_forward(full.od, full.blob_host, full.shared_host(), x[sample],
+                                out["ids"][sample], wf)
+    err = gu.max_rel_err(out["y"][sample], y_o)
+    _say("  prefill T=%d, %d sampled tokens: max|dy|/max|y| = %.3e" % (T, len(sample), err))
+    assert err <= gu.Y_TOL
+    # every token's row is finite and the routing uses many experts
+    assert np.isfinite(out["y"]).all()
+    assert len(np.unique(out["ids"])) > 400

@@ -64,7 +64,7 @@ def test_buffer_sizes():
     assert moe.moe_tier_device_bytes(D, 1) == 3 * 256
     assert moe.moe_tier_staging_bytes(D, 256) == 2 * 4096
     assert moe.moe_tier_staging_bytes(D, 0) == 0
-    assert moe.moe_tier_device_bytes(D, 257) == 0
+    assert moe.moe_tier_device_bytes(D, 4097) == 0
     big = moe.moe_tier_workspace_bytes(D, 1024, 4)
     assert big >= moe.moe_workspace_bytes(D, 4)
     assert big >= moe.moe_workspace_bytes(moe.Dims(hidden=4096, inter=1024, n_experts=1024,
@@ -77,7 +77,7 @@ def test_buffer_sizes():
     (dict(n_slots=7, t_max=2), -2),
     (dict(n_slots=1025), -2),
     (dict(t_max=0), -2),
-    (dict(t_max=300, n_slots=1024), -2),
+    (dict(t_max=300, n_slots=1024), -2),   # t_max K > n_slots
     (dict(host_stride=BLOB - 16), -2),
     (dict(slot_stride=BLOB + 16), -4),
     (dict(slots=A + (1 << 40) + 64), -4),
