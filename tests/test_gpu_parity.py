@@ -155,13 +155,18 @@ def test_layer_decode_2bit_tiny():
 
 @pytest.mark.parametrize("cfg", [
     (256, 256, 8, 2, 4, 1), (512, 2048, 32, 8, 4, 1), (1024, 256, 4, 4, 2, 0),
-    (8192, 512, 64, 1, 4, 1), (2048, 4096, 16, 3, 2, 1), (16384, 256, 2, 2, 4, 1)])
+    (8192, 512, 64, 1, 4, 1), (2048, 4096, 16, 3, 2, 1), (16384, 256, 2, 2, 4, 1),
+    # expert counts off the 16-row router tiles; 1000 experts take the fused
+    # kernel's four router rows per workgroup, with rows past E
+    (4096, 1024, 100, 4, 4, 1), (4096, 1024, 1000, 4, 4, 1), (4096, 1024, 1000, 4, 2, 0)])
 def test_layer_decode_shapes(cfg):
+    # one token (the single-token kernels) and three (the grouped path)
     H, I, E, K, bits, sh = cfg
     _say("shape", cfg)
     L = gu.DeviceLayer(H, I, E, K, bits=bits, has_shared=sh, seed=300 + H + I + E)
-    x = synth.tokens(L.seed, 1, 3, H)
-    _layer_check(L, x, "shape %s" % (cfg,))
+    for T in (1, 3):
+        x = synth.tokens(L.seed, T, T, H)
+        _layer_check(L, x, "shape %s T=%d" % (cfg, T))
 
 
 def test_expert_stride_padding():
