@@ -205,7 +205,7 @@ struct GL {  // LDS geometry
   static constexpr int BCS = kSl * BV + 1;        // uint4 per staged B column (+1 against bank conflicts)
   static constexpr int BPT = kNC * kSl * BV / 256;  // B pieces per thread
   static constexpr int A_U32 = NMAT * kRT * RW;
-  static constexpr int SB_U32 = NMAT * kRT * kGC;
+  static constexpr int SB_U32 = NMAT * kRT * kGC * 2;  // float2 (s, z - 128 s) per row and group
   static constexpr int B_U32 = kNC * BCS * 4;
   static constexpr int XS_U32 = kNC * kGC;
   static constexpr int BUF_U32 = A_U32 + SB_U32 + B_U32 + XS_U32;
@@ -217,32 +217,50 @@ struct GL {  // LDS geometry
   static_assert((A_U32 + SB_U32) % 4 == 0, "B area 16-byte aligned");
 };
 
-// Two bf16 (hi half, lo half) of 128 + the fields selected by mask m.  Plain
-// C (the compiler forms v_and_or_b32): an inline-asm producer is opaque to the
-// hazard checks that keep a VALU write from overtaking an MFMA still reading
-// the same register.
-__device__ __forceinline__ uint32_t magic_pair(uint32_t v, uint32_t m) {
-  return (v & m) | 0x43004300u;
+// Two bf16 (hi half, lo half) of 128 + the fields selected by mask m, with
+// M = 0x43004300 (the pair 128, 128).  Plain C, so that the hazard checks
+// that keep a VALU write from overtaking an MFMA still reading the register
+// see it; m and M arrive in registers (see Unpack), so the compiler can form
+// one v_and_or_b32 (VOP3 takes no literal operand on this target).
+__device__ __forceinline__ uint32_t magic_pair(uint32_t v, uint32_t m, uint32_t M) {
+  return (v & m) | M;
 }
+
+// The unpack constants, held in registers: the field mask in an SGPR, the
+// magic pair in a VGPR (an empty asm statement hides their values from
+// constant folding, which would otherwise split each v_and_or_b32 into a
+// v_and_b32 and a v_or_b32 with literals).
+struct Unpack {
+  uint32_t m, M;
+  template <int BITS>
+  __device__ static Unpack make() {
+    Unpack u;
+    u.m = BITS == 4 ? 0x000F000Fu : 0x00030003u;
+    u.M = 0x43004300u;
+    asm volatile("" : "+s"(u.m));
+    asm volatile("" : "+v"(u.M));
+    return u;
+  }
+};
 
 // A operand of one 8-column slice: bf16 128 + q in the order
 // (c0, c4, c1, c5, c2, c6, c3, c7).  For 2-bit codes the slice is one half
 // (16 bits) of a word.
 template <int BITS>
-__device__ __forceinline__ bf16x8 a_slice(uint32_t word, int half) {
+__device__ __forceinline__ bf16x8 a_slice(uint32_t word, int half, const Unpack &k) {
   uint32_t p[4];
   if (BITS == 4) {
-    p[0] = magic_pair(word, 0x000F000Fu);
-    p[1] = magic_pair(word >> 4, 0x000F000Fu);
-    p[2] = magic_pair(word >> 8, 0x000F000Fu);
-    p[3] = magic_pair(word >> 12, 0x000F000Fu);
+    p[0] = magic_pair(word, k.m, k.M);
+    p[1] = magic_pair(word >> 4, k.m, k.M);
+    p[2] = magic_pair(word >> 8, k.m, k.M);
+    p[3] = magic_pair(word >> 12, k.m, k.M);
   } else {
     const uint32_t h16 = half ? (word >> 16) : (word & 0xFFFFu);
     const uint32_t v = h16 | (h16 << 8);  // c_{j+4} lands 16 bits above c_j
-    p[0] = magic_pair(v, 0x00030003u);
-    p[1] = magic_pair(v >> 2, 0x00030003u);
-    p[2] = magic_pair(v >> 4, 0x00030003u);
-    p[3] = magic_pair(v >> 6, 0x00030003u);
+    p[0] = magic_pair(v, k.m, k.M);
+    p[1] = magic_pair(v >> 2, k.m, k.M);
+    p[2] = magic_pair(v >> 4, k.m, k.M);
+    p[3] = magic_pair(v >> 6, k.m, k.M);
   }
   uint4 u = make_uint4(p[0], p[1], p[2], p[3]);
   return __builtin_bit_cast(bf16x8, u);
@@ -378,7 +396,21 @@ __global__ void __launch_bounds__(256) k_grouped(GroupArgs a) {
       dst[2] = R.ra[i].z;
       dst[3] = R.ra[i].w;
     }
-    if (tid < G::NMAT * kRT) *reinterpret_cast<uint4 *>(SB + tid * kGC) = R.rsb;
+    if (tid < G::NMAT * kRT) {
+      // per group (s, z - 128 s): the MFMA sums (128 + q) b, so
+      // s sum q b + z sum b = s P + (z - 128 s) X
+      const uint32_t w4[4] = {R.rsb.x, R.rsb.y, R.rsb.z, R.rsb.w};
+      float f[8];
+#pragma unroll
+      for (int g = 0; g < kGC; ++g) {
+        const float sc = bf16f(w4[g] & 0xFFFFu), zb = bf16f(w4[g] >> 16);
+        f[2 * g] = sc;
+        f[2 * g + 1] = fmaf(-128.f, sc, zb);
+      }
+      float4 *dst = reinterpret_cast<float4 *>(SB + tid * kGC * 2);
+      dst[0] = make_float4(f[0], f[1], f[2], f[3]);
+      dst[1] = make_float4(f[4], f[5], f[6], f[7]);
+    }
 #pragma unroll
     for (int i = 0; i < G::BPT; ++i) {
       const int pc = tid + 256 * i;
@@ -392,6 +424,7 @@ __global__ void __launch_bounds__(256) k_grouped(GroupArgs a) {
 #pragma unroll
   for (int m = 0; m < G::NMAT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int ar = wave * 16 + col;  // A row of this lane within the tile
+  const Unpack uk = Unpack::make<BITS>();
 
   auto compute_chunk = [&](int buf) {
     const uint32_t *A = lds + (size_t)buf * G::BUF_U32;
@@ -413,7 +446,7 @@ __global__ void __launch_bounds__(256) k_grouped(GroupArgs a) {
 #pragma unroll
         for (int m = 0; m < G::NMAT; ++m) {
           const uint32_t w = A[(m * kRT + ar) * G::RW + (BITS == 4 ? sl : (sl >> 1))];
-          const bf16x8 av = a_slice<BITS>(w, sl & 1);
+          const bf16x8 av = a_slice<BITS>(w, sl & 1, uk);
 #pragma unroll
           for (int u = 0; u < G::BV; ++u)
             P[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[u], P[m], 0, 0, 0);
@@ -425,8 +458,9 @@ __global__ void __launch_bounds__(256) k_grouped(GroupArgs a) {
       for (int m = 0; m < G::NMAT; ++m)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const uint32_t sb = SB[(m * kRT + wave * 16 + 4 * q + v) * kGC + gi];
-          acc[m][v] += bf16f(sb & 0xFFFFu) * (P[m][v] - 128.f * X) + bf16f(sb >> 16) * X;
+          const float2 sz =
+              reinterpret_cast<const float2 *>(SB)[(m * kRT + wave * 16 + 4 * q + v) * kGC + gi];
+          acc[m][v] = fmaf(sz.x, P[m][v], fmaf(sz.y, X, acc[m][v]));
         }
     }
   };
