@@ -306,7 +306,8 @@ moe_status moe_dequantize(const moe_dims *dims, const uint8_t *blob,
                           int32_t which, float *out, void *stream);
 
 /* Synchronises `stream`, returns the workspace's sticky device error flags in
- * *err (0 = none; bit 0 = an expert id was out of range) and clears them.
+ * *err (0 = none; bit 0 = an expert id was out of range; bit 1 = a wait of
+ * the single-token kernel timed out, see the conventions) and clears them.
  * `err` is a host pointer.  Returns MOE_ERR_DEVICE when *err != 0. */
 moe_status moe_get_device_error(void *ws, void *stream, int32_t *err);
 
