@@ -240,7 +240,9 @@ moe_status moe_layer_decode_residual(const moe_dims *dims, const moe_layer *laye
  * device memory; results are identical to moe_route + moe_expert_forward on
  * resident experts (the same kernels run over the slots).
  * A tier object holds host-side state only (allocated with the C++ heap); it
- * is not thread-safe.
+ * is not thread-safe, and all calls on one tier must be issued on one compute
+ * stream (a slot is overwritten only after every kernel enqueued before the
+ * call's routing on that stream has finished).
  * ------------------------------------------------------------------------- */
 typedef struct moe_tier moe_tier;
 
