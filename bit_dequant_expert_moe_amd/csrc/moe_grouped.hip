@@ -205,7 +205,9 @@ struct GL {  // LDS geometry
   static constexpr int BCS = kSl * BV + 1;        // uint4 per staged B column (+1 against bank conflicts)
   static constexpr int BPT = kNC * kSl * BV / 256;  // B pieces per thread
   static constexpr int A_U32 = NMAT * kRT * RW;
-  static constexpr int SB_U32 = NMAT * kRT * kGC * 2;  // float2 (s, z - 128 s) per row and group
+  // gate/up: float2 (s, z - 128 s) per row and group; down: the (s, z) words
+  // (the smaller area keeps three down blocks within a compute unit's LDS)
+  static constexpr int SB_U32 = NMAT * kRT * kGC * (DOWN ? 1 : 2);
   static constexpr int B_U32 = kNC * BCS * 4;
   static constexpr int XS_U32 = kNC * kGC;
   static constexpr int BUF_U32 = A_U32 + SB_U32 + B_U32 + XS_U32;
@@ -396,7 +398,9 @@ __global__ void __launch_bounds__(256) k_grouped(GroupArgs a) {
       dst[2] = R.ra[i].z;
       dst[3] = R.ra[i].w;
     }
-    if (tid < G::NMAT * kRT) {
+    if (DOWN) {
+      if (tid < kRT) *reinterpret_cast<uint4 *>(SB + tid * kGC) = R.rsb;
+    } else if (tid < G::NMAT * kRT) {
       // per group (s, z - 128 s): the MFMA sums (128 + q) b, so
       // s sum q b + z sum b = s P + (z - 128 s) X
       const uint32_t w4[4] = {R.rsb.x, R.rsb.y, R.rsb.z, R.rsb.w};
@@ -458,9 +462,14 @@ __global__ void __launch_bounds__(256) k_grouped(GroupArgs a) {
       for (int m = 0; m < G::NMAT; ++m)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float2 sz =
-              reinterpret_cast<const float2 *>(SB)[(m * kRT + wave * 16 + 4 * q + v) * kGC + gi];
-          acc[m][v] = fmaf(sz.x, P[m][v], fmaf(sz.y, X, acc[m][v]));
+          if (DOWN) {
+            const uint32_t sb = SB[(wave * 16 + 4 * q + v) * kGC + gi];
+            acc[m][v] += bf16f(sb & 0xFFFFu) * (P[m][v] - 128.f * X) + bf16f(sb >> 16) * X;
+          } else {
+            const float2 sz =
+                reinterpret_cast<const float2 *>(SB)[(m * kRT + wave * 16 + 4 * q + v) * kGC + gi];
+            acc[m][v] = fmaf(sz.x, P[m][v], fmaf(sz.y, X, acc[m][v]));
+          }
         }
     }
   };
