@@ -1,6 +1,7 @@
 """Run by tests/test_gpu_paths.py in a child process whose environment
 selects a dispatch path (MOE_DISABLE_FUSED=1: the three-kernel single-token
-path; MOE_DISABLE_GROUPED=1: the per-token kernels for several tokens).  The
+path; MOE_DISABLE_GROUPED=1: the per-token kernels for more tokens than
+the single-token kernel takes one launch each).  The
 library reads these switches once per process, hence the child.  Prints one
 JSON line with the worst relative output error against the oracle."""
 import json
@@ -20,7 +21,7 @@ def main():
     worst, cases = 0.0, 0
     for bits in (4, 2):
         L = gu.DeviceLayer(4096, 1024, 32, 4, bits=bits, seed=3000 + bits)
-        for T in (1, 3):
+        for T in (1, 5):
             x = synth.tokens(3000 + bits, T, T, 4096)
             out = L.decode(x, want_logits=True)
             assert out["err"] == 0
