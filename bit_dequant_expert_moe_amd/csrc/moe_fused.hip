@@ -16,10 +16,17 @@
 //     epoch of the call); every workgroup reads the E words until all carry
 //     the current epoch -- the data arrives with the signal -- and selects
 //     the top-K itself (the selection is deterministic, so all agree);
-//   * activations h of slot k: the four gate/up waves of a workgroup hand
-//     their values over in LDS; the workgroup writes them as tagged 64-bit
-//     words; every workgroup reads the slot's I words until all are current
-//     and copies them into LDS for its down waves.
+//   * activations h: each gate/up wave writes its row of every slot as a
+//     tagged 64-bit word as soon as it is computed.  The down rows of the
+//     shared expert are split over all workgroups (16 each), those of routed
+//     slot k over workgroups 64k .. 64k+63 (64 rows each), so a workgroup
+//     reads the I words of two slots only (shared, own routed slot) until
+//     all are current, into LDS for its down waves;
+//   * routed down sums: the workgroup that computed routed rows r of slot k
+//     writes their weighted sums as tagged words; the workgroup that owns
+//     output rows r (16 per workgroup, those of its shared rows) reads the
+//     four slots' sums of its rows (one reader per word) and forms
+//     y = shared + slot 0 + .. + slot K-1 in that order.
 // Every word that all workgroups read is written once per reader group
 // (blockIdx % 8, one per XCD), so each cache line has ~32 coherent readers:
 // a line read coherently by all 256 CUs at once serialises at its memory
@@ -30,8 +37,11 @@
 //
 // Each workgroup has 8 waves (two per SIMD, so 256 VGPRs each): waves 0-3
 // compute gate/up rows (one row of every slot each), waves 4-7 compute down
-// rows (four output rows of every slot each).  Wave 4 also selects the top-K
-// and runs the activation exchange.  Weight bytes are requested as soon as
+// rows (four shared rows and 16 rows of the own routed slot each).  Wave 4
+// also selects the top-K and runs the reads of the exchanges.  Compared with
+// every workgroup reading all five slots (one ~1 us round trip per slot at
+// the end of the layer), this layout reads two slots and one small block of
+// sums, 1.2 us per layer less.  Weight bytes are requested as soon as
 // their addresses are known: router, shared expert and x at launch, routed
 // experts right after the top-K, gate/up rows first (the activation exchange
 // waits on them; the down rows are needed only after it, ~1 us per layer
@@ -43,16 +53,19 @@
 // to a polling workgroup is ~0.7 us; an all-gather round over 256 workgroups
 // ~2.3-2.6 us, longer with more bytes polled per round and under HBM
 // streaming.  Polling several slots per round, spreading the polls over more
-// waves or more copies, and splitting stores and polls into separate waves
-// all measured slower than this layout.
+// waves or more copies, and polling from the gate/up waves all measured
+// slower than this layout.  Publishing from the gate/up waves directly, not
+// through the polling wave, is ~0.5 us per layer faster: a wave waiting on a
+// poll cannot publish.
 //
 // Residual mode (RES): the layer also runs the two steps around it on the
 // residual stream r (fp32, updated in place): x = bf16(r / rms(r)) before the
 // router, r += y after the combine.  Every workgroup normalises the whole
 // vector itself (16 KB from L2; no extra exchange), and writes its own rows of
-// r only after it has received every workgroup's activations, which every
-// workgroup publishes only after it has read all of r: reads of r in any
-// workgroup precede writes of r in every workgroup.
+// r only after it has received the routed sums of those rows, which were
+// formed from activations that every workgroup publishes only after it has
+// read all of r: reads of r in any workgroup precede writes of r in every
+// workgroup.
 //
 // Termination: every wait is bounded; a wait that times out sets bit 1 of
 // the sticky error word and the kernel runs to completion.
@@ -110,6 +123,14 @@ __device__ __forceinline__ uint4 ld_coh16(const void *base, uint32_t byte_off) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// 8-byte coherent load, the same policy.
+__device__ __forceinline__ uint2 ld_coh8(const void *base, uint32_t byte_off) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, 0x7fffffff, 0x00020000);
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)byte_off, 0, 16 /* sc1 */);
+  return make_uint2(v[0], v[1]);
+}
+
 // Weight loads through a buffer resource of the blob: the per-lane byte
 // offsets are the same 32-bit values for every expert, only the (scalar)
 // resource changes, which keeps 64-bit address arithmetic out of the vector
@@ -153,6 +174,14 @@ struct Geo {
   static_assert(DLD >= 1 && D_ROWS_W % RPL == 0, "down rows must tile the waves");
   static_assert(RXC >= 1 && RCH % kNT == 0, "router row must span the workgroup");
   static_assert(SEG_X <= 64 * kGuWaves, "one x segment per gate/up thread");
+  // the down rows of each routed slot are split over OWN_WG workgroups
+  static constexpr int OWN_WG = kG / K;             // workgroups per routed slot
+  static constexpr int O_ROWS = H / OWN_WG;         // routed down rows per workgroup
+  static constexpr int O_ROWS_W = O_ROWS / kDownWaves;  // per down wave
+  static constexpr int RDLD = O_ROWS_W / RPL;       // routed down loads per lane
+  static_assert(kG % K == 0 && H % OWN_WG == 0, "routed rows must tile the workgroups");
+  static_assert(RDLD >= 1 && O_ROWS_W % RPL == 0 && O_ROWS_W <= 64, "routed rows per wave");
+  static_assert(K * D_ROWS == 64, "one routed sum per lane of the exchange wave");
 };
 
 struct FusedArgs {
@@ -168,6 +197,7 @@ struct FusedArgs {
   FCtrl *fc;
   uint64_t *tags;         // [kGroups][kMaxE] tagged logits
   uint64_t *htag;         // [kGroups][K+1][I] tagged activations
+  uint64_t *ptag;         // [K][H] tagged routed down sums
   float *resid;           // residual mode: r, fp32 [H], read and updated in place
   uint16_t *x_out;        // residual mode: the normalised x, bf16 [H], or null
   int E, has_shared;
@@ -175,11 +205,15 @@ struct FusedArgs {
 };
 
 // sum_c q_c h_c over the codes of one 32-bit word (8 at 4 bits, 16 at 2 bits)
-// of a down row, fp32; hv holds the word's activations.
+// of a down row, fp32; hv holds the word's activations.  m is the per-byte
+// code mask (0x0F0F0F0F or 0x03030303) in a register the compiler cannot see
+// through: with a literal it merges the masks into one bit-field extract per
+// code, while from a masked word every byte converts in one instruction
+// (v_cvt_f32_ubyte0..3).
 template <int BITS>
-__device__ __forceinline__ float word_dot_f32(uint32_t u, const float *hv, float acc) {
+__device__ __forceinline__ float word_dot_f32(uint32_t u, const float *hv, float acc, uint32_t m) {
   if (BITS == 4) {
-    const uint32_t lo = u & 0x0F0F0F0Fu, hi = (u >> 4) & 0x0F0F0F0Fu;
+    const uint32_t lo = u & m, hi = (u >> 4) & m;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       acc = fmaf((float)((lo >> (8 * j)) & 0xFFu), hv[2 * j], acc);
@@ -188,12 +222,64 @@ __device__ __forceinline__ float word_dot_f32(uint32_t u, const float *hv, float
   } else {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const uint32_t m = (u >> (2 * k)) & 0x03030303u;
+      const uint32_t mk = (u >> (2 * k)) & m;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc = fmaf((float)((m >> (8 * j)) & 0xFFu), hv[4 * j + k], acc);
+      for (int j = 0; j < 4; ++j) acc = fmaf((float)((mk >> (8 * j)) & 0xFFu), hv[4 * j + k], acc);
     }
   }
   return acc;
+}
+
+// Lane partial sums of N down rows, one code load per row and lane, against
+// the activations of the lane's DCOLS columns (hb, in LDS):
+// acc += wk (s sum_c q_c h_c + z sum_c h_c) with the row's group scale s and
+// bias z.  One code word's activations are read from LDS at a time.
+template <int BITS, int N, int DWORDS, int DCOLS>
+__device__ __forceinline__ void down_rows(const uint4 (&dq)[N], const uint32_t (&dsb)[N],
+                                          const float *hb, float wk, float (&acc)[N]) {
+  constexpr int CPW = 32 / BITS;  // codes per word
+  uint32_t m = BITS == 4 ? 0x0F0F0F0Fu : 0x03030303u;
+  asm volatile("" : "+s"(m));
+  static_assert(CPW * DWORDS == DCOLS, "the lane's codes fill its words");
+  float q[N];
+#pragma unroll
+  for (int ld = 0; ld < N; ++ld) q[ld] = 0.f;
+  float Hs = 0.f;
+#pragma unroll
+  for (int wd = 0; wd < DWORDS; ++wd) {
+    float hv[CPW];
+#pragma unroll
+    for (int t = 0; t < CPW / 4; ++t) {
+      const float4 v = *reinterpret_cast<const float4 *>(hb + CPW * wd + 4 * t);
+      hv[4 * t] = v.x;
+      hv[4 * t + 1] = v.y;
+      hv[4 * t + 2] = v.z;
+      hv[4 * t + 3] = v.w;
+    }
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) Hs += hv[c];
+#pragma unroll
+    for (int ld = 0; ld < N; ++ld) {
+      const uint4 c4 = dq[ld];
+      const uint32_t u = wd == 0 ? c4.x : wd == 1 ? c4.y : wd == 2 ? c4.z : c4.w;
+      q[ld] = word_dot_f32<BITS>(u, hv, q[ld], m);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int ld = 0; ld < N; ++ld) {
+    const uint32_t sb = dsb[ld];
+    acc[ld] += wk * (bf16f(sb & 0xFFFFu) * q[ld] + bf16f(sb >> 16) * Hs);
+  }
+}
+
+// Sums of the two 32-lane halves of a wave, uniform across the wave.
+__device__ __forceinline__ void half_sums32(float v, float &lo, float &hi) {
+  v = row16_sum(v);
+  lo = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 0)) +
+       __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 16));
+  hi = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 32)) +
+       __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 48));
 }
 
 // Sum over aligned groups of LPR lanes (16, 32 or 64) without LDS traffic.
@@ -214,12 +300,13 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
   __shared__ float s_red[kNT / 64][RR];
   __shared__ uint32_t s_xp[Gm::SEG_X][PAIRS];  // packed x pairs per segment
   __shared__ float2 s_cx[Gm::SEG_X];           // (1024 * sum of pairs, sum of x)
-  __shared__ float s_hb[NSL][I];               // h of every slot, for the down waves
+  __shared__ float s_hb[2][I];                 // h of the shared and the own routed slot
   __shared__ int32_t s_ids[K];
   __shared__ float s_w[K];
-  __shared__ float s_h[NSL][kGuWaves];         // this workgroup's h values
-  __shared__ uint32_t s_cnt[NSL];              // gate/up waves done, per slot
-  __shared__ uint32_t s_hready[NSL];           // s_hb[slot] filled
+  __shared__ uint32_t s_cnt[NSL];              // gate/up rows published, per slot
+  __shared__ uint32_t s_hready[2];             // s_hb[i] filled
+  __shared__ float s_part[K][Gm::D_ROWS];      // routed sums of this workgroup's y rows
+  __shared__ uint32_t s_pready;                // s_part filled
   __shared__ uint32_t s_epoch;
   __shared__ uint32_t s_ready;                 // routing selected
   __shared__ uint32_t s_dissued;               // gate/up waves that issued their routed loads
@@ -239,13 +326,12 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
   // load right there)
   uint32_t epoch_done = (uint32_t)a.E;
   if (tid == kEpochTid) epoch_done = ld_rlx(&a.fc->epoch[grp][0]);
-  if (tid < NSL) {
-    s_cnt[tid] = 0u;
-    s_hready[tid] = 0u;
-  }
+  if (tid < NSL) s_cnt[tid] = 0u;
+  if (tid < 2) s_hready[tid] = 0u;
   if (tid == 0) {
     s_ready = 0u;
     s_dissued = 0u;
+    s_pready = 0u;
   }
 
   // ---- router loads (all threads) -------------------------------------------
@@ -441,16 +527,19 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
       pu = wave_sum64(pu);
       return pg / (1.f + expf(-pg)) * pu;
     };
-    // hand h of (slot, this row) to the exchange through LDS
-    auto hand_over = [&](int slot, float hv) {
-      if (lane == 0) {
-        s_h[slot][wave] = hv;
-        lds_release();
-        __hip_atomic_fetch_add(&s_cnt[slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      }
-    };
     __syncthreads();  // (A) router partials in s_red, x pairs in s_xp, epoch in s_epoch
-    hand_over(K, a.has_shared ? gateup(K) : 0.f);
+    const uint32_t epoch = s_epoch;
+    // publish h of (slot, this wave's row): one tagged copy per reader group,
+    // then count the row for the exchange wave
+    auto publish = [&](int slot, float hv) {
+      if (lane < kGroups)
+        __hip_atomic_store(&a.htag[((size_t)lane * NSL + slot) * I + b * Gm::GU_ROWS + wave],
+                           ((uint64_t)epoch << 32) | (uint64_t)__float_as_uint(hv), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      if (lane == 0)
+        __hip_atomic_fetch_add(&s_cnt[slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
+    if (a.has_shared) publish(K, gateup(K));
     wait_lds(&s_ready, 1u);
     int eid[K];
 #pragma unroll
@@ -465,15 +554,23 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       const bool ok = eid[k] >= 0 && eid[k] < a.E;
-      hand_over(k, ok ? gateup(k) : 0.f);
+      publish(k, ok ? gateup(k) : 0.f);
     }
   } else {
     // =========================== down waves =================================
+    // Output rows: the workgroup owns y rows b D_ROWS .. + D_ROWS; it computes
+    // the shared expert's down rows there and adds the routed slots' sums,
+    // which come from the workgroups that own those rows of each routed slot:
+    // workgroup b computes the down rows O_ROWS (b % OWN_WG) .. + O_ROWS of
+    // routed slot b / OWN_WG only, so it needs the activations of the shared
+    // slot and of that one slot.
     const int dw = wave - kGuWaves;
-    const bool xchg = dw == 0;  // this wave runs routing and the exchange
+    const bool xchg = dw == 0;  // this wave runs routing and the exchanges
     const int seg = lane % Gm::LPR;
     const size_t rbytes = (size_t)I * BITS / 8;
     const int groups = I / kGroup;
+    const int ks = b / Gm::OWN_WG;  // the routed slot whose rows this workgroup computes
+    const int obase = (b % Gm::OWN_WG) * Gm::O_ROWS + dw * Gm::O_ROWS_W;  // first row of this wave
     int rows[Gm::DLD];
 #pragma unroll
     for (int ld = 0; ld < Gm::DLD; ++ld)
@@ -485,48 +582,39 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
 #pragma unroll
       for (int ld = 0; ld < Gm::DLD; ++ld) rres[ld] = a.resid[rows[ld]];
     }
-    uint4 dq[NSL][Gm::DLD];
-    uint32_t dsb[NSL][Gm::DLD];
-    uint32_t o_dq[Gm::DLD], o_dsb[Gm::DLD];
-#pragma unroll
-    for (int ld = 0; ld < Gm::DLD; ++ld) {
-      o_dq[ld] = (uint32_t)(a.off_dq + (int64_t)rows[ld] * rbytes + seg * Gm::DWORDS * 4);
-      o_dsb[ld] = (uint32_t)(a.off_dsb + ((int64_t)rows[ld] * groups + seg * Gm::DCOLS / kGroup) * 4);
-    }
-    auto load_rows = [&](int slot, const uint8_t *bl) {
-      const __amdgpu_buffer_rsrc_t rs = blob_rsrc(bl);
+    auto o_dq = [&](int row) -> uint32_t {
+      return (uint32_t)(a.off_dq + (int64_t)row * rbytes + seg * Gm::DWORDS * 4);
+    };
+    auto o_dsb = [&](int row) -> uint32_t {
+      return (uint32_t)(a.off_dsb + ((int64_t)row * groups + seg * Gm::DCOLS / kGroup) * 4);
+    };
+    auto ld_codes = [&](__amdgpu_buffer_rsrc_t rs, int row) -> uint4 {
+      if (Gm::DWORDS == 4) return bld16(rs, o_dq(row));
+      const uint2 v = bld8(rs, o_dq(row));
+      return make_uint4(v.x, v.y, 0u, 0u);
+    };
+    // shared expert rows (at launch) and the own routed slot's rows
+    uint4 dqs[Gm::DLD], dqr[Gm::RDLD];
+    uint32_t dsbs[Gm::DLD], dsbr[Gm::RDLD];
+    {
+      const __amdgpu_buffer_rsrc_t rs = blob_rsrc(a.has_shared ? a.shared : a.experts);
 #pragma unroll
       for (int ld = 0; ld < Gm::DLD; ++ld) {
-        if (Gm::DWORDS == 4) {
-          dq[slot][ld] = bld16(rs, o_dq[ld]);
-        } else {
-          const uint2 v = bld8(rs, o_dq[ld]);
-          dq[slot][ld] = make_uint4(v.x, v.y, 0u, 0u);
-        }
-        dsb[slot][ld] = bld4(rs, o_dsb[ld]);
+        dqs[ld] = ld_codes(rs, rows[ld]);
+        dsbs[ld] = bld4(rs, o_dsb(rows[ld]));
       }
       __builtin_amdgcn_sched_barrier(0);
-    };
-    load_rows(K, a.has_shared ? a.shared : a.experts);
+    }
     if (RES) norm_x();
     if (routing) router_partials();
     if (tid == kEpochTid) s_epoch = epoch_done + 1u;
     __syncthreads();  // (A)
     const uint32_t epoch = s_epoch;
 
-    // ---- the exchange (wave 4 only) ----
-    // publish this workgroup's h of `slot`: one tagged copy per reader group
-    auto publish = [&](int slot) {
-      if (lane < kGroups * kGuWaves) {
-        const int rep = lane / kGuWaves, row = lane % kGuWaves;
-        const uint64_t v = ((uint64_t)epoch << 32) | (uint64_t)__float_as_uint(s_h[slot][row]);
-        __hip_atomic_store(&a.htag[((size_t)rep * NSL + slot) * I + b * Gm::GU_ROWS + row], v,
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    };
+    // ---- the exchanges (wave 4 only) ----
     // read this group's copy of `slot`; if every entry carries the current
-    // epoch, move the values to LDS for the down waves and return true
-    auto try_consume = [&](int slot) -> bool {
+    // epoch, move the values to s_hb[dst] for the down waves and return true
+    auto try_consume = [&](int slot, int dst) -> bool {
       constexpr int NLD = I / 128;  // 16-byte loads per lane (two entries each)
       uint4 t[NLD];
       const uint32_t base = (uint32_t)(((size_t)grp * NSL + slot) * I * 8);
@@ -538,43 +626,46 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
       if (!__all(ok)) return false;
 #pragma unroll
       for (int i = 0; i < NLD; ++i)
-        *reinterpret_cast<float2 *>(&s_hb[slot][128 * i + 2 * lane]) =
+        *reinterpret_cast<float2 *>(&s_hb[dst][128 * i + 2 * lane]) =
             make_float2(__uint_as_float(t[i].x), __uint_as_float(t[i].z));
       lds_release();
-      if (lane == 0) *lds(&s_hready[slot]) = 1u;
+      if (lane == 0) *lds(&s_hready[dst]) = 1u;
       return true;
     };
-    // publish routed slots as the gate/up waves hand them over, until `slot`
-    // (published by this workgroup before it is polled) is complete everywhere
+    // routed slots this workgroup has published (its four gate/up rows)
     int published = 0;
-    long xspins = 0;
-    auto exchange_until = [&](int slot) {
+    auto count_published = [&]() {
+      while (published < K && *lds(&s_cnt[published]) >= (uint32_t)kGuWaves) ++published;
+    };
+    long xspins = 0;  // one poll budget for the rest of the call
+    auto timed_out = [&]() -> bool {
+      if (++xspins <= kSpinMax) return false;
+      if (lane == 0) atomicOr(&a.ctrl->err, 2u);
+      return true;
+    };
+    // poll `slot` into s_hb[dst] until it is complete everywhere (a routed
+    // slot only after this workgroup published it)
+    auto exchange_until = [&](int slot, int dst) {
       while (true) {
-        if (published < K && *lds(&s_cnt[published]) >= (uint32_t)kGuWaves) {
-          lds_acquire();
-          publish(published);
-          ++published;
-          continue;
-        }
-        if ((slot == K || slot < published) && try_consume(slot)) return;
-        if (++xspins > kSpinMax) {
-          if (lane == 0) atomicOr(&a.ctrl->err, 2u);
-          if (lane == 0) *lds(&s_hready[slot]) = 1u;
+        count_published();
+        if ((slot == K || slot < published) && try_consume(slot, dst)) return;
+        if (timed_out()) {
+          if (lane == 0) *lds(&s_hready[dst]) = 1u;
           return;
         }
         __builtin_amdgcn_s_sleep(1);
       }
     };
-
-    // the shared expert's h is published as soon as the gate/up waves hand
-    // it over, also while the routing poll runs
-    bool shared_out = false;
-    auto publish_shared = [&]() {
-      if (!shared_out && *lds(&s_cnt[K]) >= (uint32_t)kGuWaves) {
-        lds_acquire();
-        if (a.has_shared) publish(K);
-        shared_out = true;
-      }
+    // the routed sums of this workgroup's output rows: lane 16 k + i reads
+    // slot k, row b D_ROWS + i (one reader per word)
+    auto try_parts = [&]() -> bool {
+      const int k = lane / Gm::D_ROWS, i = lane % Gm::D_ROWS;
+      const uint2 t = ld_coh8(a.ptag, (uint32_t)(((size_t)k * H + b * Gm::D_ROWS + i) * 8));
+      if (!__all(t.y == epoch)) return false;
+      s_part[k][i] = __uint_as_float(t.x);
+      lds_release();
+      if (lane == 0) *lds(&s_pready) = 1u;
+      return true;
     };
 
     if (xchg) {
@@ -613,7 +704,6 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
             v[2 * i + 1] = idx + 1 < a.E ? __uint_as_float(t[i].z) : __builtin_nanf("");
           }
           if (__all(ok)) break;
-          publish_shared();
           if (++spins > kSpinMax) {
             if (lane == 0) atomicOr(&a.ctrl->err, 2u);
             break;
@@ -672,90 +762,87 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
       wait_lds(&s_ready, 1u);
     }
 
-    // routed down rows: issued after the gate/up waves issued theirs
+    // own routed rows: issued after the gate/up waves issued theirs; the
+    // exchange wave first reads the shared slot (a poll issued after weight
+    // loads would wait for them)
     wait_lds(&s_dissued, (uint32_t)kGuWaves);
-    int eid[K];
-    float wk[K];
+    const int eo = __builtin_amdgcn_readfirstlane(s_ids[ks]);
+    const bool oko = eo >= 0 && eo < a.E;
+    const float wko = oko ? s_w[ks] : 0.f;
+    if (xchg && a.has_shared) exchange_until(K, 0);
+    {
+      // an invalid id reads expert 0 and contributes 0
+      const __amdgpu_buffer_rsrc_t rs = blob_rsrc(a.experts + (size_t)(oko ? eo : 0) * a.stride);
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-      eid[k] = __builtin_amdgcn_readfirstlane(s_ids[k]);
-      wk[k] = s_w[k];
-      const bool ok = eid[k] >= 0 && eid[k] < a.E;
-      load_rows(k, a.experts + (size_t)(ok ? eid[k] : 0) * a.stride);
+      for (int ld = 0; ld < Gm::RDLD; ++ld) {
+        const int row = obase + ld * Gm::RPL + lane / Gm::LPR;
+        dqr[ld] = ld_codes(rs, row);
+        dsbr[ld] = bld4(rs, o_dsb(row));
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
 
-    if (xchg && !shared_out) {
-      wait_lds(&s_cnt[K], (uint32_t)kGuWaves);
-      publish_shared();
+    // shared rows (lane partial sums, one per row)
+    float accs[Gm::DLD];
+#pragma unroll
+    for (int ld = 0; ld < Gm::DLD; ++ld) accs[ld] = 0.f;
+    if (a.has_shared) {
+      if (!xchg) wait_lds(&s_hready[0], 1u);
+      down_rows<BITS, Gm::DLD, Gm::DWORDS, Gm::DCOLS>(dqs, dsbs, &s_hb[0][seg * Gm::DCOLS], 1.f, accs);
     }
-
-    float acc[Gm::DLD];
+    // own routed rows, then their sums to the workgroups that own the rows:
+    // lane 2 ld + j of the wave stores row obase + 2 ld + j
+    if (xchg) exchange_until(ks, 1);
+    else wait_lds(&s_hready[1], 1u);
+    {
+      float acco[Gm::RDLD];
 #pragma unroll
-    for (int ld = 0; ld < Gm::DLD; ++ld) acc[ld] = 0.f;
-    auto down = [&](int slot, float wkk) {
-      if (xchg) exchange_until(slot);
-      else wait_lds(&s_hready[slot], 1u);
-      // one code word's activations are read from LDS at a time
-      constexpr int CPW = 32 / BITS;
-      float q[Gm::DLD];
+      for (int ld = 0; ld < Gm::RDLD; ++ld) acco[ld] = 0.f;
+      down_rows<BITS, Gm::RDLD, Gm::DWORDS, Gm::DCOLS>(dqr, dsbr, &s_hb[1][seg * Gm::DCOLS], wko, acco);
+      static_assert(Gm::RPL == 2 && Gm::LPR == 32, "two rows per wave-wide load");
+      float pv = 0.f;
 #pragma unroll
-      for (int ld = 0; ld < Gm::DLD; ++ld) q[ld] = 0.f;
-      float Hs = 0.f;
-#pragma unroll
-      for (int wd = 0; wd < Gm::DWORDS; ++wd) {
-        float hv[CPW];
-#pragma unroll
-        for (int t = 0; t < CPW / 4; ++t) {
-          const float4 v = *reinterpret_cast<const float4 *>(&s_hb[slot][seg * Gm::DCOLS + CPW * wd + 4 * t]);
-          hv[4 * t] = v.x;
-          hv[4 * t + 1] = v.y;
-          hv[4 * t + 2] = v.z;
-          hv[4 * t + 3] = v.w;
-        }
-#pragma unroll
-        for (int c = 0; c < CPW; ++c) Hs += hv[c];
-#pragma unroll
-        for (int ld = 0; ld < Gm::DLD; ++ld) {
-          const uint4 c4 = dq[slot][ld];
-          const uint32_t u = wd == 0 ? c4.x : wd == 1 ? c4.y : wd == 2 ? c4.z : c4.w;
-          q[ld] = word_dot_f32<BITS>(u, hv, q[ld]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+      for (int ld = 0; ld < Gm::RDLD; ++ld) {
+        float lo, hi;
+        half_sums32(acco[ld], lo, hi);
+        pv = lane == 2 * ld ? lo : pv;
+        pv = lane == 2 * ld + 1 ? hi : pv;
       }
-#pragma unroll
-      for (int ld = 0; ld < Gm::DLD; ++ld) {
-        const uint32_t sb = dsb[slot][ld];
-        acc[ld] += wkk * (bf16f(sb & 0xFFFFu) * q[ld] + bf16f(sb >> 16) * Hs);
+      if (lane < Gm::O_ROWS_W) {
+        const uint64_t v = ((uint64_t)epoch << 32) | (uint64_t)__float_as_uint(pv);
+        __hip_atomic_store(&a.ptag[(size_t)ks * H + obase + lane], v, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
       }
-    };
-    if (a.has_shared) down(K, 1.f);
-#pragma unroll
-    for (int k = 0; k < K; ++k) down(k, (eid[k] >= 0 && eid[k] < a.E) ? wk[k] : 0.f);
-    // after a timed-out wait, publish what the gate/up waves still hand over
+    }
     if (xchg) {
-      long spins = 0;
-      while (published < K) {
-        if (*lds(&s_cnt[published]) >= (uint32_t)kGuWaves) {
-          lds_acquire();
-          publish(published);
-          ++published;
-        } else if (++spins > kSpinMax) {
+      // the routed sums can only be complete once every workgroup published
+      // every slot, this one included
+      while (true) {
+        count_published();
+        if (published == K && try_parts()) break;
+        if (timed_out()) {
+          if (lane == 0) *lds(&s_pready) = 1u;
           break;
-        } else {
-          __builtin_amdgcn_s_sleep(1);
         }
+        __builtin_amdgcn_s_sleep(1);
       }
+    } else {
+      wait_lds(&s_pready, 1u);
     }
+    // y = shared + routed sums of slots 0 .. K-1, in that order
 #pragma unroll
     for (int ld = 0; ld < Gm::DLD; ++ld) {
-      const float v = lane_group_sum<Gm::LPR>(acc[ld], lane);
+      float v = lane_group_sum<Gm::LPR>(accs[ld], lane);
+      const int i = rows[ld] - b * Gm::D_ROWS;
+#pragma unroll
+      for (int k = 0; k < K; ++k) v += s_part[k][i];
       if (seg == 0) {
         if (!RES || a.y) a.y[rows[ld]] = v;
         if (RES) a.resid[rows[ld]] = rres[ld] + v;
       }
     }
-    // every workgroup has published every slot, so all have passed barrier
-    // (A), where they read the epoch
+    // this workgroup has read activations of every workgroup, published after
+    // barrier (A), where they read the epoch
     if (b == 0 && xchg && lane < kGroups)
       __hip_atomic_store(&a.fc->epoch[lane][0], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -802,6 +889,7 @@ int launch_layer_fused(const moe_dims &d, const moe_layer &L, const uint16_t *x,
   a.fc = reinterpret_cast<FCtrl *>(base + W.fctrl);
   a.tags = reinterpret_cast<uint64_t *>(base + W.logits_tag);
   a.htag = reinterpret_cast<uint64_t *>(base + W.h_tag);
+  a.ptag = reinterpret_cast<uint64_t *>(base + W.p_tag);
   a.E = d.n_experts;
   a.has_shared = d.has_shared;
   a.off_gq = (int64_t)B.off[MOE_SEC_GATE_Q];

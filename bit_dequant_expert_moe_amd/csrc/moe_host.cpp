@@ -39,6 +39,7 @@ WsLayout ws_layout(const moe_dims &d, int T) {
   W.fctrl = kFCtrlOff;
   W.logits_tag = kTagOff;
   W.h_tag = kHTagOff;
+  W.p_tag = kPTagOff;
   size_t o = align_up(kHeaderBytes, kAlign);
   W.logits = o;
   o = align_up(o + (size_t)route_splits(d, T) * T * d.n_experts * 4, kAlign);

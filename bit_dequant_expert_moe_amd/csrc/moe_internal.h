@@ -30,6 +30,8 @@ BlobLayout blob_layout(const moe_dims &d);
 //   fctrl      : FCtrl (epoch of the fused single-token kernel)
 //   logits_tag : uint64 [kGroups][kMaxE]  (fp32 logit bits | epoch << 32)
 //   h_tag      : uint64 [kGroups][5][1024] (fp32 h bits | epoch << 32)
+//   p_tag      : uint64 [4][4096]  routed down sums per slot and output row
+//                (fp32 bits | epoch << 32)
 // then, not initialised:
 //   logits     : fp32 [S][T][E] partial router sums (S <= kMaxRouteSplits)
 //   ids        : int32 [T][K]
@@ -65,6 +67,7 @@ struct FCtrl {
 static_assert(sizeof(FCtrl) == 1024, "epoch copies are 128 bytes apart");
 constexpr int kFusedI = 1024;     // intermediate size the fused kernel covers
 constexpr int kFusedSlots = 5;    // top-4 + shared
+constexpr int kFusedH = 4096;     // hidden size the fused kernel covers
 
 constexpr size_t kCtrlOff = 0;
 constexpr size_t kFCtrlOff = 256;
@@ -72,10 +75,12 @@ constexpr size_t kFCtrlOff = 256;
 constexpr size_t kTagOff = kFCtrlOff + sizeof(FCtrl);
 // tagged activations: uint64 [kGroups][kFusedSlots][kFusedI]
 constexpr size_t kHTagOff = kTagOff + (size_t)kGroups * kMaxE * 8;
-constexpr size_t kHeaderBytes = kHTagOff + (size_t)kGroups * kFusedSlots * kFusedI * 8;
+// tagged routed down sums: uint64 [kFusedSlots - 1][kFusedH]
+constexpr size_t kPTagOff = kHTagOff + (size_t)kGroups * kFusedSlots * kFusedI * 8;
+constexpr size_t kHeaderBytes = kPTagOff + (size_t)(kFusedSlots - 1) * kFusedH * 8;
 
 struct WsLayout {
-  size_t ctrl, fctrl, logits_tag, h_tag, logits, ids, w, h, bk, xb, xs, hb, hs, yd, xn, yr,
+  size_t ctrl, fctrl, logits_tag, h_tag, p_tag, logits, ids, w, h, bk, xb, xs, hb, hs, yd, xn, yr,
       total;
 };
 WsLayout ws_layout(const moe_dims &d, int T);
