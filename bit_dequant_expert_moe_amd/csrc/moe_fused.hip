@@ -42,8 +42,10 @@
 // every workgroup reading all five slots (one ~1 us round trip per slot at
 // the end of the layer), this layout reads two slots and one small block of
 // sums, 1.2 us per layer less.  Weight bytes are requested as soon as
-// their addresses are known: router, shared expert and x at launch, routed
-// experts right after the top-K, gate/up rows first (the activation exchange
+// their addresses are known: router and x at launch, the shared expert once
+// the router products are formed (issued at launch, its 7 MB delayed the
+// router's 4 MB by ~0.5 us per layer), routed experts right after the top-K,
+// gate/up rows first (the activation exchange
 // waits on them; the down rows are needed only after it, ~1 us per layer
 // faster than the reverse order).  Waits between waves of a workgroup read
 // LDS only (a global or flat load in a spin loop would wait for every weight
@@ -458,14 +460,14 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
       // counter completes in order)
       __builtin_amdgcn_sched_barrier(0);
     };
-    // without a shared expert slot K reads expert 0 and is never used
-    load_rows(K, a.has_shared ? a.shared : a.experts);
     if (RES) {
       norm_x();
 #pragma unroll
       for (int t = 0; t < Gm::XLD; ++t) xr[t] = s_xn[(xs % Gm::SEG_X) * (COLS / 8) + t];
     }
     if (routing) router_partials();
+    // without a shared expert slot K reads expert 0 and is never used
+    load_rows(K, a.has_shared ? a.shared : a.experts);
     // x pairs and per-segment corrections, one code word at a time, to LDS
     if (xs < Gm::SEG_X) {
       float C = 0.f, X = 0.f;
@@ -596,6 +598,8 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
     // shared expert rows (at launch) and the own routed slot's rows
     uint4 dqs[Gm::DLD], dqr[Gm::RDLD];
     uint32_t dsbs[Gm::DLD], dsbr[Gm::RDLD];
+    if (RES) norm_x();
+    if (routing) router_partials();
     {
       const __amdgpu_buffer_rsrc_t rs = blob_rsrc(a.has_shared ? a.shared : a.experts);
 #pragma unroll
@@ -605,8 +609,6 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (RES) norm_x();
-    if (routing) router_partials();
     if (tid == kEpochTid) s_epoch = epoch_done + 1u;
     __syncthreads();  // (A)
     const uint32_t epoch = s_epoch;
