@@ -28,9 +28,9 @@
 //     four slots' sums of its rows (one reader per word) and forms
 //     y = shared + slot 0 + .. + slot K-1 in that order.
 // Every word that all workgroups read is written once per reader group
-// (blockIdx % 8, one per XCD), so each cache line has ~32 coherent readers:
-// a line read coherently by all 256 CUs at once serialises at its memory
-// channel for several microseconds.  Exchanged words travel through
+// (blockIdx % 8, one per XCD), so a cache line has at most 32 coherent
+// readers: a line read coherently by all 256 CUs at once serialises at its
+// memory channel for several microseconds.  Exchanged words travel through
 // agent-scope relaxed atomics (coherent sc1 loads and stores); no cache
 // writeback or invalidate is issued (issued by every CU at once, those cost
 // tens of microseconds).
@@ -41,11 +41,12 @@
 // also selects the top-K and runs the reads of the exchanges.  Compared with
 // every workgroup reading all five slots (one ~1 us round trip per slot at
 // the end of the layer), this layout reads two slots and one small block of
-// sums, 1.2 us per layer less.  Weight bytes are requested as soon as
-// their addresses are known: router and x at launch, the shared expert once
-// the router products are formed (issued at launch, its 7 MB delayed the
-// router's 4 MB by ~0.5 us per layer), routed experts right after the top-K,
-// gate/up rows first (the activation exchange
+// sums; with the publishing below, 1.2 us per layer less.
+//
+// Weight bytes are requested as soon as their addresses are known: router and
+// x at launch, the shared expert once the router products are formed (issued
+// at launch, its 7 MB delayed the router's 4 MB by ~0.5 us per layer), routed
+// experts right after the top-K, gate/up rows first (the activation exchange
 // waits on them; the down rows are needed only after it, ~1 us per layer
 // faster than the reverse order).  Waits between waves of a workgroup read
 // LDS only (a global or flat load in a spin loop would wait for every weight

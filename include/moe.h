@@ -83,11 +83,11 @@
  * - A call of 1 to 3 tokens on a GPU with 256 compute units, hidden 4096,
  *   intermediate 1024 and top-4 runs as one launch per token of 256
  *   workgroups, one per compute unit, that exchange data while running: it
- *   needs the whole GPU.  Do not run it concurrently with other kernels (such as a second
- *   such call on another stream): workgroups that cannot become resident
- *   make the others' waits time out, which sets bit 1 of the sticky error
- *   flags and leaves the outputs invalid (nothing hangs).  Calls on one
- *   stream, or captured in one graph, are always safe.
+ *   needs the whole GPU.  Do not run it concurrently with other kernels
+ *   (such as a second such call on another stream): workgroups that cannot
+ *   become resident make the others' waits time out, which sets bit 1 of the
+ *   sticky error flags and leaves the outputs invalid (nothing hangs).  Calls
+ *   on one stream, or captured in one graph, are always safe.
  */
 #ifndef MOE_H_
 #define MOE_H_
