@@ -14,7 +14,11 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Wall", "-Wno-unused-function",
          # no packed-FP32 instructions in device code
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # matrix-core results in ordinary VGPRs: with accumulation registers
+         # the grouped GEMM needs 288 registers per lane (one wave per SIMD)
+         # and reads every result back with v_accvgpr_read
+         "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def build(force: bool = True, extra=None) -> str:
