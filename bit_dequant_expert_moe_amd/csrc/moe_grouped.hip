@@ -456,21 +456,37 @@ __global__ void __launch_bounds__(256) k_grouped(GroupArgs a) {
             P[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[u], P[m], 0, 0, 0);
         }
       }
-      // element v of this lane: row 4 q + v of the wave's 16, B column col
-      const float X = XS[col * kGC + gi];
+      // element v of this lane: row 4 q + v of the wave's 16, B column col;
+      // the scale term here, the bias term once per chunk below
 #pragma unroll
       for (int m = 0; m < G::NMAT; ++m)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           if (DOWN) {
             const uint32_t sb = SB[(wave * 16 + 4 * q + v) * kGC + gi];
-            acc[m][v] += bf16f(sb & 0xFFFFu) * (P[m][v] - 128.f * X) + bf16f(sb >> 16) * X;
+            acc[m][v] = fmaf(bf16f(sb & 0xFFFFu), P[m][v], acc[m][v]);
           } else {
             const float2 sz =
                 reinterpret_cast<const float2 *>(SB)[(m * kRT + wave * 16 + 4 * q + v) * kGC + gi];
-            acc[m][v] = fmaf(sz.x, P[m][v], fmaf(sz.y, X, acc[m][v]));
+            acc[m][v] = fmaf(sz.x, P[m][v], acc[m][v]);
           }
         }
+    }
+    // bias term of the chunk's kGC groups, sum_g (z - 128 s)[row][g] X[g][col],
+    // as one fp32 16x16x4 product: lane l supplies row l % 16, group l / 16 of
+    // the wave's rows and group l / 16, column l % 16 of the group sums
+    static_assert(kGC == 4, "one 16x16x4 product per chunk");
+    const float xg = XS[col * kGC + q];
+#pragma unroll
+    for (int m = 0; m < G::NMAT; ++m) {
+      float zp;
+      if (DOWN) {
+        const uint32_t sb = SB[(wave * 16 + col) * kGC + q];
+        zp = fmaf(-128.f, bf16f(sb & 0xFFFFu), bf16f(sb >> 16));
+      } else {
+        zp = reinterpret_cast<const float2 *>(SB)[(m * kRT + wave * 16 + col) * kGC + q].y;
+      }
+      acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(zp, xg, acc[m], 0, 0, 0);
     }
   };
 
