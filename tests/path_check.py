@@ -1,9 +1,10 @@
 """Run by tests/test_gpu_paths.py in a child process whose environment
 selects a dispatch path (MOE_DISABLE_FUSED=1: the three-kernel single-token
-path; MOE_DISABLE_GROUPED=1: the per-token kernels for more tokens than
-the single-token kernel takes one launch each).  The
-library reads these switches once per process, hence the child.  Prints one
-JSON line with the worst relative output error against the oracle."""
+path, and the grouped path from two tokens on; MOE_DISABLE_GROUPED=1: the
+per-token kernels for more tokens than the single-token kernel takes one
+launch each).  The library reads these switches once per process, hence the
+child.  Prints one JSON line with the worst relative output error against the
+oracle."""
 import json
 import os
 import sys
@@ -21,7 +22,7 @@ def main():
     worst, cases = 0.0, 0
     for bits in (4, 2):
         L = gu.DeviceLayer(4096, 1024, 32, 4, bits=bits, seed=3000 + bits)
-        for T in (1, 5):
+        for T in (1, 2, 5):
             x = synth.tokens(3000 + bits, T, T, 4096)
             out = L.decode(x, want_logits=True)
             assert out["err"] == 0

@@ -218,6 +218,19 @@ def test_batched_equals_single_and_deterministic(full):
 
 # ---- single-token fused path: repeated calls, graphs, error word ----------------
 
+@pytest.mark.parametrize("T", [2, 3])
+def test_small_batches_run_per_token(full, T):
+    # calls of up to three tokens run the single-token kernel once per token:
+    # bitwise equal to T one-token calls, and within tolerance of the oracle
+    x = synth.tokens(1004, T, T, 4096)
+    ob = _layer_check(full, x, "full T=%d" % T)
+    for t in range(T):
+        o1 = full.decode(x[t:t + 1])
+        np.testing.assert_array_equal(o1["ids"][0], ob["ids"][t])
+        np.testing.assert_array_equal(o1["w"][0], ob["w"][t])
+        np.testing.assert_array_equal(o1["y"][0], ob["y"][t])
+
+
 def test_fused_consecutive_tokens_same_workspace(full):
     # 12 tokens decoded one call at a time on one workspace (the single-token
     # kernel's epoch advances per call) against the oracle, and against the

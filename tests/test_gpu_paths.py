@@ -1,7 +1,8 @@
 """The dispatch paths that the default process never takes for the main
 shape (hidden 4096, intermediate 1024, top-4): the three-kernel single-token
-path and the per-token kernels for several tokens.  Each runs in a child
-process (tests/path_check.py) with its switch set, against the oracle."""
+path, the grouped path for two tokens and the per-token kernels for several
+tokens.  Each runs in a child process (tests/path_check.py) with its switch
+set, against the oracle."""
 import json
 import os
 import subprocess
@@ -30,5 +31,5 @@ def test_path_against_oracle(switch):
     assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
     res = json.loads(r.stdout.strip().splitlines()[-1])
     print("  ", res, flush=True)
-    assert res["cases"] == 6
+    assert res["cases"] == 8
     assert res["worst_rel_err"] <= gu.Y_TOL
