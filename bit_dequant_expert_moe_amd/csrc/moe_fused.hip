@@ -596,7 +596,8 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
       const uint2 v = bld8(rs, o_dq(row));
       return make_uint4(v.x, v.y, 0u, 0u);
     };
-    // shared expert rows (at launch) and the own routed slot's rows
+    // shared expert rows (issued once the router products are formed) and the
+    // own routed slot's rows
     uint4 dqs[Gm::DLD], dqr[Gm::RDLD];
     uint32_t dsbs[Gm::DLD], dsbr[Gm::RDLD];
     if (RES) norm_x();

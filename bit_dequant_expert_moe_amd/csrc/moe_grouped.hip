@@ -25,9 +25,11 @@
 // The codes enter v_mfma_f32_16x16x32_bf16 as bf16 values 128 + q (exact: one
 // v_and_or_b32 puts two 4-bit fields into the mantissas of a pair of bf16
 // 128.0); the product with the bf16 activations is exact and the MFMA sums in
-// fp32.  Per group the partial result P gives sum q b = P - 128 * sum b, which
-// is scaled and biased in fp32.  x is bf16 already; h (fp32) enters as
-// bf16 hi + bf16 lo, two MFMAs, ~16 significant bits.
+// fp32.  Per group the partial result P gives sum q b = P - 128 * sum b, so
+// the group adds s P + (z - 128 s) sum b: the scale term in fp32 per group,
+// the bias terms of a staged chunk's four groups as one fp32 16x16x4 MFMA.
+// x is bf16 already; h (fp32) enters as bf16 hi + bf16 lo, two MFMAs, ~16
+// significant bits.
 //
 // The field order inside a code word makes the A operand of a lane hold the
 // columns (c0, c4, c1, c5, c2, c6, c3, c7) of its 8-column slice; the staged
