@@ -160,11 +160,13 @@ def test_layer_decode_2bit_tiny():
     # kernel's four router rows per workgroup, with rows past E
     (4096, 1024, 100, 4, 4, 1), (4096, 1024, 1000, 4, 4, 1), (4096, 1024, 1000, 4, 2, 0)])
 def test_layer_decode_shapes(cfg):
-    # one token (the single-token kernels) and three (the grouped path)
+    # one and three tokens (the single-token kernels, once per token, where
+    # they cover the shape; else the three-kernel and the grouped path) and
+    # four (the grouped path)
     H, I, E, K, bits, sh = cfg
     _say("shape", cfg)
     L = gu.DeviceLayer(H, I, E, K, bits=bits, has_shared=sh, seed=300 + H + I + E)
-    for T in (1, 3):
+    for T in (1, 3, 4):
         x = synth.tokens(L.seed, T, T, H)
         _layer_check(L, x, "shape %s T=%d" % (cfg, T))
 
