@@ -695,6 +695,11 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
         static_assert(256 * RR <= kMaxE, "tag copy holds 256 RR entries");
         float v[NV];
         long spins = 0;
+        // the first poll waits ~0.5 us: one issued before the last
+        // workgroups' logits can be visible returns incomplete and costs a
+        // whole round trip (~1.5 us under the shared-expert stream); waits
+        // of 0.3 and 0.75 us measured between none and this one
+        __builtin_amdgcn_s_sleep(19);
         while (true) {
           uint4 t[NV / 2];
 #pragma unroll
