@@ -207,27 +207,46 @@ struct FusedArgs {
   int64_t off_gq, off_uq, off_dq, off_gsb, off_usb, off_dsb;
 };
 
-// sum_c q_c h_c over the codes of one 32-bit word (8 at 4 bits, 16 at 2 bits)
-// of a down row, fp32; hv holds the word's activations.  m is the per-byte
-// code mask (0x0F0F0F0F or 0x03030303) in a register the compiler cannot see
-// through: with a literal it merges the masks into one bit-field extract per
-// code, while from a masked word every byte converts in one instruction
-// (v_cvt_f32_ubyte0..3).
+// Value of code 1 read as an fp8 bit pattern.  A masked code byte (0..15)
+// is an fp8 subnormal or the smallest normals, so its fp8 value is exactly
+// the code times this power of two (2^-9 for e4m3, 2^-10 for its FNUZ form).
+__device__ __forceinline__ float fp8_code_unit() {
+  return __builtin_amdgcn_cvt_pk_f32_fp8(1, false)[0];
+}
+
+// u sum_c q_c h_c over the codes of one 32-bit word (8 at 4 bits, 16 at 2
+// bits) of a down row, fp32, with u = fp8_code_unit(); hv holds the word's
+// activations.  m is the per-byte code mask (0x0F0F0F0F or 0x03030303) in a
+// register the compiler cannot see through.  Each masked word converts two
+// codes per instruction (v_cvt_pk_f32_fp8 on its low and high half); the
+// products are summed in code order, and since u is a power of two the sum
+// is exactly u times the one formed from integer codes.
 template <int BITS>
 __device__ __forceinline__ float word_dot_f32(uint32_t u, const float *hv, float acc, uint32_t m) {
   if (BITS == 4) {
     const uint32_t lo = u & m, hi = (u >> 4) & m;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc = fmaf((float)((lo >> (8 * j)) & 0xFFu), hv[2 * j], acc);
-      acc = fmaf((float)((hi >> (8 * j)) & 0xFFu), hv[2 * j + 1], acc);
-    }
+    const auto l0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
+    const auto l1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
+    const auto h0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
+    const auto h1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
+    acc = fmaf(l0[0], hv[0], acc);
+    acc = fmaf(h0[0], hv[1], acc);
+    acc = fmaf(l0[1], hv[2], acc);
+    acc = fmaf(h0[1], hv[3], acc);
+    acc = fmaf(l1[0], hv[4], acc);
+    acc = fmaf(h1[0], hv[5], acc);
+    acc = fmaf(l1[1], hv[6], acc);
+    acc = fmaf(h1[1], hv[7], acc);
   } else {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const uint32_t mk = (u >> (2 * k)) & m;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc = fmaf((float)((mk >> (8 * j)) & 0xFFu), hv[4 * j + k], acc);
+      const auto c0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)mk, false);
+      const auto c1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)mk, true);
+      acc = fmaf(c0[0], hv[k], acc);
+      acc = fmaf(c0[1], hv[4 + k], acc);
+      acc = fmaf(c1[0], hv[8 + k], acc);
+      acc = fmaf(c1[1], hv[12 + k], acc);
     }
   }
   return acc;
@@ -269,10 +288,12 @@ __device__ __forceinline__ void down_rows(const uint4 (&dq)[N], const uint32_t (
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+  // q holds u times the integer-code sums; 1/u is exact
+  const float iu = 1.f / fp8_code_unit();
 #pragma unroll
   for (int ld = 0; ld < N; ++ld) {
     const uint32_t sb = dsb[ld];
-    acc[ld] += wk * (bf16f(sb & 0xFFFFu) * q[ld] + bf16f(sb >> 16) * Hs);
+    acc[ld] += wk * (bf16f(sb & 0xFFFFu) * iu * q[ld] + bf16f(sb >> 16) * Hs);
   }
 }
 
