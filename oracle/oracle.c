@@ -346,15 +346,30 @@ void or_expert_forward(const or_dims *d, const uint8_t *const *blobs, const uint
  *     x_c = r_c / sqrt(mean_c r_c^2 + 1e-6),
  * rounded to bf16 (the MoE input format). */
 
-/* Round a double to the nearest bf16 (ties to even), via float: the double
- * -> float conversion rounds to nearest, then the float's upper half is
- * rounded to nearest even. */
+/* Round a double to the nearest bf16 (ties to even), in one step from the
+ * double.  bf16 keeps the sign, the 8 exponent bits of fp32 and 8 significant
+ * bits: a value with binary exponent E (2^E <= |v| < 2^(E+1)) is a multiple
+ * of 2^(E-7) when normal, and every subnormal is a multiple of 2^-133.  So v
+ * is scaled to units of that quantum (exact: a power of two), rounded to the
+ * nearest integer with ties to even (rint in the default rounding mode), and
+ * scaled back; the result is a bf16 value, so its conversion to float is
+ * exact and its upper 16 bits are the pattern.  Magnitudes that round to
+ * 2^128 or beyond give infinity. */
 uint16_t or_f64_to_bf16(double v) {
-  float f = (float)v;
+  double r = 0.0;
+  if (v != 0.0) {
+    int e;
+    frexp(v, &e); /* |v| = m 2^e, 0.5 <= m < 1, so the exponent E is e - 1 */
+    int qexp = (e - 1) - 7;
+    if (qexp < -133) qexp = -133;
+    r = ldexp(rint(ldexp(v, -qexp)), qexp);
+  }
+  uint16_t sign = signbit(v) ? 0x8000u : 0u;
+  if (fabs(r) >= 0x1p128) return (uint16_t)(sign | 0x7F80u);
+  float f = (float)r;
   uint32_t u;
   memcpy(&u, &f, 4);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return (uint16_t)((u >> 16) | sign);
 }
 
 /* x = bf16(r / sqrt(mean(r^2) + eps)) for one token of n values. */

@@ -104,24 +104,38 @@ def test_code_bit_order_hand_word():
 
 
 def test_scale_bias_per_group_and_row():
-    d = SMALL
+    # H != I so that a row or group index computed from the wrong dimension
+    # lands on another word; every (s, z) pair is distinct, so reading the word
+    # of another row or group (c / 128 in place of c / 64, r / 2 in place of r)
+    # gives a different value somewhere
+    d = oracle.Dims(H=512, I=256, E=4, K=2, bits=4)
     rng = np.random.default_rng(3)
-    # distinct exact-bf16 scales/biases per (row, group)
+    drawn = {}
+
     def s_of(rows, groups):
-        s = (1 + rng.integers(0, 127, (rows, groups))) * 2.0 ** -10
-        z = (rng.integers(-127, 128, (rows, groups))) * 2.0 ** -12
-        return s.astype(np.float32), z.astype(np.float32)
+        # exact bf16 values: scales k 2^-10 (k = 1..127), biases j 2^-12
+        n = rows * groups
+        s = (1 + rng.permutation(np.arange(n) % 127)) * 2.0 ** -10
+        z = (rng.permutation(np.arange(n) % 255) - 127) * 2.0 ** -12
+        s = s.reshape(rows, groups).astype(np.float32)
+        z = z.reshape(rows, groups).astype(np.float32)
+        drawn[len(drawn)] = (s, z)
+        return s, z
     blob, qs = _random_codes_blob(d, rng, s_of)
+    assert len(drawn) == 3  # gate, up, down, in that order
     for which, rows, cols in [(0, d.I, d.H), (1, d.I, d.H), (2, d.H, d.I)]:
-        W = oracle.dequant_matrix(d, blob, which)
-        for (r, c) in [(0, 0), (0, 63), (0, 64), (rows - 1, cols - 1), (17, 130)]:
-            s, z = oracle.scale_bias(d, blob, which, r, c)
-            assert W[r, c] == s * qs[which][r, c] + z
-        # group boundaries: columns 63 and 64 use different (s,z) words
-        s63 = oracle.scale_bias(d, blob, which, 5, 63)
-        s64 = oracle.scale_bias(d, blob, which, 5, 64)
-        s0 = oracle.scale_bias(d, blob, which, 5, 0)
-        assert s63 == s0
+        s, z = drawn[which]
+        assert s.shape == (rows, cols // 64)
+        # the (s, z) pair of every (row, group), through the oracle's accessor
+        for r in range(rows):
+            for g in range(cols // 64):
+                c = 64 * g + (r * 7 + g * 13) % 64  # any column of the group
+                assert oracle.scale_bias(d, blob, which, r, c) == (float(s[r, g]), float(z[r, g]))
+        # and every element of the dequantised matrix against s q + z built
+        # here from the drawn arrays (exact in float64)
+        want = (np.repeat(s.astype(np.float64), 64, axis=1) * qs[which]
+                + np.repeat(z.astype(np.float64), 64, axis=1))
+        np.testing.assert_array_equal(oracle.dequant_matrix(d, blob, which), want)
 
 
 def test_dequant_closed_forms():
@@ -400,6 +414,44 @@ def test_f64_to_bf16_rounds_to_nearest_even():
     assert oracle.f64_to_bf16(1.0 + 3 * 2.0 ** -8) == 0x3F82    # tie -> even (1 + 2^-6)
     assert oracle.f64_to_bf16(1.0 + 2.0 ** -8 + 2.0 ** -20) == 0x3F81  # above the tie
     assert oracle.f64_to_bf16(-2.5) == 0xC020
+    # just off a tie by less than half an fp32 step: a rounding through fp32
+    # would first land on the tie and then go to the even neighbour
+    assert oracle.f64_to_bf16(1.0 + 2.0 ** -8 + 2.0 ** -30) == 0x3F81   # above -> up
+    assert oracle.f64_to_bf16(1.0 + 3 * 2.0 ** -8 - 2.0 ** -30) == 0x3F81  # below -> down
+    assert oracle.f64_to_bf16(-(1.0 + 2.0 ** -8 + 2.0 ** -30)) == 0xBF81
+    # subnormals (spacing 2^-133) and the top of the range
+    assert oracle.f64_to_bf16(2.0 ** -133) == 0x0001
+    assert oracle.f64_to_bf16(2.0 ** -134) == 0x0000              # tie -> even (0)
+    assert oracle.f64_to_bf16(1.5 * 2.0 ** -134) == 0x0001
+    assert oracle.f64_to_bf16(3 * 2.0 ** -134) == 0x0002          # tie -> even
+    assert oracle.f64_to_bf16(2.0 ** -126) == 0x0080               # smallest normal
+    assert oracle.f64_to_bf16(float.fromhex("0x1.fep127")) == 0x7F7F   # largest finite
+    assert oracle.f64_to_bf16(float.fromhex("0x1.ffp127")) == 0x7F80   # tie -> even (inf)
+    assert oracle.f64_to_bf16(0.0) == 0x0000
+    assert oracle.f64_to_bf16(-0.0) == 0x8000
+
+
+def test_f64_to_bf16_is_the_nearest_value_by_brute_force():
+    # against the definition: among all finite bf16 patterns of the value's
+    # sign, the one nearest to v (exact rational distances), ties to an even
+    # last bit
+    from fractions import Fraction
+    pos = np.arange(0x0000, 0x7F80, dtype=np.uint32)
+    vals = [Fraction(float(v)) for v in (pos << 16).view(np.float32)]
+    rng = np.random.default_rng(17)
+    cases = list(rng.uniform(0.5, 4.0, 300)) + list(2.0 ** rng.uniform(-135, 127, 300))
+    # values exactly on and next to ties
+    for b in rng.integers(1, 0x7F7F, 200):
+        lo, hi = vals[b], vals[b + 1]
+        mid = (lo + hi) / 2
+        cases += [float(mid), float(mid) * (1 + 2.0 ** -40), float(mid) * (1 - 2.0 ** -40)]
+    import bisect
+    for v in cases:
+        fv = Fraction(v)
+        i = bisect.bisect_left(vals, fv)
+        cand = [j for j in (i - 1, i) if 0 <= j < len(vals)]
+        best = min(cand, key=lambda j: (abs(vals[j] - fv), j & 1))
+        assert oracle.f64_to_bf16(v) == best, (v, hex(best))
 
 
 def test_rmsnorm_hand_worked():
