@@ -37,15 +37,17 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=128, help="timed decode tokens")
     ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--workload", default="stack60", choices=["stack60", "stack60_chain", "stack60_2bit", "batch64", "prefill4096",
-                             "stack8_tier"])
+    ap.add_argument("--workload", default="stack60", choices=["stack60", "stack60_chain", "stack60_2bit", "layer",
+                                                         "batch64", "prefill4096", "stack8_tier"])
     ap.add_argument("--layers", type=int, default=None, help="override layer count (testing)")
     ap.add_argument("--tokens", type=int, default=None, help="override distinct tokens")
-    ap.add_argument("--cpu-layers", type=int, default=60,
-                    help="layers of the CPU oracle sample (one token)")
+    ap.add_argument("--cpu-layers", type=int, default=20,
+                    help="layers of the one-core CPU oracle sample (token 0)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--check-layers", type=int, default=3,
-                    help="layers of token 0 checked against the oracle")
+    ap.add_argument("--check-layers", type=int, default=60,
+                    help="layers of token 0 checked against the oracle (the parity gate)")
+    ap.add_argument("--reps", type=int, default=5,
+                    help="repetitions of the timed region for the spread")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB megabytes (calibrates the HBM "
                          "byte counters of the profiler) and exit")
@@ -111,6 +113,8 @@ def main():
     from synth.workloads import WORKLOADS
 
     wl = WORKLOADS[args.workload]
+    if wl.name == "layer":
+        return bench_layer(args, wl)
     if wl.T > 1:
         return bench_batch(args, wl)
     if wl.tier_slots:
@@ -222,6 +226,19 @@ def main():
                      for t in range(1, ntok) for l in range(nl)]) if ntok > 1 else float("nan")
     log("expert reuse between consecutive tokens: %.3f" % reuse)
 
+    # ---- spread over repetitions of the timed region -------------------------
+    rep_tok_s = []
+    for _ in range(args.reps):
+        e0.record()
+        for i in range(args.steps):
+            graphs[i % ntok].replay()
+        e1.record()
+        torch.cuda.synchronize()
+        rep_tok_s.append(1000.0 * args.steps / e0.elapsed_time(e1))
+    reps = spread(rep_tok_s)
+    log("tok/s over %d repetitions: median %.1f, p10 %.1f, p90 %.1f" % (
+        args.reps, reps["median"], reps["p10"], reps["p90"]))
+
     # ---- per-launch duration of the layer call ---------------------------------
     # On the single-token path one moe_layer_decode is one kernel (k_layer1) and
     # a token graph is nl of them back to back, so the timed region above (HIP
@@ -249,85 +266,31 @@ def main():
     if err:
         log("device error flags: %d" % err)
 
-    # ---- spot parity against the oracle (token 0, first layers) --------------
-    check = None
-    if args.check_layers > 0:
-        try:
-            import oracle
-            od = oracle.Dims(H=wl.H, I=wl.I, E=wl.E, K=wl.K, bits=wl.bits,
-                             has_shared=wl.has_shared)
-            graphs[0].replay()
-            torch.cuda.synchronize()
-            worst = 0.0
-            # on the chain: the x each layer formed, against the oracle's norm
-            # of the residual rebuilt on the host from r0 and the layers' y
-            # (r += y in fp32, as the kernel does)
-            xk = x[0].cpu().numpy().view(np.uint16) if chain else x_h[0]
-            rr = r0_h[0].copy() if chain else None
-            norm_mis = 0
-            for l in range(min(args.check_layers, nl)):
-                if chain:
-                    norm_mis += int(np.count_nonzero(xk[l] != oracle.rmsnorm_bf16(rr)))
-                    rr = (rr + y[0, l].cpu().numpy()).astype(np.float32)
-                idl = ids[0, l].cpu().numpy()
-                lg = oracle.router_logits(od, routers_h[l], xk[l])
-                sel = lg[idl]
-                wo = np.exp(sel - sel.max())
-                wo /= wo.sum()
-                blobs = {int(e): experts[l][int(e) * stride:int(e) * stride + blob].cpu().numpy()
-                         for e in idl}
-                yo = oracle.expert_forward(od, blobs, shared[l].cpu().numpy(), xk[l][None],
-                                           idl[None], wo[None])[0]
-                yg = y[0, l].cpu().numpy()
-                e_l = float(np.max(np.abs(yg - yo)) / np.max(np.abs(yo)))
-                if e_l > 2e-3:
-                    log("  layer %d: ids %s, max|y| %.3e (oracle %.3e), rel err %.2e" % (
-                        l, idl.tolist(), float(np.max(np.abs(yg))), float(np.max(np.abs(yo))),
-                        e_l))
-                worst = max(worst, e_l)
-            check = worst
-            log("oracle spot check (%d layers): max|dy|/max|y| = %.2e" % (args.check_layers, worst))
-            if chain:
-                log("  normalised x: %d bf16 elements differ from the oracle's norm (one step)"
-                    % norm_mis)
-        except Exception as ex:  # the check is informational; the tests are the gate
-            log("oracle spot check skipped: %r" % (ex,))
+    # ---- measured streaming-read rate at the layer's and the token's size -----
+    stream = stream_read_rates(torch, moe, experts, launch_bytes, nl * launch_bytes, sp)
+    stream["layer_call_frac_of_layer_size_rate"] = achieved / stream["layer_size_back_to_back_GBps"]
+    stream["token_frac_of_token_size_rate"] = (
+        (expert_bytes_tok + router_bytes_tok) * tok_s / 1e9 / stream["token_size_single_launch_GBps"])
+    log("stream read: %.0f GB/s per launch of %d B back to back (%.0f GB/s isolated), "
+        "%.0f GB/s for one launch of %d B" % (
+            stream["layer_size_back_to_back_GBps"], launch_bytes,
+            stream["layer_size_isolated_GBps"], stream["token_size_single_launch_GBps"],
+            stream["token_bytes"]))
+
+    # ---- parity gate: every layer of token 0 against the float64 oracle -----
+    import oracle
+    oracle.set_threads(os.cpu_count() or 1)
+    od = oracle.Dims(H=wl.H, I=wl.I, E=wl.E, K=wl.K, bits=wl.bits, has_shared=wl.has_shared)
+    graphs[0].replay()
+    torch.cuda.synchronize()
+    check = parity_check(oracle, od, wl, nl, args.check_layers, x, y, ids, wts, experts, shared,
+                         routers_h, x_h, r0_h if chain else None, stride, blob, chain)
 
     # ---- CPU baseline: the float64 oracle on a bounded sample ----------------
     cpu = None
     if not args.no_cpu_baseline:
-        import oracle
-        od = oracle.Dims(H=wl.H, I=wl.I, E=wl.E, K=wl.K, bits=wl.bits, has_shared=wl.has_shared)
-        ncl = min(args.cpu_layers, nl)
-        data = []
-        rr = r0_h[0:1] if chain else None
-        for l in range(ncl):
-            # host copies of the experts the oracle itself selects (not timed)
-            if chain:
-                r_o, xo, _, _, _, _, _ = oracle.residual_layer(
-                    od, routers_h[l], lambda e, l=l: experts[l][e * stride:e * stride + blob]
-                    .cpu().numpy(), shared[l].cpu().numpy(), rr)
-                rr = r_o.astype(np.float32)
-            else:
-                xo = x_h[0, l][None]
-            ido, _, _, _ = oracle.route(od, routers_h[l], xo)
-            blobs = {int(e): experts[l][int(e) * stride:int(e) * stride + blob].cpu().numpy()
-                     for e in ido[0]}
-            data.append((blobs, shared[l].cpu().numpy()))
-        tc = time.perf_counter()
-        rr = r0_h[0:1] if chain else None
-        for l in range(ncl):
-            if chain:
-                rr = oracle.residual_layer(od, routers_h[l], data[l][0], data[l][1],
-                                           rr)[0].astype(np.float32)
-            else:
-                oracle.layer(od, routers_h[l], data[l][0], data[l][1], x_h[0, l][None])
-        dt = time.perf_counter() - tc
-        cpu_tok_s = 1.0 / (dt * nl / ncl)
-        cpu = {"value": cpu_tok_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-               "sample": "token 0, layers 0..%d of %d (%.1f s), scaled to %d layers" % (
-                   ncl - 1, nl, dt, nl)}
-        log("cpu oracle: %.1f s for %d layers -> %.4f tok/s" % (dt, ncl, cpu_tok_s))
+        cpu = cpu_baseline(oracle, od, wl, nl, args.cpu_layers, experts, shared, routers_h, x_h,
+                           r0_h if chain else None, stride, blob, chain)
 
     out = {
         "metric": "MoE decode tokens/s (60 layers, batch 1) + expert-weight GB/s as % HBM peak",
@@ -350,6 +313,7 @@ def main():
         "expert_weight_frac_hbm_peak": expert_gbs / HBM_PEAK_GBS,
         "all_bytes_GBps": all_gbs,
         "layers_per_s": tok_s * nl,
+        "repetitions": dict(reps, unit="tokens/s", n=args.reps, steps_each=args.steps),
         "roofline": {"bound": "hbm",
                      "kernel": ("k_layer1 (moe_layer_decode_residual)" if chain else
                                 "k_layer1 (moe_layer_decode)") if fused else
@@ -359,11 +323,306 @@ def main():
                      "traffic": traffic["traffic_bytes_per_launch"] if traffic else None,
                      "avg_launch_us": layer_us, "isolated_launch_us": iso_us,
                      "bytes_per_launch": launch_bytes},
+        "stream_read": stream,
         "device_error_flags": err,
-        "oracle_check_max_rel_err": check,
+        "parity": check,
+        "parity_ok": check["ok"],
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+    if not check["ok"] or err:
+        log("PARITY FAILED (or device error): see the parity object")
+        sys.exit(3)
+
+
+def spread(vals):
+    v = np.asarray(vals, dtype=np.float64)
+    return {"median": float(np.median(v)), "p10": float(np.percentile(v, 10)),
+            "p90": float(np.percentile(v, 90)), "min": float(v.min()), "max": float(v.max())}
+
+
+def stream_read_rates(torch, moe, buffers, layer_bytes, token_bytes, sp):
+    """moe_stream_read over resident expert memory that the decode did not
+    just touch: one launch per buffer of layer_bytes (back to back, and each
+    between its own events), and one launch of token_bytes (capped at a
+    buffer's size)."""
+    n = len(buffers)
+    off = (buffers[0].numel() // 3) // 256 * 256
+    lb = layer_bytes // 16 * 16
+    tb = min(token_bytes, buffers[0].numel() - 256) // 16 * 16
+    sink = torch.empty(moe.moe_stream_read_sink_words(max(lb, tb)), dtype=torch.int32,
+                       device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    moe.moe_flush(flush, flush.numel(), sp)
+    e0.record()
+    for i in range(n):
+        moe.moe_stream_read(buffers[i][off:], lb, sink, sp)
+    e1.record()
+    torch.cuda.synchronize()
+    b2b_us = e0.elapsed_time(e1) * 1e3 / n
+    iso = []
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    moe.moe_flush(flush, flush.numel(), sp)
+    for i in range(n):
+        evs[i][0].record()
+        moe.moe_stream_read(buffers[(i + n // 2) % n][off + lb:], lb, sink, sp)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    iso = [a.elapsed_time(b) * 1e3 for a, b in evs]
+    tok_us = []
+    for i in range(3):
+        moe.moe_flush(flush, flush.numel(), sp)
+        e0.record()
+        moe.moe_stream_read(buffers[i % n], tb, sink, sp)
+        e1.record()
+        torch.cuda.synchronize()
+        tok_us.append(e0.elapsed_time(e1) * 1e3)
+    return {"layer_bytes": lb, "layer_size_back_to_back_us": b2b_us,
+            "layer_size_back_to_back_GBps": lb / b2b_us / 1e3,
+            "layer_size_isolated_us": float(np.median(iso)),
+            "layer_size_isolated_GBps": lb / float(np.median(iso)) / 1e3,
+            "token_bytes": tb, "token_size_single_launch_us": float(np.median(tok_us)),
+            "token_size_single_launch_GBps": tb / float(np.median(tok_us)) / 1e3}
+
+
+def parity_check(oracle, od, wl, nl, n_check, x, y, ids, wts, experts, shared, routers_h, x_h,
+                 r0_h, stride, blob, chain):
+    """Token 0 of the last replay, layer by layer, against the float64 oracle:
+    ids exact where the float64 gap is at least 1e-3 (else each pick within
+    1e-3 of the correct logit at its rank), w within 1e-5 of the float64
+    softmax of the pick, y within 2e-3 max|y| teacher-forced on the x and
+    the pick the GPU used; on the chain also the x each layer formed against
+    the oracle's norm of the residual (rebuilt as r + y in fp32)."""
+    TIE, WT, YT = 1e-3, 1e-5, 2e-3
+    xk = x[0].cpu().numpy().view(np.uint16) if chain else x_h[0]
+    yk, idk, wk = y[0].cpu().numpy(), ids[0].cpu().numpy(), wts[0].cpu().numpy()
+    rr = r0_h[0].copy() if chain else None
+    worst, worst_w, bad, norm_mis, near_ties = 0.0, 0.0, [], 0, 0
+    n_check = min(n_check, nl)
+    for l in range(n_check):
+        if chain:
+            xo = oracle.rmsnorm_bf16(rr)
+            d = xk[l].astype(np.int32) - xo.astype(np.int32)
+            nm = int(np.count_nonzero(d))
+            norm_mis += nm
+            if nm > 8 or np.any(np.abs(d) > 1):
+                bad.append("layer %d: x differs from the oracle's norm in %d elements" % (l, nm))
+            rr = (rr + yk[l]).astype(np.float32)
+        _, _, lg, gap = oracle.route(od, routers_h[l], xk[l][None])
+        lg, gap = lg[0], float(gap[0])
+        order = np.lexsort((np.arange(lg.size), -lg))[:wl.K]
+        if gap >= TIE:
+            if not np.array_equal(idk[l], order):
+                bad.append("layer %d: ids %s, oracle %s" % (l, idk[l].tolist(), order.tolist()))
+        else:
+            near_ties += 1
+            if np.any(np.abs(lg[idk[l]] - lg[order]) > TIE) or len(set(idk[l].tolist())) != wl.K:
+                bad.append("layer %d: ids %s not within the near-tie margin" % (
+                    l, idk[l].tolist()))
+        sel = lg[idk[l]]
+        wo = np.exp(sel - sel.max())
+        wo /= wo.sum()
+        worst_w = max(worst_w, float(np.max(np.abs(wk[l] - wo))))
+        if abs(float(np.sum(wk[l], dtype=np.float64)) - 1) > 1e-6 or np.max(np.abs(wk[l] - wo)) > WT:
+            bad.append("layer %d: w %s, oracle %s" % (l, wk[l].tolist(), wo.tolist()))
+        blobs = {int(e): experts[l][int(e) * stride:int(e) * stride + blob].cpu().numpy()
+                 for e in idk[l]}
+        yo = oracle.expert_forward(od, blobs, shared[l].cpu().numpy(), xk[l][None], idk[l][None],
+                                   wo[None])[0]
+        e_l = float(np.max(np.abs(yk[l] - yo)) / np.max(np.abs(yo)))
+        worst = max(worst, e_l)
+        if not e_l <= YT:
+            bad.append("layer %d: max|dy|/max|y| = %.2e" % (l, e_l))
+    ok = not bad
+    log("oracle check of token 0, %d layers: max|dy|/max|y| = %.2e, max|dw| = %.1e, %d near "
+        "ties, %s" % (n_check, worst, worst_w, near_ties, "ok" if ok else "FAILED"))
+    for b in bad:
+        log("  " + b)
+    out = {"ok": ok, "token": 0, "layers_checked": n_check, "max_rel_err_y": worst,
+           "max_abs_err_w": worst_w, "near_ties": near_ties, "y_tol": YT, "failures": bad[:10]}
+    if chain:
+        out["x_norm_mismatches"] = norm_mis
+    return out
+
+
+def cpu_baseline(oracle, od, wl, nl, n_single, experts, shared, routers_h, x_h, r0_h, stride,
+                 blob, chain):
+    """The float64 oracle on token 0 of the workload: every layer on all host
+    cores (output rows over threads, results independent of the count), and
+    the first n_single layers on one core, timed without the device-to-host
+    copies of the selected experts."""
+    data = []
+    rr = r0_h[0:1] if chain else None
+    fetch = lambda l: (lambda e: experts[l][e * stride:e * stride + blob].cpu().numpy())
+    oracle.set_threads(1)
+    for l in range(nl):
+        if chain:
+            xo = oracle.rmsnorm_bf16(rr)
+        else:
+            xo = x_h[0, l][None]
+        ido, _, _, _ = oracle.route(od, routers_h[l], xo)
+        blobs = {int(e): fetch(l)(int(e)) for e in ido[0]}
+        data.append((blobs, shared[l].cpu().numpy()))
+        if chain:
+            rr = oracle.residual_layer(od, routers_h[l], blobs, data[l][1], rr)[0].astype(np.float32)
+
+    def run(n):
+        rr = r0_h[0:1] if chain else None
+        tc = time.perf_counter()
+        for l in range(n):
+            if chain:
+                rr = oracle.residual_layer(od, routers_h[l], data[l][0], data[l][1],
+                                           rr)[0].astype(np.float32)
+            else:
+                oracle.layer(od, routers_h[l], data[l][0], data[l][1], x_h[0, l][None])
+        return time.perf_counter() - tc
+
+    ns = max(1, min(n_single, nl))
+    oracle.set_threads(1)
+    dt1 = run(ns)
+    cores = os.cpu_count() or 1
+    oracle.set_threads(cores)
+    dta = run(nl)
+    oracle.set_threads(1)
+    tok1, toka = 1.0 / (dt1 * nl / ns), 1.0 / dta
+    log("cpu oracle: 1 core %.1f s for %d layers -> %.4f tok/s; %d threads %.1f s for %d layers "
+        "-> %.4f tok/s" % (dt1, ns, tok1, cores, dta, nl, toka))
+    return {"value": toka, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": "token 0, all %d layers, output rows over %d threads (%.1f s)" % (
+                nl, cores, dta),
+            "single_core": {"value": tok1, "unit": "tokens/s", "cores": 1,
+                            "sample": "token 0, layers 0..%d of %d (%.1f s), scaled to %d layers"
+                                      % (ns - 1, nl, dt1, nl)}}
+
+
+def bench_layer(args, wl):
+    """One full 512-expert layer, one token per call, with the last-level cache
+    flushed (512 MB of stores) before every call: the call's events exclude
+    the flush.  128 distinct tokens (independent activations, so distinct
+    routings), cycled.  value = calls per second from the summed call times."""
+    import torch
+    import bit_dequant_expert_moe_amd as moe
+    import synth
+    import oracle
+    dims = moe.Dims(hidden=wl.H, inter=wl.I, n_experts=wl.E, top_k=wl.K, bits=wl.bits,
+                    has_shared=wl.has_shared)
+    blob = moe.moe_expert_bytes(dims)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    sp = torch.cuda.current_stream().cuda_stream
+    params = synth.BlobParams(seed=wl.blob_seed, H=wl.H, I=wl.I, bits=wl.bits)
+    ex = torch.empty(wl.E * blob, dtype=torch.uint8, device=dev)
+    synth.gen_blobs_dev(params, 0, 0, wl.E, ex.data_ptr(), blob, sp)
+    sh = torch.empty(blob, dtype=torch.uint8, device=dev)
+    synth.gen_blobs_dev(params, 0, 0xFFFF, 1, sh.data_ptr(), blob, sp)
+    rh = synth.router_weights(wl.seed, 0, wl.E, wl.H)
+    r = torch.from_numpy(rh.view(np.int16)).to(dev)
+    L = moe.make_layer(r, ex, blob, sh)
+    ntok = args.tokens or wl.tokens
+    x_h = synth.tokens(wl.seed, 0, ntok, wl.H)
+    x = torch.from_numpy(x_h.view(np.int16)).to(dev)
+    y = torch.empty((ntok, wl.H), dtype=torch.float32, device=dev)
+    ids = torch.empty((ntok, wl.K), dtype=torch.int32, device=dev)
+    wts = torch.empty((ntok, wl.K), dtype=torch.float32, device=dev)
+    ws = moe.alloc_workspace(dims, 1)
+    wsb = ws.numel()
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def call(t):
+        moe.moe_layer_decode(dims, L, x[t], 1, y[t], ids[t], wts[t], ws, wsb, sp)
+
+    for i in range(args.warmup):
+        moe.moe_flush(flush, flush.numel(), sp)
+        call(i % ntok)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i in range(args.steps):
+        moe.moe_flush(flush, flush.numel(), sp)
+        evs[i][0].record()
+        call(i % ntok)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    err = moe.moe_get_device_error(ws, sp)
+    layer_bytes = wl.E * wl.H * 2 + (wl.K + wl.has_shared) * blob
+    value = len(us) / (us.sum() * 1e-6)
+    achieved = layer_bytes / (np.mean(us) * 1e-6) / 1e9
+    sp_us = spread(us)
+    log("layer call with flushed caches: median %.2f us (p10 %.2f, p90 %.2f), %.0f layers/s, "
+        "%.0f GB/s of algorithmic bytes (%.1f%% of 8 TB/s)" % (
+            sp_us["median"], sp_us["p10"], sp_us["p90"], value, achieved,
+            100 * achieved / HBM_PEAK_GBS))
+    # parity gate: the first tokens against the oracle, teacher-forced
+    oracle.set_threads(os.cpu_count() or 1)
+    od = oracle.Dims(H=wl.H, I=wl.I, E=wl.E, K=wl.K, bits=wl.bits, has_shared=wl.has_shared)
+    fetch = lambda e: ex[e * blob:(e + 1) * blob].cpu().numpy()
+    n_chk = min(args.check_layers, ntok, 8)
+    idh, wh, yh = ids.cpu().numpy(), wts.cpu().numpy(), y.cpu().numpy()
+    bad, worst = [], 0.0
+    _, _, lg, gap = oracle.route(od, rh, x_h[:n_chk])
+    for t in range(n_chk):
+        order = np.lexsort((np.arange(wl.E), -lg[t]))[:wl.K]
+        if gap[t] >= 1e-3 and not np.array_equal(order, idh[t]):
+            bad.append("token %d: ids %s, oracle %s" % (t, idh[t].tolist(), order.tolist()))
+        sel = lg[t][idh[t]]
+        wo = np.exp(sel - sel.max())
+        wo /= wo.sum()
+        if np.max(np.abs(wo - wh[t])) > 1e-5:
+            bad.append("token %d: w" % t)
+        yo = oracle.expert_forward(od, fetch, sh.cpu().numpy(), x_h[t:t + 1], idh[t:t + 1],
+                                   wo[None])[0]
+        e = float(np.max(np.abs(yh[t] - yo)) / np.max(np.abs(yo)))
+        worst = max(worst, e)
+        if not e <= 2e-3:
+            bad.append("token %d: max|dy|/max|y| = %.2e" % (t, e))
+    check = {"ok": not bad, "tokens_checked": n_chk, "max_rel_err_y": worst, "failures": bad}
+    log("oracle check of %d tokens: max|dy|/max|y| = %.2e, %s" % (n_chk, worst,
+                                                                   "ok" if not bad else bad))
+    cpu = None
+    if not args.no_cpu_baseline:
+        nt = 5
+        ido, _, _, _ = oracle.route(od, rh, x_h[:nt])
+        blobs = {int(e): fetch(int(e)) for e in np.unique(ido)}
+        shh = sh.cpu().numpy()
+        cores = os.cpu_count() or 1
+        oracle.set_threads(cores)
+        tc = time.perf_counter()
+        oracle.layer(od, rh, blobs, shh, x_h[:nt])
+        dta = time.perf_counter() - tc
+        oracle.set_threads(1)
+        tc = time.perf_counter()
+        oracle.layer(od, rh, blobs, shh, x_h[:1])
+        dt1 = time.perf_counter() - tc
+        cpu = {"value": nt / dta, "unit": "layers/s", "cores": cores, "kind": "oracle",
+               "sample": "%d tokens of the layer, output rows over %d threads (%.1f s)" % (
+                   nt, cores, dta),
+               "single_core": {"value": 1 / dt1, "unit": "layers/s", "cores": 1,
+                               "sample": "1 token of the layer (%.1f s)" % dt1}}
+        log("cpu oracle: %.2f layers/s on %d threads, %.2f on one core" % (nt / dta, cores,
+                                                                            1 / dt1))
+    out = {
+        "metric": "MoE layer decode (1 token, one full 512-expert layer, caches flushed): "
+                  "layers/s + algorithmic GB/s as % HBM peak",
+        "value": value, "unit": "layers/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": float(np.mean(us)) * 1e-3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "u%d+bf16/fp32" % wl.bits, "data": "synthetic",
+        "config": {"workload": wl.name, "experts": wl.E, "top_k": wl.K, "bits": wl.bits,
+                   "hidden": wl.H, "inter": wl.I, "tokens": ntok, "flush_bytes": flush.numel()},
+        "call_us": sp_us,
+        "roofline": {"bound": "hbm", "kernel": "moe_layer_decode (k_layer1)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "bytes_per_launch": layer_bytes, "avg_launch_us": float(np.mean(us))},
+        "device_error_flags": err, "parity": check, "parity_ok": check["ok"],
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    if bad or err:
+        sys.exit(3)
 
 
 def bench_tier(args, wl):

@@ -18,14 +18,17 @@ MOE_OK = 0
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_UNSUPPORTED",
           -4: "MOE_ERR_ALIGN", -5: "MOE_ERR_WORKSPACE", -6: "MOE_ERR_HIP", -7: "MOE_ERR_DEVICE"}
 SEC_GATE_Q, SEC_UP_Q, SEC_DOWN_Q, SEC_GATE_SB, SEC_UP_SB, SEC_DOWN_SB = range(6)
+# code decoders of the kernel paths (moe_dequantize_as)
+DEQ_SCALAR, DEQ_FP16_PAIR, DEQ_FP8_PAIR, DEQ_BF16_PAIR, DEQ_BF16_SLICE = range(5)
 
 # Entry points that libmoe.so exports (one per declaration in include/moe.h).
 EXPORTS = ("moe_abi_version", "moe_status_str", "moe_check_dims", "moe_expert_bytes",
            "moe_blob_layout", "moe_workspace_bytes", "moe_workspace_init", "moe_route",
            "moe_expert_forward", "moe_layer_decode", "moe_layer_decode_residual",
-           "moe_dequantize", "moe_get_device_error", "moe_tier_staging_bytes",
+           "moe_dequantize", "moe_dequantize_as", "moe_get_device_error", "moe_tier_staging_bytes",
            "moe_tier_device_bytes", "moe_tier_workspace_bytes", "moe_tier_create",
-           "moe_tier_decode", "moe_tier_plan", "moe_tier_stats", "moe_tier_destroy")
+           "moe_tier_decode", "moe_tier_plan", "moe_tier_stats", "moe_tier_destroy",
+           "moe_stream_read_sink_words", "moe_stream_read", "moe_flush")
 
 
 class MoeError(RuntimeError):
@@ -92,6 +95,7 @@ def lib() -> ctypes.CDLL:
             "moe_layer_decode": (i32, [dp, lp, vp, i32, vp, vp, vp, vp, sz, vp]),
             "moe_layer_decode_residual": (i32, [dp, lp, vp, i32, vp, vp, vp, vp, vp, sz, vp]),
             "moe_dequantize": (i32, [dp, vp, i32, vp, vp]),
+            "moe_dequantize_as": (i32, [dp, vp, i32, i32, vp, vp]),
             "moe_get_device_error": (i32, [vp, vp, ctypes.POINTER(i32)]),
             "moe_tier_staging_bytes": (sz, [dp, i32]),
             "moe_tier_device_bytes": (sz, [dp, i32]),
@@ -101,6 +105,9 @@ def lib() -> ctypes.CDLL:
             "moe_tier_plan": (i32, [vp, i32, vp, i32, vp, vp]),
             "moe_tier_stats": (i32, [vp, ctypes.POINTER(ctypes.c_int64)]),
             "moe_tier_destroy": (None, [vp]),
+            "moe_stream_read_sink_words": (sz, [sz]),
+            "moe_stream_read": (i32, [vp, sz, vp, vp]),
+            "moe_flush": (i32, [vp, sz, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -223,6 +230,11 @@ def moe_dequantize(d: Dims, blob, which: int, out, stream=None):
                                 _stream(stream)), "moe_dequantize")
 
 
+def moe_dequantize_as(d: Dims, blob, which: int, decoder: int, out, stream=None):
+    _check(lib().moe_dequantize_as(ctypes.byref(d.c()), _ptr(blob), which, decoder, _ptr(out),
+                                   _stream(stream)), "moe_dequantize_as")
+
+
 def moe_get_device_error(ws, stream=None) -> int:
     err = ctypes.c_int32(0)
     rc = lib().moe_get_device_error(_ptr(ws), _stream(stream), ctypes.byref(err))
@@ -306,3 +318,22 @@ def moe_tier_device_bytes(d: Dims, t_max: int) -> int:
 
 def moe_tier_workspace_bytes(d: Dims, n_slots: int, T: int) -> int:
     return int(lib().moe_tier_workspace_bytes(ctypes.byref(d.c()), n_slots, T))
+
+
+# ---- measurement helpers ---------------------------------------------------------
+
+def moe_stream_read_sink_words(nbytes: int) -> int:
+    return int(lib().moe_stream_read_sink_words(nbytes))
+
+
+def moe_stream_read(src, nbytes: int, sink, stream=None):
+    """One launch reading nbytes of device memory at src (a tensor or a
+    device address); sink: int32/uint32 device tensor of
+    moe_stream_read_sink_words(nbytes) words."""
+    _check(lib().moe_stream_read(_ptr(src), nbytes, _ptr(sink), _stream(stream)),
+           "moe_stream_read")
+
+
+def moe_flush(dst, nbytes: int, stream=None):
+    """One launch overwriting nbytes of device memory at dst."""
+    _check(lib().moe_flush(_ptr(dst), nbytes, _stream(stream)), "moe_flush")

@@ -7,7 +7,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe.so")
 SOURCES = [os.path.join(CSRC, "moe_host.cpp"), os.path.join(CSRC, "moe_kernels.hip"),
            os.path.join(CSRC, "moe_fused.hip"), os.path.join(CSRC, "moe_grouped.hip"),
-           os.path.join(CSRC, "moe_tier.cpp")]
+           os.path.join(CSRC, "moe_tier.cpp"), os.path.join(CSRC, "moe_probe.hip")]
 HEADERS = [os.path.join(CSRC, "moe_internal.h"), os.path.join(CSRC, "moe_device.h"),
            os.path.join(os.path.dirname(HERE), "include", "moe.h")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

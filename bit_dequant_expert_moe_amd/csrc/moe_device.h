@@ -185,34 +185,70 @@ __device__ void stage_x(const uint16_t *__restrict__ x, int H, uint32_t *xp, flo
   }
 }
 
+// Packed fp16 pair p of one 32-bit code word: (1024 + m q_a, 1024 + m q_b)
+// with one v_and_or_b32 against the magic 0x6400 (1024.0).  The pair holds
+//   4 bits: codes (p, p + 4) of the word's 8, with m = 16^(p & 1);
+//   2 bits: codes (p, p + 8) of the word's 16, with m = 4^p (p < 5) or
+//           4^(p - 5) (p >= 5, fields taken from the word shifted by 10).
+// 1024 + m q is exact in fp16 (m q <= 256 < 1024 = its unit step times 2^10).
+// This is the unpack of the single-token gate/up products (seg_dot_x); the
+// dequantisation hook (moe_dequantize_as) calls it too.
+// (us is the word shifted right by 8 at 4 bits, by 10 at 2 bits; the caller
+// forms it once per word.)
+template <int BITS>
+__device__ __forceinline__ uint32_t h2_code_pair(uint32_t u, uint32_t us, int p) {
+  const uint32_t M = kMagicH;
+  if (BITS == 4) {
+    return and_or(p < 2 ? u : us, (p & 1) ? 0x00F000F0u : 0x000F000Fu, M);
+  } else {
+    const int f = p < 5 ? p : p - 5;
+    return and_or(p < 5 ? u : us, 0x00030003u << (2 * f), M);
+  }
+}
+template <int BITS>
+__device__ __forceinline__ uint32_t h2_shifted(uint32_t u) {
+  return BITS == 4 ? u >> 8 : u >> 10;
+}
+
 // sum_c (magic_c + q_c) * xtilde_c over one 16-byte segment.
 template <int BITS>
 __device__ __forceinline__ float seg_dot_x(uint4 c, const uint32_t *xp) {
-  const uint32_t M = kMagicH;
+  constexpr int NP = 16 / BITS;  // pairs per word (4 or 8)
   float acc = 0.f;
   const uint32_t w[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
   for (int wd = 0; wd < 4; ++wd) {
-    const uint32_t u = w[wd];
-    if (BITS == 4) {
-      const uint32_t u8 = u >> 8;
-      acc = dot2h(and_or(u, 0x000F000Fu, M), xp[4 * wd + 0], acc);
-      acc = dot2h(and_or(u, 0x00F000F0u, M), xp[4 * wd + 1], acc);
-      acc = dot2h(and_or(u8, 0x000F000Fu, M), xp[4 * wd + 2], acc);
-      acc = dot2h(and_or(u8, 0x00F000F0u, M), xp[4 * wd + 3], acc);
-    } else {
-      const uint32_t u10 = u >> 10;
-      acc = dot2h(and_or(u, 0x00030003u, M), xp[8 * wd + 0], acc);
-      acc = dot2h(and_or(u, 0x000C000Cu, M), xp[8 * wd + 1], acc);
-      acc = dot2h(and_or(u, 0x00300030u, M), xp[8 * wd + 2], acc);
-      acc = dot2h(and_or(u, 0x00C000C0u, M), xp[8 * wd + 3], acc);
-      acc = dot2h(and_or(u, 0x03000300u, M), xp[8 * wd + 4], acc);
-      acc = dot2h(and_or(u10, 0x00030003u, M), xp[8 * wd + 5], acc);
-      acc = dot2h(and_or(u10, 0x000C000Cu, M), xp[8 * wd + 6], acc);
-      acc = dot2h(and_or(u10, 0x00300030u, M), xp[8 * wd + 7], acc);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const uint32_t us = h2_shifted<BITS>(w[wd]);
+      acc = dot2h(h2_code_pair<BITS>(w[wd], us, p), xp[NP * wd + p], acc);
     }
   }
   return acc;
+}
+
+// ---------------------------------------------------------------------------
+// Dequantisation hooks (moe_dequantize, moe_dequantize_as): one matrix of a
+// blob as fp32, one thread per 32-bit code word, each code decoded by the
+// unpack of one kernel path.
+// ---------------------------------------------------------------------------
+struct DequantArgs {
+  const uint32_t *q, *sb;  // the matrix's code words [rows][cols / cpw] and (s, z) words
+  float *out;              // fp32 [rows][cols]
+  int rows, cols, bits;
+};
+
+// Writes s q_j + z for the CPW codes of word (r, c0 / CPW), q in column
+// order as exact integers in fp32: s q is exact in fp32 (8 significant bits
+// times at most 4), so the FMA rounds the exact value s q + z once.
+template <int CPW>
+__device__ __forceinline__ void store_dequant_word(const DequantArgs &a, size_t r, int c0,
+                                                   const float (&q)[CPW]) {
+  const uint32_t sz = a.sb[r * (a.cols / 64) + c0 / 64];
+  const float s = bf16f(sz & 0xFFFFu), z = bf16f(sz >> 16);
+  float *o = a.out + r * a.cols + c0;
+#pragma unroll
+  for (int j = 0; j < CPW; ++j) o[j] = fmaf(s, q[j], z);
 }
 
 }  // namespace dev

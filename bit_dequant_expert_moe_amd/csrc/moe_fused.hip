@@ -214,39 +214,64 @@ __device__ __forceinline__ float fp8_code_unit() {
   return __builtin_amdgcn_cvt_pk_f32_fp8(1, false)[0];
 }
 
-// u sum_c q_c h_c over the codes of one 32-bit word (8 at 4 bits, 16 at 2
-// bits) of a down row, fp32, with u = fp8_code_unit(); hv holds the word's
-// activations.  m is the per-byte code mask (0x0F0F0F0F or 0x03030303) in a
-// register the compiler cannot see through.  Each masked word converts two
-// codes per instruction (v_cvt_pk_f32_fp8 on its low and high half); the
-// products are summed in code order, and since u is a power of two the sum
-// is exactly u times the one formed from integer codes.
+// The codes of one 32-bit word of a down row as fp32 values u q_c, in column
+// order (8 at 4 bits, 16 at 2 bits), u = fp8_code_unit().  m is the per-byte
+// code mask (0x0F0F0F0F or 0x03030303) in a register the compiler cannot see
+// through.  Each masked word converts two codes per instruction
+// (v_cvt_pk_f32_fp8 on its low and high half): at 4 bits the masked word
+// holds codes (0, 2, 4, 6) and the word shifted by 4 codes (1, 3, 5, 7); at
+// 2 bits the word shifted by 2k holds codes (k, 4 + k, 8 + k, 12 + k).
+// This is the unpack of the single-token down products (word_dot_f32); the
+// dequantisation hook (moe_dequantize_as) calls it too.
 template <int BITS>
-__device__ __forceinline__ float word_dot_f32(uint32_t u, const float *hv, float acc, uint32_t m) {
+__device__ __forceinline__ void fp8_word_codes(uint32_t u, uint32_t m, float (&q)[32 / BITS]) {
   if (BITS == 4) {
     const uint32_t lo = u & m, hi = (u >> 4) & m;
     const auto l0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
     const auto l1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
     const auto h0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
     const auto h1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
-    acc = fmaf(l0[0], hv[0], acc);
-    acc = fmaf(h0[0], hv[1], acc);
-    acc = fmaf(l0[1], hv[2], acc);
-    acc = fmaf(h0[1], hv[3], acc);
-    acc = fmaf(l1[0], hv[4], acc);
-    acc = fmaf(h1[0], hv[5], acc);
-    acc = fmaf(l1[1], hv[6], acc);
-    acc = fmaf(h1[1], hv[7], acc);
+    q[0] = l0[0];
+    q[1] = h0[0];
+    q[2] = l0[1];
+    q[3] = h0[1];
+    q[4] = l1[0];
+    q[5] = h1[0];
+    q[6] = l1[1];
+    q[7] = h1[1];
   } else {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const uint32_t mk = (u >> (2 * k)) & m;
       const auto c0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)mk, false);
       const auto c1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)mk, true);
-      acc = fmaf(c0[0], hv[k], acc);
-      acc = fmaf(c0[1], hv[4 + k], acc);
-      acc = fmaf(c1[0], hv[8 + k], acc);
-      acc = fmaf(c1[1], hv[12 + k], acc);
+      q[k] = c0[0];
+      q[4 + k] = c0[1];
+      q[8 + k] = c1[0];
+      q[12 + k] = c1[1];
+    }
+  }
+}
+
+// u sum_c q_c h_c over the codes of one 32-bit word of a down row, fp32; hv
+// holds the word's activations.  The products are summed in the order the
+// conversions produce them (column order at 4 bits; k-major at 2 bits); u is
+// a power of two, so the sum is exactly u times the one formed from integer
+// codes.
+template <int BITS>
+__device__ __forceinline__ float word_dot_f32(uint32_t u, const float *hv, float acc, uint32_t m) {
+  float q[32 / BITS];
+  fp8_word_codes<BITS>(u, m, q);
+  if (BITS == 4) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc = fmaf(q[c], hv[c], acc);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      acc = fmaf(q[k], hv[k], acc);
+      acc = fmaf(q[4 + k], hv[4 + k], acc);
+      acc = fmaf(q[8 + k], hv[8 + k], acc);
+      acc = fmaf(q[12 + k], hv[12 + k], acc);
     }
   }
   return acc;
@@ -878,9 +903,39 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
   }
 }
 
+// Dequantisation hook of the fp8 pair convert: s q + z per code, with q the
+// value fp8_word_codes forms (u q) times 1 / u (exact, a power of two).
+template <int BITS>
+__global__ void __launch_bounds__(256) k_dequant_fp8(DequantArgs a) {
+  constexpr int CPW = 32 / BITS;
+  uint32_t m = BITS == 4 ? 0x0F0F0F0Fu : 0x03030303u;
+  asm volatile("" : "+s"(m));
+  const float iu = 1.f / fp8_code_unit();
+  const int wpr = a.cols / CPW;
+  const size_t n = (size_t)a.rows * wpr;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const size_t r = i / wpr;
+    const int c0 = (int)(i - r * wpr) * CPW;
+    float q[CPW];
+    fp8_word_codes<BITS>(a.q[i], m, q);
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) q[j] *= iu;
+    store_dequant_word<CPW>(a, r, c0, q);
+  }
+}
+
 inline hipStream_t S(void *s) { return static_cast<hipStream_t>(s); }
 
 }  // namespace
+
+int launch_dequant_fp8(const DequantArgs &a, int blocks, void *stream) {
+  if (a.bits == 4)
+    hipLaunchKernelGGL(k_dequant_fp8<4>, dim3(blocks), dim3(256), 0, S(stream), a);
+  else
+    hipLaunchKernelGGL(k_dequant_fp8<2>, dim3(blocks), dim3(256), 0, S(stream), a);
+  return (int)hipGetLastError();
+}
 
 // Returns true if the fused single-token kernel covers these dims.
 bool fused_supported(const moe_dims &d) {

@@ -63,11 +63,18 @@ static_assert(kRT == kGroup, "a gate/up row tile is one group of the down column
 //   bk[2 + 2 maxB + p]          pair code t (K + 1) + slot (slot K = shared),
 //                               p < T (K + 1) = pair_cap
 //   bk[2 + 2 maxB + pair_cap]   number of work items
-//   bk[3 + 2 maxB + pair_cap + i]  work item i = bucket << 8 | chunk: the pairs
+//   bk[3 + 2 maxB + pair_cap + i]  work item i = bucket << 16 | chunk: the pairs
 //                               kNC chunk .. kNC chunk + kNC - 1 of the bucket
+//                               (bucket < maxB <= 1025 and chunk < T K / kNC
+//                               <= 2048 even when a token repeats an expert)
 // One GEMM block per (row tile, work item): no block is launched for an
 // empty chunk of a bucket.
 // ---------------------------------------------------------------------------
+
+// Work item = bucket << kItemShift | chunk.
+constexpr int kItemShift = 16;
+static_assert((kMaxT * kMaxK + kNC - 1) / kNC < (1 << kItemShift), "chunk field holds every chunk");
+static_assert((kMaxE + 1) < (1 << (31 - kItemShift)), "bucket field holds every bucket");
 
 // Upper bound of the number of work items for T tokens.
 __host__ __device__ constexpr int max_items(int E, int T, int K, int has_shared) {
@@ -152,11 +159,11 @@ __global__ void __launch_bounds__(1024) k_bucket(BucketArgs a) {
   int nitems;
   const int ioff = block_exscan(nz, s_wtot, &nitems);
   int32_t *items = a.bk + 3 + 2 * a.maxB + a.pair_cap;
-  for (int z = 0; z < nz; ++z) items[ioff + z] = (j << 8) | z;
+  for (int z = 0; z < nz; ++z) items[ioff + z] = (j << kItemShift) | z;
   if (tid == 0) {
     if (a.has_shared) {
       const int nzs = (a.T + kNC - 1) / kNC;
-      for (int z = 0; z < nzs; ++z) items[nitems + z] = (nrb << 8) | z;
+      for (int z = 0; z < nzs; ++z) items[nitems + z] = (nrb << kItemShift) | z;
       nitems += nzs;
     }
     a.bk[2 + 2 * a.maxB + a.pair_cap] = nitems;
@@ -315,10 +322,10 @@ __global__ void __launch_bounds__(256) k_grouped(GroupArgs a) {
   const int32_t *items = a.bk + 2 + 2 * a.maxB + a.pair_cap;
   if ((int)blockIdx.y >= items[0]) return;
   const int item = items[1 + blockIdx.y];
-  const int j = item >> 8;
+  const int j = item >> kItemShift;
   const int e = a.bk[1 + j];
   const int p0 = a.bk[1 + a.maxB + j], p1 = a.bk[2 + a.maxB + j];
-  const int pbase = p0 + kNC * (item & 255);
+  const int pbase = p0 + kNC * (item & ((1 << kItemShift) - 1));
   if (pbase >= p1) return;
   const int nn = min(kNC, p1 - pbase);
   const int32_t *pairs = a.bk + 2 + 2 * a.maxB + pbase;
@@ -590,6 +597,35 @@ __global__ void __launch_bounds__(256) k_combine(CombineArgs a) {
   *reinterpret_cast<float4 *>(a.y + (size_t)t * a.H + r) = s;
 }
 
+// Dequantisation hook of the grouped GEMM's A operand: s q + z per code, with
+// q = (128 + q) - 128 from the bf16 slices a_slice forms, element i of a
+// slice being column i / 2 (i even) or i / 2 + 4 (i odd) of its 8 columns.
+template <int BITS>
+__global__ void __launch_bounds__(256) k_dequant_slices(DequantArgs a) {
+  constexpr int CPW = 32 / BITS;
+  const Unpack uk = Unpack::make<BITS>();
+  const int wpr = a.cols / CPW;
+  const size_t n = (size_t)a.rows * wpr;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const size_t r = i / wpr;
+    const int c0 = (int)(i - r * wpr) * CPW;
+    const uint32_t w = a.q[i];
+    float q[CPW];
+#pragma unroll
+    for (int half = 0; half < CPW / 8; ++half) {
+      const uint4 v = __builtin_bit_cast(uint4, a_slice<BITS>(w, half, uk));
+      const uint32_t e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        q[8 * half + k] = bf16f(e[k] & 0xFFFFu) - 128.f;
+        q[8 * half + k + 4] = bf16f(e[k] >> 16) - 128.f;
+      }
+    }
+    store_dequant_word<CPW>(a, r, c0, q);
+  }
+}
+
 inline hipStream_t S(void *s) { return static_cast<hipStream_t>(s); }
 
 // Allows `bytes` of dynamic LDS for kernel f; the default cap (64 KB) needs
@@ -614,6 +650,14 @@ int launch_gemms(const GroupArgs &gu, const GroupArgs &dn, dim3 grid_gu, dim3 gr
 }
 
 }  // namespace
+
+int launch_dequant_slices(const DequantArgs &a, int blocks, void *stream) {
+  if (a.bits == 4)
+    hipLaunchKernelGGL(k_dequant_slices<4>, dim3(blocks), dim3(256), 0, S(stream), a);
+  else
+    hipLaunchKernelGGL(k_dequant_slices<2>, dim3(blocks), dim3(256), 0, S(stream), a);
+  return (int)hipGetLastError();
+}
 
 int grouped_max_buckets(const moe_dims &d, int T) {
   const int routed = d.n_experts < T * d.top_k ? d.n_experts : T * d.top_k;

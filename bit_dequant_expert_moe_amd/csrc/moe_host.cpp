@@ -302,13 +302,41 @@ moe_status moe_layer_decode_residual(const moe_dims *dims, const moe_layer *laye
   return MOE_OK;
 }
 
-moe_status moe_dequantize(const moe_dims *dims, const uint8_t *blob, int32_t which, float *out,
-                          void *stream) {
+moe_status moe_dequantize_as(const moe_dims *dims, const uint8_t *blob, int32_t which,
+                             int32_t decoder, float *out, void *stream) {
   MOE_TRY(check_dims(dims));
   if (!blob || !out) return MOE_ERR_NULL;
   if (which < 0 || which > 2) return MOE_ERR_SHAPE;
+  if (decoder < MOE_DEQ_SCALAR || decoder > MOE_DEQ_BF16_SLICE) return MOE_ERR_SHAPE;
   if (!aligned(blob, kAlign) || !aligned(out, 16)) return MOE_ERR_ALIGN;
-  return launch_dequantize(*dims, blob, which, out, stream) == 0 ? MOE_OK : MOE_ERR_HIP;
+  return launch_dequantize_as(*dims, blob, which, decoder, out, stream) == 0 ? MOE_OK
+                                                                              : MOE_ERR_HIP;
+}
+
+moe_status moe_dequantize(const moe_dims *dims, const uint8_t *blob, int32_t which, float *out,
+                          void *stream) {
+  // the decoders of the single-token kernel: fp16 pairs for gate and up,
+  // the fp8 pair convert for down
+  return moe_dequantize_as(dims, blob, which, which == 2 ? MOE_DEQ_FP8_PAIR : MOE_DEQ_FP16_PAIR,
+                           out, stream);
+}
+
+size_t moe_stream_read_sink_words(size_t bytes) {
+  return (size_t)stream_read_blocks(bytes);
+}
+
+moe_status moe_stream_read(const void *src, size_t bytes, uint32_t *sink, void *stream) {
+  if (!src || !sink) return MOE_ERR_NULL;
+  if (bytes == 0 || bytes % 16 != 0) return MOE_ERR_SHAPE;
+  if (!aligned(src, 16) || !aligned(sink, 4)) return MOE_ERR_ALIGN;
+  return launch_stream_read(src, bytes, sink, stream) == 0 ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_flush(void *dst, size_t bytes, void *stream) {
+  if (!dst) return MOE_ERR_NULL;
+  if (bytes == 0 || bytes % 16 != 0) return MOE_ERR_SHAPE;
+  if (!aligned(dst, 16)) return MOE_ERR_ALIGN;
+  return launch_flush(dst, bytes, stream) == 0 ? MOE_OK : MOE_ERR_HIP;
 }
 
 moe_status moe_get_device_error(void *ws, void *stream, int32_t *err) {

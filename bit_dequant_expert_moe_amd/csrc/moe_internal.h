@@ -129,8 +129,14 @@ int launch_layer_fused(const moe_dims &d, const moe_layer &L, const uint16_t *x,
 // Residual stream steps of the unfused path.
 int launch_rmsnorm(const moe_dims &d, const float *r, int T, uint16_t *x, void *stream);
 int launch_resid_add(const moe_dims &d, float *r, const float *y, int T, void *stream);
-int launch_dequantize(const moe_dims &d, const uint8_t *blob, int which, float *out,
-                      void *stream);
+// One matrix of a blob as fp32 through the unpack of `decoder` (MOE_DEQ_*).
+int launch_dequantize_as(const moe_dims &d, const uint8_t *blob, int which, int decoder,
+                         float *out, void *stream);
+namespace dev {
+struct DequantArgs;
+}
+int launch_dequant_fp8(const dev::DequantArgs &a, int blocks, void *stream);     // moe_fused.hip
+int launch_dequant_slices(const dev::DequantArgs &a, int blocks, void *stream);  // moe_grouped.hip
 // Batched path (moe_grouped.hip): pairs grouped by expert, MFMA GEMMs.
 int grouped_max_buckets(const moe_dims &d, int T);
 int grouped_bucket_words(const moe_dims &d, int T);  // int32 words of the bucket area
@@ -138,5 +144,9 @@ int launch_expert_forward_grouped(const moe_dims &d, const moe_layer &L, const u
                                   int T, const int32_t *ids, const float *w, float *y, void *ws,
                                   void *stream);
 int read_device_error(void *ws, void *stream, int32_t *err);
+// Measurement kernels (moe_probe.hip).
+int stream_read_blocks(size_t bytes);
+int launch_stream_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
+int launch_flush(void *dst, size_t bytes, void *stream);
 
 }  // namespace moe

@@ -68,29 +68,29 @@ __device__ void stage_h(const float *__restrict__ h, int I, uint32_t *hp, float2
   }
 }
 
+// bf16 pair j of one code word for the unfused down products:
+// (128 + q_a, 128 + q_b) with one v_and_or_b32 against the magic 0x4300
+// (128.0); codes (j, j + 4) of 8 at 4 bits, (j, j + 8) of 16 at 2 bits.
+// 128 + q is exact in bf16 (q < 16 < 128's unit step times 2^7).  The
+// dequantisation hook (moe_dequantize_as) calls it too.
+template <int BITS>
+__device__ __forceinline__ uint32_t b2_code_pair(uint32_t u, int j) {
+  return and_or(u >> (BITS * j), BITS == 4 ? 0x000F000Fu : 0x00030003u, kMagicB);
+}
+
 template <int BITS>
 __device__ __forceinline__ float seg_dot_h(uint4 c, const uint32_t *hp) {
   constexpr int kPairs = XSeg<BITS>::kPairs;
-  const uint32_t M = kMagicB;
+  constexpr int NP = 16 / BITS;  // pairs per word (4 or 8)
   float acc = 0.f;
   const uint32_t w[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
   for (int wd = 0; wd < 4; ++wd) {
-    const uint32_t u = w[wd];
-    if (BITS == 4) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t v = and_or(u >> (4 * j), 0x000F000Fu, M);
-        acc = dot2b(v, hp[4 * wd + j], acc);
-        acc = dot2b(v, hp[kPairs + 4 * wd + j], acc);
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const uint32_t v = and_or(u >> (2 * k), 0x00030003u, M);
-        acc = dot2b(v, hp[8 * wd + k], acc);
-        acc = dot2b(v, hp[kPairs + 8 * wd + k], acc);
-      }
+    for (int j = 0; j < NP; ++j) {
+      const uint32_t v = b2_code_pair<BITS>(w[wd], j);
+      acc = dot2b(v, hp[NP * wd + j], acc);
+      acc = dot2b(v, hp[kPairs + NP * wd + j], acc);
     }
   }
   return acc;
@@ -396,14 +396,15 @@ __global__ void __launch_bounds__(256) k_down(DownArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Dequantisation hook: one thread per code word.
+// Dequantisation hooks: one thread per code word; each writes s q + z for
+// the word's codes, with q as the named decoder produces it.
+//   k_dequantize        mask and shift per code (the plain reading of the format)
+//   k_dequant_pairs<1>  fp16 pairs 1024 + m q (h2_code_pair: single-token and
+//                       unfused gate/up products)
+//   k_dequant_pairs<3>  bf16 pairs 128 + q (b2_code_pair: unfused down products)
+// The fp8 pair convert of the single-token down products and the bf16 slices
+// of the grouped GEMM have their hooks beside their kernels.
 // ---------------------------------------------------------------------------
-struct DequantArgs {
-  const uint32_t *q, *sb;
-  float *out;
-  int rows, cols, bits;
-};
-
 __global__ void __launch_bounds__(256) k_dequantize(DequantArgs a) {
   const int cpw = 32 / a.bits;
   const int wpr = a.cols / cpw;
@@ -418,6 +419,38 @@ __global__ void __launch_bounds__(256) k_dequantize(DequantArgs a) {
     const float s = bf16f(sz & 0xFFFFu), z = bf16f(sz >> 16);
     float *o = a.out + r * a.cols + c0;
     for (int j = 0; j < cpw; ++j) o[j] = fmaf(s, (float)((w >> (a.bits * j)) & mask), z);
+  }
+}
+
+template <int BITS, int DEC>
+__global__ void __launch_bounds__(256) k_dequant_pairs(DequantArgs a) {
+  constexpr int CPW = 32 / BITS, NP = CPW / 2;
+  const int wpr = a.cols / CPW;
+  const size_t n = (size_t)a.rows * wpr;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const size_t r = i / wpr;
+    const int c0 = (int)(i - r * wpr) * CPW;
+    const uint32_t w = a.q[i];
+    float q[CPW];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      // pair p holds codes (p, p + NP) of the word
+      if (DEC == MOE_DEQ_FP16_PAIR) {
+        const uint32_t v = h2_code_pair<BITS>(w, h2_shifted<BITS>(w), p);
+        const h2_t hv = __builtin_bit_cast(h2_t, v);
+        // 1024 + m q with m = 16^(p & 1) (4 bits) or 4^f (2 bits); 1 / m is exact
+        const int f = BITS == 4 ? 2 * (p & 1) : (p < 5 ? p : p - 5);
+        const float im = 1.f / (float)(1 << (2 * f));
+        q[p] = ((float)hv.x - 1024.f) * im;
+        q[p + NP] = ((float)hv.y - 1024.f) * im;
+      } else {
+        const uint32_t v = b2_code_pair<BITS>(w, p);
+        q[p] = bf16f(v & 0xFFFFu) - 128.f;
+        q[p + NP] = bf16f(v >> 16) - 128.f;
+      }
+    }
+    store_dequant_word<CPW>(a, r, c0, q);
   }
 }
 
@@ -608,8 +641,8 @@ int launch_resid_add(const moe_dims &d, float *r, const float *y, int T, void *s
   return (int)hipGetLastError();
 }
 
-int launch_dequantize(const moe_dims &d, const uint8_t *blob, int which, float *out,
-                      void *stream) {
+int launch_dequantize_as(const moe_dims &d, const uint8_t *blob, int which, int decoder,
+                         float *out, void *stream) {
   const BlobLayout B = blob_layout(d);
   DequantArgs a;
   a.q = reinterpret_cast<const uint32_t *>(blob + B.off[which]);
@@ -621,7 +654,26 @@ int launch_dequantize(const moe_dims &d, const uint8_t *blob, int which, float *
   const size_t words = (size_t)a.rows * a.cols / (32 / d.bits);
   size_t blocks = (words + 255) / 256;
   if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL(k_dequantize, dim3((unsigned)blocks), dim3(256), 0, S(stream), a);
+  const dim3 g((unsigned)blocks), b(256);
+  switch (decoder) {
+    case MOE_DEQ_SCALAR:
+      hipLaunchKernelGGL(k_dequantize, g, b, 0, S(stream), a);
+      break;
+    case MOE_DEQ_FP16_PAIR:
+      if (d.bits == 4) hipLaunchKernelGGL((k_dequant_pairs<4, MOE_DEQ_FP16_PAIR>), g, b, 0, S(stream), a);
+      else hipLaunchKernelGGL((k_dequant_pairs<2, MOE_DEQ_FP16_PAIR>), g, b, 0, S(stream), a);
+      break;
+    case MOE_DEQ_BF16_PAIR:
+      if (d.bits == 4) hipLaunchKernelGGL((k_dequant_pairs<4, MOE_DEQ_BF16_PAIR>), g, b, 0, S(stream), a);
+      else hipLaunchKernelGGL((k_dequant_pairs<2, MOE_DEQ_BF16_PAIR>), g, b, 0, S(stream), a);
+      break;
+    case MOE_DEQ_FP8_PAIR:
+      return launch_dequant_fp8(a, (int)blocks, stream);
+    case MOE_DEQ_BF16_SLICE:
+      return launch_dequant_slices(a, (int)blocks, stream);
+    default:
+      return (int)hipErrorInvalidValue;
+  }
   return (int)hipGetLastError();
 }
 

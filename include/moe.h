@@ -300,10 +300,35 @@ moe_status moe_tier_stats(const moe_tier *tier, int64_t out[4]);
 /* Frees the tier object (not the caller's buffers).  NULL is ignored. */
 void moe_tier_destroy(moe_tier *tier);
 
+/* Code decoders of the kernels, for moe_dequantize_as.  Each turns the codes
+ * of a 32-bit word into numbers the way one kernel path does before its
+ * products ([MC], "The Architecture": the dequantisation sits inside the
+ * matrix-vector inner loop, so each path has its own unpack):
+ *   MOE_DEQ_SCALAR      mask and shift per code (the format read directly)
+ *   MOE_DEQ_FP16_PAIR   fp16 pairs 1024 + m q from one AND-OR with 0x6400:
+ *                       gate/up of the single-token and unfused paths
+ *   MOE_DEQ_FP8_PAIR    masked code bytes converted two at a time as fp8:
+ *                       down of the single-token path
+ *   MOE_DEQ_BF16_PAIR   bf16 pairs 128 + q from one AND-OR with 0x4300: down
+ *                       of the unfused path
+ *   MOE_DEQ_BF16_SLICE  bf16 slices 128 + q of the matrix-core A operand:
+ *                       gate/up and down of the grouped path (T >= 2) */
+enum {
+  MOE_DEQ_SCALAR = 0, MOE_DEQ_FP16_PAIR = 1, MOE_DEQ_FP8_PAIR = 2,
+  MOE_DEQ_BF16_PAIR = 3, MOE_DEQ_BF16_SLICE = 4
+};
+
 /* Test hook: writes the dequantised fp32 matrix `which` (0 Gate [I][H],
- * 1 Up [I][H], 2 Down [H][I]) of one blob to out (row-major).  Each element
- * is s*q + z rounded once to fp32 (s*q is exact in fp32), so the result is
- * bit-exact against any correct decoder of the format. */
+ * 1 Up [I][H], 2 Down [H][I]) of one blob to out (row-major), each code
+ * decoded by `decoder` (any of the MOE_DEQ_* values, for any matrix).  Each
+ * element is s*q + z rounded once to fp32 (s*q is exact in fp32), so every
+ * correct decoder gives the same bits.  blob 256-byte aligned, out 16-byte
+ * aligned.  MOE_ERR_SHAPE for `which` or `decoder` out of range. */
+moe_status moe_dequantize_as(const moe_dims *dims, const uint8_t *blob,
+                             int32_t which, int32_t decoder, float *out, void *stream);
+
+/* moe_dequantize_as with the decoders of the single-token kernel:
+ * MOE_DEQ_FP16_PAIR for gate and up, MOE_DEQ_FP8_PAIR for down. */
 moe_status moe_dequantize(const moe_dims *dims, const uint8_t *blob,
                           int32_t which, float *out, void *stream);
 
@@ -312,6 +337,28 @@ moe_status moe_dequantize(const moe_dims *dims, const uint8_t *blob,
  * the single-token kernel timed out, see the conventions) and clears them.
  * `err` is a host pointer.  Returns MOE_ERR_DEVICE when *err != 0. */
 moe_status moe_get_device_error(void *ws, void *stream, int32_t *err);
+
+/* ---------------------------------------------------------------------------
+ * Measurement helpers (beside the method, for benchmarks)
+ * ------------------------------------------------------------------------- */
+
+/* Words of `sink` that moe_stream_read writes for a read of `bytes` (one per
+ * workgroup).  Host only. */
+size_t moe_stream_read_sink_words(size_t bytes);
+
+/* Enqueues one launch that reads `bytes` of device memory at `src` with
+ * 16-byte loads spread over up to 2048 workgroups and writes an XOR of what
+ * each workgroup read to sink[0 .. moe_stream_read_sink_words(bytes) - 1]:
+ * the streaming read rate a single launch reaches at that size, the
+ * achievable counterpart of the HBM peak for the layer's byte counts.
+ * src 16-byte aligned, bytes a nonzero multiple of 16, sink device uint32. */
+moe_status moe_stream_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
+
+/* Enqueues a launch that overwrites `bytes` of device memory at `dst`
+ * (16-byte aligned, nonzero multiple of 16) with stores: with a size above
+ * the last-level cache (256 MB) the next launch finds none of its bytes
+ * cached. */
+moe_status moe_flush(void *dst, size_t bytes, void *stream);
 
 #ifdef __cplusplus
 }

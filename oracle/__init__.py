@@ -56,7 +56,8 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", "-O2", "-std=c99", "-Wall", "-ffp-contract=off",
-                               "-fno-fast-math", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"])
+                               "-fno-fast-math", "-fopenmp", "-fPIC", "-shared", "-o", tmp,
+                               _SRC, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -70,6 +71,10 @@ def lib():
         build(force=False)
         L = ctypes.CDLL(_LIB)
         dp = ctypes.POINTER(_Dims)
+        L.or_set_threads.restype = None
+        L.or_set_threads.argtypes = [ctypes.c_int]
+        L.or_get_threads.restype = ctypes.c_int
+        L.or_get_threads.argtypes = []
         L.or_bf16.restype = ctypes.c_double
         L.or_bf16.argtypes = [ctypes.c_uint16]
         L.or_section_offset.restype = ctypes.c_int64
@@ -115,6 +120,16 @@ def lib():
                                         _f64p, _f64p]
         _lib = L
     return _lib
+
+
+def set_threads(n: int) -> None:
+    """Threads for independent output rows (1: sequential).  Results are the
+    same for every thread count."""
+    lib().or_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return int(lib().or_get_threads())
 
 
 def _p(a: np.ndarray, t):

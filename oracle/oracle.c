@@ -20,12 +20,16 @@
  *   renormalisation of the K kept probabilities; ties in the logits go to the
  *   lower expert index; SwiGLU h = silu(gate x) * (up x); the shared expert
  *   is added with weight 1.
- * Every sum is a plain sequential loop in double precision.
+ * Every sum is a plain sequential loop in double precision.  Independent
+ * output rows (router logits, expert rows) may run on several threads
+ * (OpenMP, or_set_threads); each row's sum is the same sequential loop, so
+ * results do not depend on the thread count.
  *
  * Parity pins: see tests/test_oracle.py (hand-worked cases, closed forms,
  * identities, brute force).  No function here is "parity unpinned".
  */
 #include <math.h>
+#include <omp.h>
 #include <stddef.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -35,6 +39,11 @@
 typedef struct {
   int32_t H, I, E, K, bits, group, has_shared;
 } or_dims;
+
+/* Threads used for independent output rows (1 = fully sequential). */
+static int or_threads = 1;
+void or_set_threads(int n) { or_threads = n < 1 ? 1 : n; }
+int or_get_threads(void) { return or_threads; }
 
 /* ---- bf16 ---------------------------------------------------------------- */
 
@@ -170,6 +179,7 @@ void or_dequant_matrix_f32(const or_dims *d, const uint8_t *blob, int which, flo
 /* Router logits of one token: l[e] = sum_c R[e][c] * x[c]. */
 void or_router_logits(const or_dims *d, const uint16_t *router, const uint16_t *x,
                       double *logits) {
+#pragma omp parallel for schedule(static) num_threads(or_threads)
   for (int64_t e = 0; e < d->E; ++e) {
     double acc = 0.0;
     for (int64_t c = 0; c < d->H; ++c)
@@ -251,12 +261,14 @@ void or_expert(const or_dims *d, const uint8_t *blob, const double *x, double *y
   const or_mat gate = or_matrix(d, blob, 0), up = or_matrix(d, blob, 1),
                down = or_matrix(d, blob, 2);
   double *h = (double *)malloc(sizeof(double) * I);
+#pragma omp parallel for schedule(static) num_threads(or_threads)
   for (int64_t r = 0; r < I; ++r) {
     double g = 0.0, u = 0.0;
     for (int64_t c = 0; c < H; ++c) g += or_mat_dequant(&gate, r, c) * x[c];
     for (int64_t c = 0; c < H; ++c) u += or_mat_dequant(&up, r, c) * x[c];
     h[r] = or_silu(g) * u;
   }
+#pragma omp parallel for schedule(static) num_threads(or_threads)
   for (int64_t j = 0; j < H; ++j) {
     double acc = 0.0;
     for (int64_t r = 0; r < I; ++r) acc += or_mat_dequant(&down, j, r) * h[r];

@@ -54,8 +54,9 @@ CENTRED_Z = (-0.08 - 7.5 * 0.0125, 0.08 - 7.5 * 0.0125)
 WORKLOADS = {
     "tiny": Workload("tiny", 4096, 1024, 16, 4, 4, 1, 1, 1, 1000, 1000,
                      description="one layer, 16 experts, 1 token"),
-    "layer": Workload("layer", 4096, 1024, 512, 4, 4, 1, 1, 1, 1001, 1001,
-                      description="one full layer, 512 experts, 1 token"),
+    "layer": Workload("layer", 4096, 1024, 512, 4, 4, 1, 1, 128, 1001, 1001,
+                      description="one full layer, 512 experts, 1 token per call, 128 "
+                                  "distinct tokens"),
     "stack60": Workload("stack60", 4096, 1024, 512, 4, 4, 60, 1, 128, 1002, 1002, rho=STACK_RHO,
                         description="60 HBM-resident layers x 512 4-bit experts, "
                                     "128 consecutive decode tokens"),

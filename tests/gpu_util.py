@@ -2,6 +2,8 @@
 of its exact bytes for the oracle, and the parity comparisons."""
 from __future__ import annotations
 
+import os
+
 import numpy as np
 
 import bit_dequant_expert_moe_amd as moe
@@ -9,6 +11,9 @@ import oracle
 import synth
 
 SHARED_ID = 0xFFFF  # generator expert index used for the shared expert
+
+# the oracle's output rows on the host cores (same results for any count)
+oracle.set_threads(min(16, os.cpu_count() or 1))
 
 # Near-tie margin for routing: the fp32 router sums 4096 exact bf16 products
 # per logit; with |W| ~ 0.02 and |x| ~ 1 the worst-case rounding bound is

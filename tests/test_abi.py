@@ -143,6 +143,11 @@ def test_dequantize_and_misc_validation():
     assert _status(moe.moe_dequantize, d=D, blob=A, which=3, out=A, stream=0) == -2
     assert _status(moe.moe_dequantize, d=D, blob=A + 16, which=0, out=A, stream=0) == -4
     assert _status(moe.moe_dequantize, d=D, blob=None, which=0, out=A, stream=0) == -1
+    f = moe.moe_dequantize_as
+    assert _status(f, d=D, blob=A, which=0, decoder=5, out=A, stream=0) == -2
+    assert _status(f, d=D, blob=A, which=0, decoder=-1, out=A, stream=0) == -2
+    assert _status(f, d=D, blob=A, which=-1, decoder=0, out=A, stream=0) == -2
+    assert _status(f, d=D, blob=A, which=0, decoder=0, out=A + 4, stream=0) == -4
     assert _status(moe.moe_workspace_init, ws=None, ws_bytes=256, stream=0) == -1
     assert _status(moe.moe_workspace_init, ws=WS, ws_bytes=16, stream=0) == -5
     assert moe.lib().moe_get_device_error(None, None, ctypes.byref(ctypes.c_int32())) == -1

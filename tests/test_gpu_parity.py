@@ -45,32 +45,47 @@ def test_device_generator_matches_host(bits):
     np.testing.assert_array_equal(L.shared_host(), synth.blob_host(L.params, 0, gu.SHARED_ID))
 
 
-def _dequant_dev(L, blob_dev, which):
+DECODERS = [("scalar", moe.DEQ_SCALAR), ("fp16 pair", moe.DEQ_FP16_PAIR),
+            ("fp8 pair", moe.DEQ_FP8_PAIR), ("bf16 pair", moe.DEQ_BF16_PAIR),
+            ("bf16 slice", moe.DEQ_BF16_SLICE)]
+
+
+def _dequant_dev(L, blob_dev, which, decoder=None):
     rows, cols = (L.dims.hidden, L.dims.inter) if which == 2 else (L.dims.inter, L.dims.hidden)
-    out = torch.empty((rows, cols), dtype=torch.float32, device="cuda")
-    moe.moe_dequantize(L.dims, blob_dev, which, out)
+    out = torch.full((rows, cols), float("nan"), dtype=torch.float32, device="cuda")
+    if decoder is None:
+        moe.moe_dequantize(L.dims, blob_dev, which, out)
+    else:
+        moe.moe_dequantize_as(L.dims, blob_dev, which, decoder, out)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
 
 @pytest.mark.parametrize("shape", [(4096, 1024, 4), (4096, 1024, 2), (256, 512, 4), (1024, 256, 2)])
 def test_dequantize_bit_exact(shape):
+    # every decoder the kernels use (the unpack function each kernel calls),
+    # on every matrix, against the oracle's one rounding of s q + z
     H, I, bits = shape
     _say("dequant", shape)
     L = gu.DeviceLayer(H, I, 3, 2, bits=bits, seed=7)
     for e in [0, 2]:
         blob_dev = L.experts[e * L.stride:]
         for which in range(3):
+            want = oracle.dequant_matrix_f32(L.od, L.blob_host(e), which).view(np.uint32)
             got = _dequant_dev(L, blob_dev, which)
-            want = oracle.dequant_matrix_f32(L.od, L.blob_host(e), which)
-            np.testing.assert_array_equal(got.view(np.uint32), want.view(np.uint32))
+            np.testing.assert_array_equal(got.view(np.uint32), want)
+            for name, dec in DECODERS:
+                got = _dequant_dev(L, blob_dev, which, dec)
+                np.testing.assert_array_equal(got.view(np.uint32), want,
+                                              err_msg="%s, matrix %d" % (name, which))
 
 
 def test_dequantize_shared_tiny(tiny):
     for which in range(3):
-        got = _dequant_dev(tiny, tiny.shared, which)
-        want = oracle.dequant_matrix_f32(tiny.od, tiny.shared_host(), which)
-        np.testing.assert_array_equal(got.view(np.uint32), want.view(np.uint32))
+        want = oracle.dequant_matrix_f32(tiny.od, tiny.shared_host(), which).view(np.uint32)
+        for name, dec in DECODERS:
+            got = _dequant_dev(tiny, tiny.shared, which, dec)
+            np.testing.assert_array_equal(got.view(np.uint32), want, err_msg=name)
 
 
 # ---- routing ------------------------------------------------------------------
@@ -196,6 +211,33 @@ def test_expert_forward_given_ids_and_invalid_id(tiny):
     y_o = oracle.expert_forward(L.od, L.blob_host, L.shared_host(), x, ids,
                                 w.astype(np.float64))
     assert gu.max_rel_err(y.cpu().numpy(), y_o) <= gu.Y_TOL
+
+
+def test_expert_forward_repeated_ids_large_bucket(full):
+    # the grouped path with a token that names one expert in three slots:
+    # 2048 tokens x 3 slots put 6144 pairs (384 chunks of 16) in one bucket,
+    # beyond what an 8-bit chunk field of a work item could index
+    L = full
+    T = 2048
+    x = synth.tokens(1021, 0, T, 4096)
+    rng = np.random.default_rng(5)
+    ids = np.empty((T, 4), np.int32)
+    ids[:, :3] = 5
+    ids[:, 3] = rng.integers(0, 512, T)
+    w = rng.dirichlet(np.ones(4), T).astype(np.float32)
+    ws = moe.alloc_workspace(L.dims, T)
+    y = torch.empty((T, 4096), dtype=torch.float32, device="cuda")
+    moe.moe_expert_forward(L.dims, L.L, L.x_dev(x), T, torch.from_numpy(ids).cuda(),
+                           torch.from_numpy(w).cuda(), y, ws)
+    torch.cuda.synchronize()
+    assert moe.moe_get_device_error(ws) == 0
+    yh = y.cpu().numpy()
+    for t in (0, 1, 777, 2047):
+        y_o = oracle.expert_forward(L.od, L.blob_host, L.shared_host(), x[t:t + 1],
+                                    ids[t:t + 1], w[t:t + 1].astype(np.float64))
+        err = gu.max_rel_err(yh[t], y_o)
+        _say("  repeated ids, token %d: max|dy|/max|y| = %.2e" % (t, err))
+        assert err <= gu.Y_TOL
 
 
 # ---- invariants ---------------------------------------------------------------------

@@ -1,10 +1,12 @@
 """GPU checks of the off-HBM expert tier through the C ABI: experts in pinned
-host memory, a few device slots (so that calls evict), and every output
-bitwise equal to moe_route + moe_expert_forward over the same experts held
-in device memory."""
+host memory, a few device slots (so that calls evict), every output bitwise
+equal to moe_route + moe_expert_forward over the same experts held in device
+memory, and sampled calls against the float64 oracle (routing exact away
+from near-ties, y within 2e-3 max|y|, teacher-forced on the tier's routing)."""
 import numpy as np
 import pytest
 
+import oracle
 import synth
 from tests import gpu_util as gu
 
@@ -54,6 +56,7 @@ def test_tier_equals_resident(bits, T, n_slots):
     _say("tier bits %d T %d slots %d" % (bits, T, n_slots))
     layers, host, tier, keep = _setup(bits, 3, n_slots, T)
     d = layers[0].dims
+    blob_b = moe.moe_expert_bytes(d)
     wsb = moe.moe_tier_workspace_bytes(d, n_slots, T)
     ws = _aligned(wsb, "cuda")
     moe.moe_workspace_init(ws, wsb)
@@ -78,6 +81,22 @@ def test_tier_equals_resident(bits, T, n_slots):
             np.testing.assert_array_equal(w.cpu().numpy(), w_r.cpu().numpy())
             np.testing.assert_array_equal(y.cpu().numpy(), y_r.cpu().numpy())
             n_valid += len({(int(e)) for e in ids.cpu().numpy().reshape(-1)})
+            if t in (1, ntok - 1):
+                # the oracle on the bytes the tier copied from host memory:
+                # routing from x, y teacher-forced on the tier's choice
+                xh = x_all[t * T:(t + 1) * T]
+                ids_h, w_h, y_h = ids.cpu().numpy(), w.cpu().numpy(), y.cpu().numpy()
+                _, _, logits_o, gap_o = oracle.route(L.od, L.router_h, xh)
+                gu.check_routing(L.od, ids_h, w_h, logits_o, gap_o, 4)
+                wf = np.empty((T, 4))
+                for tt in range(T):
+                    sel = logits_o[tt][ids_h[tt]]
+                    wf[tt] = np.exp(sel - sel.max()) / np.exp(sel - sel.max()).sum()
+                blob_of = (lambda e, l=l: host[l][e * blob_b:(e + 1) * blob_b].numpy())
+                y_o = oracle.expert_forward(L.od, blob_of, L.shared_host(), xh, ids_h, wf)
+                err = gu.max_rel_err(y_h, y_o)
+                _say("  token %d layer %d: max|dy|/max|y| = %.2e (oracle)" % (t, l, err))
+                assert err <= gu.Y_TOL
     assert moe.moe_get_device_error(ws) == 0
     st = tier.stats()
     _say("  stats", st)

@@ -502,3 +502,19 @@ def test_residual_layer_with_zero_experts_keeps_the_residual():
     r_out, _, y, _, _, _, _ = oracle.residual_layer(d, router, {e: zero for e in range(8)}, zero, r)
     assert np.all(y == 0.0)
     np.testing.assert_array_equal(r_out, r.astype(np.float64))
+
+
+def test_threads_do_not_change_results():
+    # output rows on several threads: every row is the same sequential sum
+    d, router, blobs, shared, x = _layer_inputs(E=8, K=4, T=2)
+    try:
+        oracle.set_threads(1)
+        y1, ids1, w1, l1, g1 = oracle.layer(d, router, blobs, shared, x)
+        oracle.set_threads(4)
+        assert oracle.get_threads() == 4
+        y4, ids4, w4, l4, g4 = oracle.layer(d, router, blobs, shared, x)
+    finally:
+        oracle.set_threads(1)
+    np.testing.assert_array_equal(y1, y4)
+    np.testing.assert_array_equal(l1, l4)
+    np.testing.assert_array_equal(ids1, ids4)
