@@ -48,6 +48,11 @@ def parse():
                     help="layers of token 0 checked against the oracle (the parity gate)")
     ap.add_argument("--reps", type=int, default=5,
                     help="repetitions of the timed region for the spread")
+    ap.add_argument("--per-layer", action="store_true",
+                    help="one moe_layer_decode call per layer instead of one multi-layer call "
+                         "per token")
+    ap.add_argument("--compare-paths", type=int, default=1,
+                    help="also time the other path on a few tokens (0: skip)")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB megabytes (calibrates the HBM "
                          "byte counters of the profiler) and exit")
@@ -55,6 +60,8 @@ def parse():
 
 
 KERNEL_SOURCES = ["bit_dequant_expert_moe_amd/csrc/moe_fused.hip",
+                  "bit_dequant_expert_moe_amd/csrc/moe_stack.hip",
+                  "bit_dequant_expert_moe_amd/csrc/moe_fused_dev.h",
                   "bit_dequant_expert_moe_amd/csrc/moe_device.h",
                   "bit_dequant_expert_moe_amd/csrc/moe_internal.h"]
 
@@ -167,6 +174,9 @@ def main():
     log("resident: %d layers x %d experts (%.1f GB) in %.1fs" % (
         nl, wl.E, nl * (wl.E + 1) * blob / 1e9, time.time() - t0))
 
+    layer_arr = moe.layer_array(layers_c)
+    stack_path = not args.per_layer
+
     def call_layer(t, l, sp_):
         if chain:
             moe.moe_layer_decode_residual(dims, layers_c[l], r[t], 1, x[t, l], y[t, l],
@@ -175,27 +185,44 @@ def main():
             moe.moe_layer_decode(dims, layers_c[l], x[t, l], 1, y[t, l], ids[t, l], wts[t, l],
                                  ws, ws_bytes, sp_)
 
-    def enqueue_token(t, sp_):
+    def call_token(t, sp_, stack):
+        # the token's layers: one multi-layer call, or one call per layer
+        if stack:
+            if chain:
+                moe.moe_stack_decode_residual(dims, layer_arr, r[t], x[t], y[t], ids[t], wts[t],
+                                              ws, ws_bytes, sp_)
+            else:
+                moe.moe_stack_decode(dims, layer_arr, x[t], y[t], ids[t], wts[t], ws, ws_bytes,
+                                     sp_)
+        else:
+            for l in range(nl):
+                call_layer(t, l, sp_)
+
+    def enqueue_token(t, sp_, stack=stack_path):
         # on the chain, the token's residual is restored first (a 16 KB device
         # copy on torch's current stream, inside the step)
         if chain:
             r[t].copy_(r0[t])
-        for l in range(nl):
-            call_layer(t, l, sp_)
+        call_token(t, sp_, stack)
+
+    def capture(n, stack):
+        gs = []
+        cs = torch.cuda.Stream()
+        with torch.cuda.stream(cs):
+            for t in range(n):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cs):
+                    enqueue_token(t, torch.cuda.current_stream().cuda_stream, stack)
+                gs.append(g)
+        torch.cuda.synchronize()
+        return gs
 
     # ---- one graph per token ------------------------------------------------
     enqueue_token(0, sp)  # eager run first (also checks the path)
     torch.cuda.synchronize()
-    graphs = []
-    cs = torch.cuda.Stream()
-    with torch.cuda.stream(cs):
-        for t in range(ntok):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=cs):
-                enqueue_token(t, torch.cuda.current_stream().cuda_stream)
-            graphs.append(g)
-    torch.cuda.synchronize()
-    log("captured %d token graphs of %d layers" % (ntok, nl))
+    graphs = capture(ntok, stack_path)
+    log("captured %d token graphs of %d layers (%s)" % (
+        ntok, nl, "one multi-layer call" if stack_path else "one call per layer"))
 
     for i in range(args.warmup):
         graphs[i % ntok].replay()
@@ -239,36 +266,77 @@ def main():
     log("tok/s over %d repetitions: median %.1f, p10 %.1f, p90 %.1f" % (
         args.reps, reps["median"], reps["p10"], reps["p90"]))
 
-    # ---- per-launch duration of the layer call ---------------------------------
-    # On the single-token path one moe_layer_decode is one kernel (k_layer1) and
-    # a token graph is nl of them back to back, so the timed region above (HIP
-    # events on the replay stream) divided by the launches it holds is the
-    # average launch duration.  An isolated launch (events around each call)
-    # is reported beside it: the events themselves add a gap per launch.
+    # ---- per-launch duration of the dominant kernel ------------------------------
+    # Multi-layer path: a token graph is one k_stack launch (plus, on the chain,
+    # the 16 KB restore of the token's residual); per-layer path: nl k_layer1
+    # launches back to back.  The timed region above (HIP events on the replay
+    # stream) divided by the launches it holds is the average launch duration.
+    # Launches between their own events are reported beside it (the events add
+    # a gap per launch).
     fused = os.environ.get("MOE_DISABLE_FUSED", "0") != "1"
+    layer_bytes = router_bytes_tok // nl + (wl.K + wl.has_shared) * blob
     layer_us = ms_per_step * 1e3 / nl
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(nl)]
     t_tok = 1 % ntok
-    torch.cuda._sleep(100_000_000)
-    for l in range(nl):
-        ev[l][0].record()
-        call_layer(t_tok, l, sp)
-        ev[l][1].record()
-    torch.cuda.synchronize()
-    iso_us = float(np.mean([ev[l][0].elapsed_time(ev[l][1]) * 1e3 for l in range(nl)]))
-    launch_bytes = router_bytes_tok // nl + (wl.K + wl.has_shared) * blob
-    achieved = launch_bytes / (layer_us * 1e-6) / 1e9
-    log("layer call %.2f us/launch in the token graphs (%.2f us isolated) -> %.0f GB/s of "
-        "algorithmic bytes (%d B per launch)" % (layer_us, iso_us, achieved, launch_bytes))
-    traffic = measured_traffic("k_layer1_%s" % wl.name) if fused else None
+    if stack_path:
+        launch_us = ms_per_step * 1e3
+        launch_bytes = nl * layer_bytes
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(8)]
+        for i in range(8):
+            ev[i][0].record()
+            call_token((t_tok + i) % ntok, sp, True)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        iso_us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
+        kname = "k_stack_%s" % wl.name
+    else:
+        launch_us = layer_us
+        launch_bytes = layer_bytes
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(nl)]
+        torch.cuda._sleep(100_000_000)
+        for l in range(nl):
+            ev[l][0].record()
+            call_layer(t_tok, l, sp)
+            ev[l][1].record()
+        torch.cuda.synchronize()
+        iso_us = float(np.mean([ev[l][0].elapsed_time(ev[l][1]) * 1e3 for l in range(nl)]))
+        kname = "k_layer1_%s" % wl.name
+    achieved = launch_bytes / (launch_us * 1e-6) / 1e9
+    log("%s: %.2f us per launch in the token graphs (%.2f us between events), %.2f us per "
+        "layer -> %.0f GB/s of algorithmic bytes (%d B per launch)" % (
+            "k_stack" if stack_path else "k_layer1", launch_us, iso_us, layer_us, achieved,
+            launch_bytes))
+    traffic = measured_traffic(kname) if fused else None
     err = moe.moe_get_device_error(ws, sp)
     if err:
         log("device error flags: %d" % err)
 
+    # ---- the other path, for comparison (a few tokens) -------------------------
+    other = None
+    if fused and args.compare_paths:
+        nt = min(16, ntok)
+        g2 = capture(nt, not stack_path)
+        for i in range(4):
+            g2[i % nt].replay()
+        e0.record()
+        for i in range(4 * nt):
+            g2[i % nt].replay()
+        e1.record()
+        torch.cuda.synchronize()
+        o_ms = e0.elapsed_time(e1) / (4 * nt)
+        other = {"path": "one call per layer" if stack_path else "one multi-layer call",
+                 "tokens_per_s": 1000.0 / o_ms, "us_per_layer": o_ms * 1e3 / nl}
+        del g2
+        log("the other path (%s): %.1f tok/s, %.2f us per layer" % (
+            other["path"], other["tokens_per_s"], other["us_per_layer"]))
+        graphs[0].replay()
+        torch.cuda.synchronize()
+
     # ---- measured streaming-read rate at the layer's and the token's size -----
-    stream = stream_read_rates(torch, moe, experts, launch_bytes, nl * launch_bytes, sp)
-    stream["layer_call_frac_of_layer_size_rate"] = achieved / stream["layer_size_back_to_back_GBps"]
+    stream = stream_read_rates(torch, moe, experts, layer_bytes, nl * layer_bytes, sp)
+    stream["layer_frac_of_layer_size_rate"] = (layer_bytes / (layer_us * 1e-6) / 1e9 /
+                                               stream["layer_size_back_to_back_GBps"])
     stream["token_frac_of_token_size_rate"] = (
         (expert_bytes_tok + router_bytes_tok) * tok_s / 1e9 / stream["token_size_single_launch_GBps"])
     log("stream read: %.0f GB/s per launch of %d B back to back (%.0f GB/s isolated), "
@@ -315,14 +383,18 @@ def main():
         "layers_per_s": tok_s * nl,
         "repetitions": dict(reps, unit="tokens/s", n=args.reps, steps_each=args.steps),
         "roofline": {"bound": "hbm",
-                     "kernel": ("k_layer1 (moe_layer_decode_residual)" if chain else
-                                "k_layer1 (moe_layer_decode)") if fused else
+                     "kernel": (("k_stack (moe_stack_decode_residual)" if chain else
+                                 "k_stack (moe_stack_decode)") if stack_path else
+                                ("k_layer1 (moe_layer_decode_residual)" if chain else
+                                 "k_layer1 (moe_layer_decode)")) if fused else
                                "moe_layer_decode (k_route + k_gateup + k_down)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic["traffic_bytes_per_launch"] if traffic else None,
-                     "avg_launch_us": layer_us, "isolated_launch_us": iso_us,
-                     "bytes_per_launch": launch_bytes},
+                     "avg_launch_us": launch_us, "between_events_launch_us": iso_us,
+                     "bytes_per_launch": launch_bytes, "us_per_layer": layer_us,
+                     "layers_per_launch": nl if stack_path else 1},
+        "other_path": other,
         "stream_read": stream,
         "device_error_flags": err,
         "parity": check,
@@ -499,8 +571,8 @@ def cpu_baseline(oracle, od, wl, nl, n_single, experts, shared, routers_h, x_h, 
 
 def bench_layer(args, wl):
     """One full 512-expert layer, one token per call, with the last-level cache
-    flushed (512 MB of stores) before every call: the call's events exclude
-    the flush.  128 distinct tokens (independent activations, so distinct
+    flushed (512 MB of stores, then 512 MB of reads of other memory) before
+    every call: the call's events exclude the flush.  128 distinct tokens (independent activations, so distinct
     routings), cycled.  value = calls per second from the summed call times."""
     import torch
     import bit_dequant_expert_moe_amd as moe
@@ -530,17 +602,29 @@ def bench_layer(args, wl):
     wsb = ws.numel()
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
 
+    clean = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    clean.fill_(7)
+    sink = torch.empty(moe.moe_stream_read_sink_words(clean.numel()), dtype=torch.int32,
+                       device=dev)
+
     def call(t):
         moe.moe_layer_decode(dims, L, x[t], 1, y[t], ids[t], wts[t], ws, wsb, sp)
 
-    for i in range(args.warmup):
+    def flush_caches():
+        # 512 MB of stores, then a 512 MB read of other memory, so that the
+        # cache holds clean unrelated lines (no write-back of the flush's own
+        # lines inside the timed call)
         moe.moe_flush(flush, flush.numel(), sp)
+        moe.moe_stream_read(clean, clean.numel(), sink, sp)
+
+    for i in range(args.warmup):
+        flush_caches()
         call(i % ntok)
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     for i in range(args.steps):
-        moe.moe_flush(flush, flush.numel(), sp)
+        flush_caches()
         evs[i][0].record()
         call(i % ntok)
         evs[i][1].record()

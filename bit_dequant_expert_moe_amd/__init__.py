@@ -28,7 +28,8 @@ EXPORTS = ("moe_abi_version", "moe_status_str", "moe_check_dims", "moe_expert_by
            "moe_dequantize", "moe_dequantize_as", "moe_get_device_error", "moe_tier_staging_bytes",
            "moe_tier_device_bytes", "moe_tier_workspace_bytes", "moe_tier_create",
            "moe_tier_decode", "moe_tier_plan", "moe_tier_stats", "moe_tier_destroy",
-           "moe_stream_read_sink_words", "moe_stream_read", "moe_flush")
+           "moe_stream_read_sink_words", "moe_stream_read", "moe_flush", "moe_stack_decode",
+           "moe_stack_decode_residual")
 
 
 class MoeError(RuntimeError):
@@ -108,6 +109,8 @@ def lib() -> ctypes.CDLL:
             "moe_stream_read_sink_words": (sz, [sz]),
             "moe_stream_read": (i32, [vp, sz, vp, vp]),
             "moe_flush": (i32, [vp, sz, vp]),
+            "moe_stack_decode": (i32, [dp, lp, i32, vp, vp, vp, vp, vp, sz, vp]),
+            "moe_stack_decode_residual": (i32, [dp, lp, i32, vp, vp, vp, vp, vp, vp, sz, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -223,6 +226,38 @@ def moe_layer_decode_residual(d: Dims, layer: moe_layer, resid, T: int, x_out=No
                                          ws_bytes if ws_bytes is not None else ws.numel(),
                                          _stream(stream))
     _check(rc, "moe_layer_decode_residual")
+
+
+def layer_array(layers) -> ctypes.Array:
+    """A host array of moe_layer descriptors (keep it alive while in use)."""
+    return (moe_layer * len(layers))(*layers)
+
+
+def _layers(layers):
+    return layers if isinstance(layers, ctypes.Array) else layer_array(layers)
+
+
+def moe_stack_decode(d: Dims, layers, x, y, ids=None, w=None, ws=None, ws_bytes=None,
+                     stream=None):
+    """len(layers) consecutive layers of one token: x bf16 [L][H] -> y fp32
+    [L][H] (ids/w [L][K] optional)."""
+    arr = _layers(layers)
+    rc = lib().moe_stack_decode(ctypes.byref(d.c()), arr, len(arr), _ptr(x), _ptr(y), _ptr(ids),
+                                _ptr(w), _ptr(ws),
+                                ws_bytes if ws_bytes is not None else ws.numel(), _stream(stream))
+    _check(rc, "moe_stack_decode")
+
+
+def moe_stack_decode_residual(d: Dims, layers, resid, x_out=None, y=None, ids=None, w=None,
+                              ws=None, ws_bytes=None, stream=None):
+    """len(layers) consecutive layers of one token on the residual stream
+    resid fp32 [H] (updated in place)."""
+    arr = _layers(layers)
+    rc = lib().moe_stack_decode_residual(ctypes.byref(d.c()), arr, len(arr), _ptr(resid),
+                                         _ptr(x_out), _ptr(y), _ptr(ids), _ptr(w), _ptr(ws),
+                                         ws_bytes if ws_bytes is not None else ws.numel(),
+                                         _stream(stream))
+    _check(rc, "moe_stack_decode_residual")
 
 
 def moe_dequantize(d: Dims, blob, which: int, out, stream=None):

@@ -76,116 +76,13 @@
 #include <stdint.h>
 
 #include "moe_device.h"
+#include "moe_fused_dev.h"
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
 using namespace dev;
-
-constexpr int kG = 256;          // workgroups
-constexpr int kGuWaves = 4;      // gate/up waves 0..3
-constexpr int kDownWaves = 4;    // down waves 4..7 (wave 4 runs the exchange)
-constexpr int kNT = 64 * (kGuWaves + kDownWaves);
-constexpr long kSpinMax = 1L << 18;
-constexpr float kRmsEps = 1e-6f;  // epsilon of the pre-MoE RMS norm
-
-typedef __attribute__((address_space(3))) volatile uint32_t lds_u32;
-
-__device__ __forceinline__ lds_u32 *lds(uint32_t *p) { return (lds_u32 *)(p); }
-
-// Ordering of LDS accesses between waves of the workgroup only: these wait
-// for outstanding LDS operations, never for global loads.
-__device__ __forceinline__ void lds_release() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-}
-__device__ __forceinline__ void lds_acquire() {
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-// Bounded wait until an LDS word written by another wave reaches `want`.
-__device__ __forceinline__ void wait_lds(uint32_t *p, uint32_t want) {
-  long spins = 0;
-  while (*lds(p) < want) {
-    if (++spins > (kSpinMax << 4)) break;
-    __builtin_amdgcn_s_sleep(1);
-  }
-  lds_acquire();
-}
-
-__device__ __forceinline__ uint32_t ld_rlx(const uint32_t *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// 16-byte coherent load (buffer_load_dwordx4 with the sc1 policy, the same
-// policy as an agent-scope relaxed atomic load), coalesced across the wave.
-__device__ __forceinline__ uint4 ld_coh16(const void *base, uint32_t byte_off) {
-  const __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, 0x7fffffff, 0x00020000);
-  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 16 /* sc1 */);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
-
-// 8-byte coherent load, the same policy.
-__device__ __forceinline__ uint2 ld_coh8(const void *base, uint32_t byte_off) {
-  const __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, 0x7fffffff, 0x00020000);
-  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)byte_off, 0, 16 /* sc1 */);
-  return make_uint2(v[0], v[1]);
-}
-
-// Weight loads through a buffer resource of the blob: the per-lane byte
-// offsets are the same 32-bit values for every expert, only the (scalar)
-// resource changes, which keeps 64-bit address arithmetic out of the vector
-// registers.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t blob_rsrc(const uint8_t *base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), 0, 0x7fffffff, 0x00020000);
-}
-__device__ __forceinline__ uint4 bld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
-__device__ __forceinline__ uint2 bld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
-  return make_uint2(v[0], v[1]);
-}
-__device__ __forceinline__ uint32_t bld4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
-}
-
-template <int BITS, int H, int I, int K>
-struct Geo {
-  static constexpr int COLS = 128 / BITS;           // columns per 16-byte segment
-  static constexpr int PAIRS = COLS / 2;            // packed x pairs per segment
-  static constexpr int SEG_X = H * BITS / 128;      // segments per gate/up row
-  static constexpr int LSEG = SEG_X / 64;           // segments per lane per gate/up row
-  static constexpr int XLD = COLS * 2 / 16;         // 16-byte x loads per segment
-  static constexpr int RCH = H / 8;                 // 16-byte chunks per router row
-  static constexpr int RXC = RCH / kNT;             // router x chunks per thread
-  static constexpr int GU_ROWS = I / kG;            // gate/up rows per workgroup and slot
-  static constexpr int DCOLS = 32;                  // down codes per lane (one load)
-  static constexpr int DWORDS = DCOLS * BITS / 32;  // their code words (4 or 2)
-  static constexpr int LPR = I / DCOLS;             // lanes per down row
-  static constexpr int RPL = 64 / LPR;              // down rows per wave-wide load
-  static constexpr int NSEGD = 1;
-  static constexpr int D_ROWS = H / kG;             // down rows per workgroup
-  static constexpr int D_ROWS_W = D_ROWS / kDownWaves;  // per down wave
-  static constexpr int DLD = D_ROWS_W / RPL;        // down loads per lane per slot
-  static_assert(LSEG >= 1 && SEG_X % 64 == 0, "gate/up row must span a wave");
-  static_assert(GU_ROWS == kGuWaves, "one gate/up row per gate/up wave and slot");
-  static_assert(LPR <= 64 && 64 % LPR == 0, "a down row within one wave");
-  static_assert(DLD >= 1 && D_ROWS_W % RPL == 0, "down rows must tile the waves");
-  static_assert(RXC >= 1 && RCH % kNT == 0, "router row must span the workgroup");
-  static_assert(SEG_X <= 64 * kGuWaves, "one x segment per gate/up thread");
-  // the down rows of each routed slot are split over OWN_WG workgroups
-  static constexpr int OWN_WG = kG / K;             // workgroups per routed slot
-  static constexpr int O_ROWS = H / OWN_WG;         // routed down rows per workgroup
-  static constexpr int O_ROWS_W = O_ROWS / kDownWaves;  // per down wave
-  static constexpr int RDLD = O_ROWS_W / RPL;       // routed down loads per lane
-  static_assert(kG % K == 0 && H % OWN_WG == 0, "routed rows must tile the workgroups");
-  static_assert(RDLD >= 1 && O_ROWS_W % RPL == 0 && O_ROWS_W <= 64, "routed rows per wave");
-  static_assert(K * D_ROWS == 64, "one routed sum per lane of the exchange wave");
-};
 
 struct FusedArgs {
   const uint16_t *x, *router;
@@ -206,139 +103,6 @@ struct FusedArgs {
   int E, has_shared;
   int64_t off_gq, off_uq, off_dq, off_gsb, off_usb, off_dsb;
 };
-
-// Value of code 1 read as an fp8 bit pattern.  A masked code byte (0..15)
-// is an fp8 subnormal or the smallest normals, so its fp8 value is exactly
-// the code times this power of two (2^-9 for e4m3, 2^-10 for its FNUZ form).
-__device__ __forceinline__ float fp8_code_unit() {
-  return __builtin_amdgcn_cvt_pk_f32_fp8(1, false)[0];
-}
-
-// The codes of one 32-bit word of a down row as fp32 values u q_c, in column
-// order (8 at 4 bits, 16 at 2 bits), u = fp8_code_unit().  m is the per-byte
-// code mask (0x0F0F0F0F or 0x03030303) in a register the compiler cannot see
-// through.  Each masked word converts two codes per instruction
-// (v_cvt_pk_f32_fp8 on its low and high half): at 4 bits the masked word
-// holds codes (0, 2, 4, 6) and the word shifted by 4 codes (1, 3, 5, 7); at
-// 2 bits the word shifted by 2k holds codes (k, 4 + k, 8 + k, 12 + k).
-// This is the unpack of the single-token down products (word_dot_f32); the
-// dequantisation hook (moe_dequantize_as) calls it too.
-template <int BITS>
-__device__ __forceinline__ void fp8_word_codes(uint32_t u, uint32_t m, float (&q)[32 / BITS]) {
-  if (BITS == 4) {
-    const uint32_t lo = u & m, hi = (u >> 4) & m;
-    const auto l0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
-    const auto l1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
-    const auto h0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
-    const auto h1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
-    q[0] = l0[0];
-    q[1] = h0[0];
-    q[2] = l0[1];
-    q[3] = h0[1];
-    q[4] = l1[0];
-    q[5] = h1[0];
-    q[6] = l1[1];
-    q[7] = h1[1];
-  } else {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t mk = (u >> (2 * k)) & m;
-      const auto c0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)mk, false);
-      const auto c1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)mk, true);
-      q[k] = c0[0];
-      q[4 + k] = c0[1];
-      q[8 + k] = c1[0];
-      q[12 + k] = c1[1];
-    }
-  }
-}
-
-// u sum_c q_c h_c over the codes of one 32-bit word of a down row, fp32; hv
-// holds the word's activations.  The products are summed in the order the
-// conversions produce them (column order at 4 bits; k-major at 2 bits); u is
-// a power of two, so the sum is exactly u times the one formed from integer
-// codes.
-template <int BITS>
-__device__ __forceinline__ float word_dot_f32(uint32_t u, const float *hv, float acc, uint32_t m) {
-  float q[32 / BITS];
-  fp8_word_codes<BITS>(u, m, q);
-  if (BITS == 4) {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) acc = fmaf(q[c], hv[c], acc);
-  } else {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      acc = fmaf(q[k], hv[k], acc);
-      acc = fmaf(q[4 + k], hv[4 + k], acc);
-      acc = fmaf(q[8 + k], hv[8 + k], acc);
-      acc = fmaf(q[12 + k], hv[12 + k], acc);
-    }
-  }
-  return acc;
-}
-
-// Lane partial sums of N down rows, one code load per row and lane, against
-// the activations of the lane's DCOLS columns (hb, in LDS):
-// acc += wk (s sum_c q_c h_c + z sum_c h_c) with the row's group scale s and
-// bias z.  One code word's activations are read from LDS at a time.
-template <int BITS, int N, int DWORDS, int DCOLS>
-__device__ __forceinline__ void down_rows(const uint4 (&dq)[N], const uint32_t (&dsb)[N],
-                                          const float *hb, float wk, float (&acc)[N]) {
-  constexpr int CPW = 32 / BITS;  // codes per word
-  uint32_t m = BITS == 4 ? 0x0F0F0F0Fu : 0x03030303u;
-  asm volatile("" : "+s"(m));
-  static_assert(CPW * DWORDS == DCOLS, "the lane's codes fill its words");
-  float q[N];
-#pragma unroll
-  for (int ld = 0; ld < N; ++ld) q[ld] = 0.f;
-  float Hs = 0.f;
-#pragma unroll
-  for (int wd = 0; wd < DWORDS; ++wd) {
-    float hv[CPW];
-#pragma unroll
-    for (int t = 0; t < CPW / 4; ++t) {
-      const float4 v = *reinterpret_cast<const float4 *>(hb + CPW * wd + 4 * t);
-      hv[4 * t] = v.x;
-      hv[4 * t + 1] = v.y;
-      hv[4 * t + 2] = v.z;
-      hv[4 * t + 3] = v.w;
-    }
-#pragma unroll
-    for (int c = 0; c < CPW; ++c) Hs += hv[c];
-#pragma unroll
-    for (int ld = 0; ld < N; ++ld) {
-      const uint4 c4 = dq[ld];
-      const uint32_t u = wd == 0 ? c4.x : wd == 1 ? c4.y : wd == 2 ? c4.z : c4.w;
-      q[ld] = word_dot_f32<BITS>(u, hv, q[ld], m);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  // q holds u times the integer-code sums; 1/u is exact
-  const float iu = 1.f / fp8_code_unit();
-#pragma unroll
-  for (int ld = 0; ld < N; ++ld) {
-    const uint32_t sb = dsb[ld];
-    acc[ld] += wk * (bf16f(sb & 0xFFFFu) * iu * q[ld] + bf16f(sb >> 16) * Hs);
-  }
-}
-
-// Sums of the two 32-lane halves of a wave, uniform across the wave.
-__device__ __forceinline__ void half_sums32(float v, float &lo, float &hi) {
-  v = row16_sum(v);
-  lo = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 0)) +
-       __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 16));
-  hi = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 32)) +
-       __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 48));
-}
-
-// Sum over aligned groups of LPR lanes (16, 32 or 64) without LDS traffic.
-template <int LPR>
-__device__ __forceinline__ float lane_group_sum(float v, int lane) {
-  static_assert(LPR == 16 || LPR == 32 || LPR == 64, "group of 16, 32 or 64 lanes");
-  if (LPR == 16) return row16_sum(v);
-  if (LPR == 32) return half_sum32(v, lane);
-  return wave_sum64(v);
-}
 
 template <int BITS, int H, int I, int K, int RR, bool RES>
 __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
@@ -799,10 +563,8 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
           for (int k = 0; k < K; ++k) {
             s_ids[k] = sel_i[k];
             s_w[k] = p[k] / den;
-            if (b == 0 && a.ids_out) {
-              a.ids_out[k] = sel_i[k];
-              a.w_out[k] = p[k] / den;
-            }
+            if (b == 0 && a.ids_out) a.ids_out[k] = sel_i[k];
+            if (b == 0 && a.w_out) a.w_out[k] = p[k] / den;
           }
         }
       } else if (lane < K) {

@@ -40,6 +40,7 @@ WsLayout ws_layout(const moe_dims &d, int T) {
   W.logits_tag = kTagOff;
   W.h_tag = kHTagOff;
   W.p_tag = kPTagOff;
+  W.r_tag = kRTagOff;
   size_t o = align_up(kHeaderBytes, kAlign);
   W.logits = o;
   o = align_up(o + (size_t)route_splits(d, T) * T * d.n_experts * 4, kAlign);
@@ -135,6 +136,18 @@ static int fused_tokens(const moe_dims &d, const moe_layer &L, const uint16_t *x
     if (rc != 0) return rc;
   }
   return 0;
+}
+
+// Stacks of layers run the multi-layer kernel where the single-token kernel
+// covers the dims; MOE_DISABLE_STACK=1 runs one single-layer call per layer
+// instead (used to compare the two).
+static bool stack_disabled() {
+  static int disabled = -1;
+  if (disabled < 0) {
+    const char *e = getenv("MOE_DISABLE_STACK");
+    disabled = (e && e[0] == '1') ? 1 : 0;
+  }
+  return disabled == 1;
 }
 
 // Two or more tokens that the fused kernel does not take run the grouped path
@@ -299,6 +312,76 @@ moe_status moe_layer_decode_residual(const moe_dims *dims, const moe_layer *laye
     return MOE_ERR_HIP;
   if (expert_forward(*dims, *layer, x_d, T, ids_d, w_d, y_d, ws, stream) != 0) return MOE_ERR_HIP;
   if (launch_resid_add(*dims, resid, y_d, T, stream) != 0) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+moe_status moe_stack_decode(const moe_dims *dims, const moe_layer *layers, int32_t n_layers,
+                            const uint16_t *x, float *y, int32_t *ids, float *w, void *ws,
+                            size_t ws_bytes, void *stream) {
+  MOE_TRY(check_dims(dims));
+  if (!layers || !x || !y) return MOE_ERR_NULL;
+  if (n_layers < 1) return MOE_ERR_SHAPE;
+  for (int l = 0; l < n_layers; ++l) {
+    MOE_TRY(check_layer(dims, &layers[l]));
+    if (!layers[l].router) return MOE_ERR_NULL;
+    if (!aligned(layers[l].router, 16)) return MOE_ERR_ALIGN;
+  }
+  if (!aligned(x, 16) || !aligned(y, 16) || (ids && !aligned(ids, 4)) || (w && !aligned(w, 4)))
+    return MOE_ERR_ALIGN;
+  MOE_TRY(check_ws(dims, 1, ws, ws_bytes));
+  const size_t H = (size_t)dims->hidden, K = (size_t)dims->top_k;
+  if (use_fused(*dims, 1) && !stack_disabled()) {
+    for (int l0 = 0; l0 < n_layers; l0 += kMaxStackLayers) {
+      const int n = n_layers - l0 < kMaxStackLayers ? n_layers - l0 : kMaxStackLayers;
+      if (launch_stack_fused(*dims, layers + l0, n, x + l0 * H, y + l0 * H,
+                             ids ? ids + l0 * K : nullptr, w ? w + l0 * K : nullptr, nullptr,
+                             nullptr, ws, stream) != 0)
+        return MOE_ERR_HIP;
+    }
+    return MOE_OK;
+  }
+  for (int l = 0; l < n_layers; ++l) {
+    const moe_status st = moe_layer_decode(dims, &layers[l], x + l * H, 1, y + l * H,
+                                           ids ? ids + l * K : nullptr, w ? w + l * K : nullptr,
+                                           ws, ws_bytes, stream);
+    if (st != MOE_OK) return st;
+  }
+  return MOE_OK;
+}
+
+moe_status moe_stack_decode_residual(const moe_dims *dims, const moe_layer *layers,
+                                     int32_t n_layers, float *resid, uint16_t *x_out, float *y,
+                                     int32_t *ids, float *w, void *ws, size_t ws_bytes,
+                                     void *stream) {
+  MOE_TRY(check_dims(dims));
+  if (!layers || !resid) return MOE_ERR_NULL;
+  if (n_layers < 1) return MOE_ERR_SHAPE;
+  for (int l = 0; l < n_layers; ++l) {
+    MOE_TRY(check_layer(dims, &layers[l]));
+    if (!layers[l].router) return MOE_ERR_NULL;
+    if (!aligned(layers[l].router, 16)) return MOE_ERR_ALIGN;
+  }
+  if (!aligned(resid, 16) || (x_out && !aligned(x_out, 16)) || (y && !aligned(y, 16)) ||
+      (ids && !aligned(ids, 4)) || (w && !aligned(w, 4)))
+    return MOE_ERR_ALIGN;
+  MOE_TRY(check_ws(dims, 1, ws, ws_bytes));
+  const size_t H = (size_t)dims->hidden, K = (size_t)dims->top_k;
+  if (use_fused(*dims, 1) && !stack_disabled()) {
+    for (int l0 = 0; l0 < n_layers; l0 += kMaxStackLayers) {
+      const int n = n_layers - l0 < kMaxStackLayers ? n_layers - l0 : kMaxStackLayers;
+      if (launch_stack_fused(*dims, layers + l0, n, nullptr, y ? y + l0 * H : nullptr,
+                             ids ? ids + l0 * K : nullptr, w ? w + l0 * K : nullptr, resid,
+                             x_out ? x_out + l0 * H : nullptr, ws, stream) != 0)
+        return MOE_ERR_HIP;
+    }
+    return MOE_OK;
+  }
+  for (int l = 0; l < n_layers; ++l) {
+    const moe_status st = moe_layer_decode_residual(
+        dims, &layers[l], resid, 1, x_out ? x_out + l * H : nullptr, y ? y + l * H : nullptr,
+        ids ? ids + l * K : nullptr, w ? w + l * K : nullptr, ws, ws_bytes, stream);
+    if (st != MOE_OK) return st;
+  }
   return MOE_OK;
 }
 

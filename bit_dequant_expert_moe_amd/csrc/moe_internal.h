@@ -32,6 +32,8 @@ BlobLayout blob_layout(const moe_dims &d);
 //   h_tag      : uint64 [kGroups][5][1024] (fp32 h bits | epoch << 32)
 //   p_tag      : uint64 [4][4096]  routed down sums per slot and output row
 //                (fp32 bits | epoch << 32)
+//   r_tag      : uint64 [kGroups][4096] r + y per output row (multi-layer
+//                kernel, residual mode)
 // then, not initialised:
 //   logits     : fp32 [S][T][E] partial router sums (S <= kMaxRouteSplits)
 //   ids        : int32 [T][K]
@@ -77,11 +79,14 @@ constexpr size_t kTagOff = kFCtrlOff + sizeof(FCtrl);
 constexpr size_t kHTagOff = kTagOff + (size_t)kGroups * kMaxE * 8;
 // tagged routed down sums: uint64 [kFusedSlots - 1][kFusedH]
 constexpr size_t kPTagOff = kHTagOff + (size_t)kGroups * kFusedSlots * kFusedI * 8;
-constexpr size_t kHeaderBytes = kPTagOff + (size_t)(kFusedSlots - 1) * kFusedH * 8;
+// tagged residual rows r + y of the multi-layer kernel: uint64 [kGroups][kFusedH]
+constexpr size_t kRTagOff = kPTagOff + (size_t)(kFusedSlots - 1) * kFusedH * 8;
+constexpr size_t kHeaderBytes = kRTagOff + (size_t)kGroups * kFusedH * 8;
+constexpr int kMaxStackLayers = 64;  // layers per launch of the multi-layer kernel
 
 struct WsLayout {
-  size_t ctrl, fctrl, logits_tag, h_tag, p_tag, logits, ids, w, h, bk, xb, xs, hb, hs, yd, xn, yr,
-      total;
+  size_t ctrl, fctrl, logits_tag, h_tag, p_tag, r_tag, logits, ids, w, h, bk, xb, xs, hb, hs, yd,
+      xn, yr, total;
 };
 WsLayout ws_layout(const moe_dims &d, int T);
 
@@ -126,6 +131,12 @@ int launch_layer_fused(const moe_dims &d, const moe_layer &L, const uint16_t *x,
                        const int32_t *ids_in, const float *w_in, int32_t *ids_out,
                        float *w_out, float *y, float *resid, uint16_t *x_out, void *ws,
                        void *stream);
+// n_layers (<= kMaxStackLayers) consecutive layers of one token in one launch
+// (moe_stack.hip); resid != null selects residual mode (x from resid, x_out
+// optional, y optional), else x [n_layers][H] and y [n_layers][H].
+int launch_stack_fused(const moe_dims &d, const moe_layer *layers, int n_layers,
+                       const uint16_t *x, float *y, int32_t *ids_out, float *w_out, float *resid,
+                       uint16_t *x_out, void *ws, void *stream);
 // Residual stream steps of the unfused path.
 int launch_rmsnorm(const moe_dims &d, const float *r, int T, uint16_t *x, void *stream);
 int launch_resid_add(const moe_dims &d, float *r, const float *y, int T, void *stream);

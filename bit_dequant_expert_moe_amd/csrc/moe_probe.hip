@@ -14,23 +14,27 @@ namespace {
 
 constexpr int kProbeThreads = 256;
 constexpr int kLoadsInFlight = 8;  // 16-byte loads per thread per round
+constexpr size_t kStreamBlocks = 2048;
 
-// Reads `n16` 16-byte words; each workgroup writes the XOR of what it read
-// to sink[blockIdx.x] (so that no load can be dropped).
+// Reads `n16` 16-byte words; workgroup b reads the b-th of gridDim.x
+// contiguous ranges, kLoadsInFlight coalesced 4 KB blocks per round, and
+// writes the XOR of what it read to sink[b] (so that no load can be dropped).
 __global__ void __launch_bounds__(kProbeThreads) k_stream_read(const uint4 *__restrict__ src,
                                                                size_t n16, uint32_t *sink) {
   __shared__ uint32_t s_x[kProbeThreads / 64];
-  const size_t stride = (size_t)gridDim.x * kProbeThreads;
+  const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const size_t b0 = (size_t)blockIdx.x * per;
+  const size_t b1 = b0 + per < n16 ? b0 + per : n16;
   uint32_t acc = 0;
-  size_t i = (size_t)blockIdx.x * kProbeThreads + threadIdx.x;
-  for (; i + (kLoadsInFlight - 1) * stride < n16; i += kLoadsInFlight * stride) {
+  size_t i = b0 + threadIdx.x;
+  for (; i + (kLoadsInFlight - 1) * kProbeThreads < b1; i += kLoadsInFlight * kProbeThreads) {
     uint4 v[kLoadsInFlight];
 #pragma unroll
-    for (int k = 0; k < kLoadsInFlight; ++k) v[k] = src[i + k * stride];
+    for (int k = 0; k < kLoadsInFlight; ++k) v[k] = src[i + k * kProbeThreads];
 #pragma unroll
     for (int k = 0; k < kLoadsInFlight; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
   }
-  for (; i < n16; i += stride) {
+  for (; i < b1; i += kProbeThreads) {
     const uint4 v = src[i];
     acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
@@ -54,11 +58,11 @@ inline hipStream_t S(void *s) { return static_cast<hipStream_t>(s); }
 }  // namespace
 
 int stream_read_blocks(size_t bytes) {
-  // enough workgroups to keep ~8 of them on every compute unit, fewer for
-  // small sizes (at least one round of loads per thread)
+  // up to 8 workgroups per compute unit (2048), fewer for small sizes: each
+  // reads at least one round of loads
   const size_t per_round = (size_t)kProbeThreads * 16 * kLoadsInFlight;
   size_t b = (bytes + per_round - 1) / per_round;
-  if (b > 2048) b = 2048;
+  if (b > kStreamBlocks) b = kStreamBlocks;
   if (b < 1) b = 1;
   return (int)b;
 }

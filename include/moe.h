@@ -229,6 +229,39 @@ moe_status moe_layer_decode_residual(const moe_dims *dims, const moe_layer *laye
                                      int32_t *ids, float *w, void *ws, size_t ws_bytes,
                                      void *stream);
 
+/* Consecutive layers of one decode token ([HL], "How the SSD expert
+ * streaming pipeline works": a token runs the layers in sequence, each one
+ * router -> top-K -> expert forward -> combine; the pages keep the next
+ * layer's command queued so that the GPU does not wait between layers).
+ * For l = 0 .. n_layers - 1, exactly as moe_layer_decode of one token:
+ *   y[l] = the MoE layer `layers[l]` of x[l];  ids[l], w[l] its routing.
+ * layers: HOST array of n_layers layer descriptors (device pointers inside,
+ * each as for moe_layer_decode).  x bf16 [n_layers][H], y fp32
+ * [n_layers][H] (16-byte aligned); ids int32 [n_layers][K] and w fp32
+ * [n_layers][K], each optional (NULL).  ws: at least moe_workspace_bytes(
+ * dims, 1) bytes, initialised.  Where the single-token kernel covers the
+ * dims (see the conventions), up to 64 layers run in one launch that keeps
+ * all 256 compute units (same condition: nothing may run beside it); the
+ * routing-independent bytes of each layer (router, shared expert) are read
+ * while the layer before it routes.  Results are bitwise those of
+ * n_layers moe_layer_decode calls; other dims run exactly those calls. */
+moe_status moe_stack_decode(const moe_dims *dims, const moe_layer *layers, int32_t n_layers,
+                            const uint16_t *x, float *y, int32_t *ids, float *w, void *ws,
+                            size_t ws_bytes, void *stream);
+
+/* The same on the residual stream: for l = 0 .. n_layers - 1, exactly as
+ * moe_layer_decode_residual of one token,
+ *   x[l] = bf16(rmsnorm(r)),  y[l] = layer l of x[l],  r = r + y[l],
+ * so each layer's routing depends on the layer before it.  resid fp32 [H]
+ * (16-byte aligned), read and written (r after the last layer); x_out bf16
+ * [n_layers][H], y fp32 [n_layers][H], ids, w: each optional.  Results are
+ * bitwise those of n_layers moe_layer_decode_residual calls.  After a call
+ * that leaves a device error resid is undefined. */
+moe_status moe_stack_decode_residual(const moe_dims *dims, const moe_layer *layers,
+                                     int32_t n_layers, float *resid, uint16_t *x_out, float *y,
+                                     int32_t *ids, float *w, void *ws, size_t ws_bytes,
+                                     void *stream);
+
 /* ---------------------------------------------------------------------------
  * Off-HBM expert tier ([HL], "How the SSD expert streaming pipeline works":
  * per token only the K routed experts of a layer are read from the slow tier,

@@ -48,7 +48,7 @@ def chain_stack():
 
 def _oracle_layer_check(L, x, ids, w, y, label):
     _, _, logits_o, gap_o = oracle.route(L.od, L.router_h, x[None])
-    gu.check_routing(L.od, ids[None], w[None], logits_o, gap_o, 4)
+    gu.check_routing(L.od, ids[None], w[None], logits_o, gap_o, L.dims.top_k)
     sel = logits_o[0][ids]
     wf = np.exp(sel - sel.max())
     wf /= wf.sum()
@@ -60,10 +60,13 @@ def _oracle_layer_check(L, x, ids, w, y, label):
 
 
 class _Run:
-    """Device buffers of N_TOK tokens through the stack."""
+    """Device buffers of N_TOK tokens through the stack; `fused` runs each
+    token as one moe_stack_decode(_residual) call, else one single-layer call
+    per layer."""
 
-    def __init__(self, layers, chain):
-        self.layers, self.chain = layers, chain
+    def __init__(self, layers, chain, fused=False):
+        self.layers, self.chain, self.fused = layers, chain, fused
+        self.arr = moe.layer_array([L.L for L in layers])
         self.dims = layers[0].dims
         H = 4096
         if chain:
@@ -84,6 +87,14 @@ class _Run:
     def enqueue(self, t, sp):
         if self.chain:
             self.r[t].copy_(self.r0[t])
+        if self.fused:
+            if self.chain:
+                moe.moe_stack_decode_residual(self.dims, self.arr, self.r[t], self.x[t], self.y[t],
+                                              self.ids[t], self.w[t], self.ws, self.wsb, sp)
+            else:
+                moe.moe_stack_decode(self.dims, self.arr, self.x[t], self.y[t], self.ids[t],
+                                     self.w[t], self.ws, self.wsb, sp)
+            return
         for l, L in enumerate(self.layers):
             if self.chain:
                 moe.moe_layer_decode_residual(self.dims, L.L, self.r[t], 1, self.x[t, l],
@@ -117,6 +128,148 @@ def _check_stack(run, out):
             # the residual after the last layer is r + y of every layer, in fp32
             np.testing.assert_array_equal(out["r"][t], r)
     return worst
+
+
+def _eager(run):
+    sp = torch.cuda.current_stream().cuda_stream
+    for t in range(N_TOK):
+        run.enqueue(t, sp)
+    torch.cuda.synchronize()
+    assert moe.moe_get_device_error(run.ws) == 0
+    return run.host()
+
+
+@pytest.mark.parametrize("chain", [False, True], ids=["plain", "chain"])
+def test_stack_kernel_equals_per_layer_calls(chain, plain_stack, chain_stack):
+    # the multi-layer kernel: ids, w, y (and x, r on the chain) bitwise those
+    # of one single-layer call per layer, and every layer against the oracle
+    layers = chain_stack if chain else plain_stack
+    _say("multi-layer kernel, %d layers, chain=%s" % (N_LAYERS, chain))
+    ref = _eager(_Run(layers, chain, fused=False))
+    run = _Run(layers, chain, fused=True)
+    got = _eager(run)
+    for k in ref:
+        np.testing.assert_array_equal(got[k], ref[k], err_msg=k)
+    worst = _check_stack(run, got)
+    _say("  bitwise equal to the per-layer calls; worst max|dy|/max|y| %.2e" % worst)
+    # a second call on the same workspace (the epochs continue)
+    again = _eager(run)
+    for k in ref:
+        np.testing.assert_array_equal(again[k], ref[k], err_msg="second call, " + k)
+
+
+@pytest.mark.parametrize("chain", [False, True], ids=["plain", "chain"])
+def test_stack_kernel_graph_replays(chain, plain_stack, chain_stack):
+    layers = chain_stack if chain else plain_stack
+    run = _Run(layers, chain, fused=True)
+    eager = _eager(run)
+    graphs = []
+    cs = torch.cuda.Stream()
+    with torch.cuda.stream(cs):
+        for t in range(N_TOK):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cs):
+                run.enqueue(t, torch.cuda.current_stream().cuda_stream)
+            graphs.append(g)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        run.y.zero_()
+        run.ids.zero_()
+        for t in range(N_TOK):
+            graphs[t].replay()
+            torch.cuda.synchronize()
+            # eager single-layer work on the same workspace between replays
+            if rep == 1:
+                L = layers[0]
+                yy = torch.empty(4096, dtype=torch.float32, device="cuda")
+                moe.moe_layer_decode(L.dims, L.L, L.x_dev(synth.tokens(5, 0, 1, 4096)), 1, yy,
+                                     None, None, run.ws, run.wsb)
+        got = run.host()
+        for k in eager:
+            np.testing.assert_array_equal(got[k], eager[k], err_msg="replay %d, %s" % (rep, k))
+    assert moe.moe_get_device_error(run.ws) == 0
+
+
+def test_stack_kernel_2bit_and_partial_layers():
+    # 2-bit codes, and a call over a subset of the layers (3 of 5)
+    layers = [gu.DeviceLayer(4096, 1024, 64, 4, bits=2, seed=1007, layer=l) for l in range(5)]
+    d = layers[0].dims
+    ws = moe.alloc_workspace(d, 1)
+    x_h = np.stack([synth.tokens(1007, l, 1, 4096)[0] for l in range(5)])
+    x = torch.from_numpy(x_h.view(np.int16)).cuda()
+    for sel in (list(range(5)), [1, 2, 4]):
+        y = torch.zeros((len(sel), 4096), dtype=torch.float32, device="cuda")
+        ids = torch.zeros((len(sel), 4), dtype=torch.int32, device="cuda")
+        w = torch.zeros((len(sel), 4), dtype=torch.float32, device="cuda")
+        xs = x[sel].contiguous()
+        moe.moe_stack_decode(d, [layers[l].L for l in sel], xs, y, ids, w, ws)
+        for i, l in enumerate(sel):
+            yr = torch.zeros(4096, dtype=torch.float32, device="cuda")
+            ir = torch.zeros(4, dtype=torch.int32, device="cuda")
+            wr = torch.zeros(4, dtype=torch.float32, device="cuda")
+            moe.moe_layer_decode(d, layers[l].L, xs[i], 1, yr, ir, wr, ws)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(y[i].cpu().numpy(), yr.cpu().numpy())
+            np.testing.assert_array_equal(ids[i].cpu().numpy(), ir.cpu().numpy())
+            np.testing.assert_array_equal(w[i].cpu().numpy(), wr.cpu().numpy())
+        _oracle_layer_check(layers[sel[-1]], x_h[sel[-1]], ids[-1].cpu().numpy(),
+                            w[-1].cpu().numpy(), y[-1].cpu().numpy(), "2-bit layer %d" % sel[-1])
+    assert moe.moe_get_device_error(ws) == 0
+
+
+@pytest.mark.parametrize("chain", [False, True], ids=["plain", "chain"])
+def test_stack_kernel_more_layers_than_one_launch(chain):
+    # 70 layers (64 per launch): the same layers of 16 experts repeated
+    base = [gu.DeviceLayer(4096, 1024, 16, 4, bits=4, seed=1008, layer=l,
+                           z_range=synth.workloads.CENTRED_Z) for l in range(5)]
+    n = 70
+    layers = [base[l % 5] for l in range(n)]
+    d = base[0].dims
+    ws = moe.alloc_workspace(d, 1)
+    ys = []
+    for fused in (False, True):
+        y = torch.zeros((n, 4096), dtype=torch.float32, device="cuda")
+        ids = torch.zeros((n, 4), dtype=torch.int32, device="cuda")
+        if chain:
+            r = torch.from_numpy(synth.residual(1008, 1, 4096)[0]).cuda()
+            xo = torch.zeros((n, 4096), dtype=torch.int16, device="cuda")
+            if fused:
+                moe.moe_stack_decode_residual(d, [L.L for L in layers], r, xo, y, ids, None, ws)
+            else:
+                for l, L in enumerate(layers):
+                    moe.moe_layer_decode_residual(d, L.L, r, 1, xo[l], y[l], ids[l], None, ws)
+            out = (y, ids, r, xo)
+        else:
+            x = torch.from_numpy(synth.tokens(1008, 0, n, 4096).view(np.int16)).cuda()
+            if fused:
+                moe.moe_stack_decode(d, [L.L for L in layers], x, y, ids, None, ws)
+            else:
+                for l, L in enumerate(layers):
+                    moe.moe_layer_decode(d, L.L, x[l], 1, y[l], ids[l], None, ws)
+            out = (y, ids)
+        torch.cuda.synchronize()
+        ys.append([o.cpu().numpy() for o in out])
+    for a, b in zip(*ys):
+        np.testing.assert_array_equal(a, b)
+    assert moe.moe_get_device_error(ws) == 0
+
+
+def test_stack_fallback_dims_run_per_layer_calls():
+    # dims the single-token kernel does not cover (H = 1024): the stack entry
+    # point runs one single-layer call per layer
+    layers = [gu.DeviceLayer(1024, 512, 32, 2, bits=4, seed=1009, layer=l) for l in range(3)]
+    d = layers[0].dims
+    ws = moe.alloc_workspace(d, 1)
+    x_h = synth.tokens(1009, 0, 3, 1024)
+    x = torch.from_numpy(x_h.view(np.int16)).cuda()
+    y = torch.zeros((3, 1024), dtype=torch.float32, device="cuda")
+    ids = torch.zeros((3, 2), dtype=torch.int32, device="cuda")
+    w = torch.zeros((3, 2), dtype=torch.float32, device="cuda")
+    moe.moe_stack_decode(d, [L.L for L in layers], x, y, ids, w, ws)
+    torch.cuda.synchronize()
+    for l, L in enumerate(layers):
+        _oracle_layer_check(L, x_h[l], ids[l].cpu().numpy(), w[l].cpu().numpy(),
+                            y[l].cpu().numpy(), "fallback layer %d" % l)
 
 
 @pytest.mark.parametrize("chain", [False, True], ids=["plain", "chain"])
