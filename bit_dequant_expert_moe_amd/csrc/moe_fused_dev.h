@@ -75,16 +75,22 @@ __device__ __forceinline__ uint2 ld_coh8(const void *base, uint32_t byte_off) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t blob_rsrc(const uint8_t *base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), 0, 0x7fffffff, 0x00020000);
 }
+// POL: the cache-policy bits of the load (0: default; kPolStream: the
+// non-temporal hint for bytes that are read once)
+constexpr int kPolStream = 2;
+template <int POL = 0>
 __device__ __forceinline__ uint4 bld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, POL);
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
+template <int POL = 0>
 __device__ __forceinline__ uint2 bld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, POL);
   return make_uint2(v[0], v[1]);
 }
+template <int POL = 0>
 __device__ __forceinline__ uint32_t bld4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, POL);
 }
 
 template <int BITS, int H, int I, int K>

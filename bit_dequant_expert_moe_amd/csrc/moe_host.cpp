@@ -41,6 +41,7 @@ WsLayout ws_layout(const moe_dims &d, int T) {
   W.h_tag = kHTagOff;
   W.p_tag = kPTagOff;
   W.r_tag = kRTagOff;
+  W.r_done = kRDoneOff;
   size_t o = align_up(kHeaderBytes, kAlign);
   W.logits = o;
   o = align_up(o + (size_t)route_splits(d, T) * T * d.n_experts * 4, kAlign);

@@ -34,6 +34,8 @@ BlobLayout blob_layout(const moe_dims &d);
 //                (fp32 bits | epoch << 32)
 //   r_tag      : uint64 [kGroups][4096] r + y per output row (multi-layer
 //                kernel, residual mode)
+//   r_done     : uint64 [kGroups][256] per workgroup: its rows of r_tag are
+//                stored (epoch in the high half)
 // then, not initialised:
 //   logits     : fp32 [S][T][E] partial router sums (S <= kMaxRouteSplits)
 //   ids        : int32 [T][K]
@@ -81,11 +83,13 @@ constexpr size_t kHTagOff = kTagOff + (size_t)kGroups * kMaxE * 8;
 constexpr size_t kPTagOff = kHTagOff + (size_t)kGroups * kFusedSlots * kFusedI * 8;
 // tagged residual rows r + y of the multi-layer kernel: uint64 [kGroups][kFusedH]
 constexpr size_t kRTagOff = kPTagOff + (size_t)(kFusedSlots - 1) * kFusedH * 8;
-constexpr size_t kHeaderBytes = kRTagOff + (size_t)kGroups * kFusedH * 8;
+// one tagged word per workgroup once its r + y rows are stored: uint64 [kGroups][256]
+constexpr size_t kRDoneOff = kRTagOff + (size_t)kGroups * kFusedH * 8;
+constexpr size_t kHeaderBytes = kRDoneOff + (size_t)kGroups * 256 * 8;
 constexpr int kMaxStackLayers = 64;  // layers per launch of the multi-layer kernel
 
 struct WsLayout {
-  size_t ctrl, fctrl, logits_tag, h_tag, p_tag, r_tag, logits, ids, w, h, bk, xb, xs, hb, hs, yd,
+  size_t ctrl, fctrl, logits_tag, h_tag, p_tag, r_tag, r_done, logits, ids, w, h, bk, xb, xs, hb, hs, yd,
       xn, yr, total;
 };
 WsLayout ws_layout(const moe_dims &d, int T);

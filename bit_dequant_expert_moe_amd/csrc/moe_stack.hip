@@ -86,7 +86,8 @@ struct StackArgs {
   FCtrl *fc;
   uint64_t *tags;  // [kGroups][kMaxE] tagged logits
   uint64_t *htag;  // [kGroups][K+1][I] tagged activations
-  uint64_t *rtag;  // residual mode: [kGroups][H] tagged r + y
+  uint64_t *rtag;   // residual mode: [kGroups][H] tagged r + y
+  uint64_t *rdone;  // residual mode: [kGroups][kG] tagged: the workgroup's rows are stored
   int E, has_shared;
   int64_t off_gq, off_uq, off_dq, off_gsb, off_usb, off_dsb;
 };
@@ -98,7 +99,7 @@ struct StackArgs {
 #define MOE_TRACE(ev)                                                              \
   do {                                                                             \
     if (trace && lane == 0)                                                        \
-      trace[((size_t)b * kMaxStackLayers + l) * 16 + (ev)] =                       \
+      trace[((size_t)b * kMaxStackLayers + l) * 32 + (ev)] =                       \
           __builtin_amdgcn_s_memrealtime();                                         \
   } while (0)
 #else
@@ -133,6 +134,20 @@ __device__ __forceinline__ StackLayer uniform_layer(const StackLayer &s) {
   return r;
 }
 
+// Which weight loads carry the non-temporal hint: 0 none, 1 the routed
+// experts', 2 also the shared expert's and the router's.
+#ifndef MOE_STACK_NT
+#define MOE_STACK_NT 1
+#endif
+constexpr int kPolRouted = MOE_STACK_NT >= 1 ? kPolStream : 0;
+// First wait of the exchange wave before its logits poll, in s_sleep units
+// (64 clocks): a poll issued before the last logits can be visible comes
+// back incomplete and costs a whole round trip.
+#ifndef MOE_STACK_SLEEP0
+#define MOE_STACK_SLEEP0 19
+#endif
+constexpr int kPolShared = MOE_STACK_NT >= 2 ? kPolStream : 0;
+
 // LDS-only workgroup barrier: orders the waves' LDS accesses without waiting
 // for their global loads in flight (a barrier with a global fence would wait
 // for the prefetched weights).
@@ -161,9 +176,11 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
   __shared__ uint32_t s_hready[NSL];  // layers whose s_hb[slot] is filled
   __shared__ uint32_t s_epoch;        // epoch of the last call completed before this one
   __shared__ uint32_t s_ready;        // layers routed
+  __shared__ uint32_t s_gu_issued;    // gate/up waves x layers whose routed loads are issued
   __shared__ float s_ss[NW];          // residual mode: sum of r^2 per wave
   __shared__ uint4 s_xn[RES ? H / 8 : 1];  // residual mode: normalised x, bf16
   __shared__ uint32_t s_rseen;        // residual mode: layers whose r + y words are all written
+  __shared__ uint32_t s_rstored;      // residual mode: row waves x layers that stored their r + y
   // the layers' pointers, copied from the kernel arguments once (a scalar
   // load of a later layer's entry from the argument segment can miss the
   // scalar cache and cost a memory round trip on the routing path)
@@ -186,7 +203,9 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
   }
   if (tid == 0) {
     s_ready = 0u;
+    s_gu_issued = 0u;
     s_rseen = 0u;
+    s_rstored = 0u;
   }
   static_assert(sizeof(StackLayer) == 32, "four 8-byte words per layer");
   if (tid < 4 * NL)
@@ -205,26 +224,26 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
       rf[1] = p[1];
       return;
     }
-    // one wave polls one word per writer (the first row of each workgroup's
-    // 16, 2 KB per round) until all carry the previous layer's epoch; then
-    // every thread reads its 8 words once (and again only if one of them is
-    // still old: the sample says nothing about the writer's other rows)
-    if (wave == kGuWaves) {  // the exchange wave (free at the end of a layer)
+    // the exchange wave polls the dense array of the writers' done words
+    // (2 KB) until all carry the previous layer's epoch; then every thread
+    // reads its 8 words once (again only if one of them is still old: a done
+    // word orders nothing, the tags of the data words decide)
+    if (wave == kGuWaves) {
       long spins = 0;
-      const uint32_t base = (uint32_t)((size_t)grp * H * 8);
+      const uint32_t base = (uint32_t)((size_t)grp * kG * 8);
       while (true) {
         bool ok = true;
 #pragma unroll
-        for (int i = 0; i < kG / 64; ++i) {
-          const uint2 t = ld_coh8(a.rtag, base + (uint32_t)(Gm::D_ROWS * (lane + 64 * i)) * 8u);
-          ok &= t.y == epoch_prev;
+        for (int i = 0; i < kG / 128; ++i) {
+          const uint4 t = ld_coh16(a.rdone, base + (uint32_t)(128 * i + 2 * lane) * 8u);
+          ok &= t.y == epoch_prev && t.w == epoch_prev;
         }
         if (__all(ok)) break;
         if (++spins > kSpinMax) {
           if (lane == 0) atomicOr(&a.ctrl->err, 2u);
           break;
         }
-        __builtin_amdgcn_s_sleep(4);
+        __builtin_amdgcn_s_sleep(2);
       }
       lds_release();
       if (lane == 0) *lds(&s_rseen) = (uint32_t)l;
@@ -302,14 +321,15 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
       o_gsb[j] = (uint32_t)(a.off_gsb + ((int64_t)r * groups + sg * COLS / kGroup) * 4);
       o_usb[j] = (uint32_t)(a.off_usb + ((int64_t)r * groups + sg * COLS / kGroup) * 4);
     }
-    auto load_rows = [&](int slot, const uint8_t *bl) {
+    auto load_rows = [&](auto pol_tag, int slot, const uint8_t *bl) {
+      constexpr int P = decltype(pol_tag)::value;
       const __amdgpu_buffer_rsrc_t rs = blob_rsrc(bl);
 #pragma unroll
       for (int j = 0; j < LSEG; ++j) {
-        gq[slot][j] = bld16(rs, o_gq[j]);
-        uq[slot][j] = bld16(rs, o_uq[j]);
-        gsb[slot][j] = bld4(rs, o_gsb[j]);
-        usb[slot][j] = bld4(rs, o_usb[j]);
+        gq[slot][j] = bld16<P>(rs, o_gq[j]);
+        uq[slot][j] = bld16<P>(rs, o_uq[j]);
+        gsb[slot][j] = bld4<P>(rs, o_gsb[j]);
+        usb[slot][j] = bld4<P>(rs, o_usb[j]);
       }
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -323,8 +343,13 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
         const int ec = e < a.E ? e : a.E - 1;
 #pragma unroll
         for (int c = 0; c < 2; ++c)
-          rw[row][c] = *reinterpret_cast<const uint4 *>(Ly.router + (size_t)ec * H +
-                                                       (size_t)(tid + HALF * c) * 8);
+        {
+          typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+          const u32x4 *p = reinterpret_cast<const u32x4 *>(Ly.router + (size_t)ec * H +
+                                                           (size_t)(tid + HALF * c) * 8);
+          const u32x4 v = kPolShared ? __builtin_nontemporal_load(p) : *p;
+          rw[row][c] = make_uint4(v[0], v[1], v[2], v[3]);
+        }
       }
       if (!RES) {
         const uint16_t *xl = a.x + (size_t)l * H;
@@ -336,7 +361,7 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
           xr[t] = *reinterpret_cast<const uint4 *>(xl + (size_t)(xs % Gm::SEG_X) * COLS + 8 * t);
       }
       // without a shared expert slot K reads expert 0 and is never used
-      load_rows(K, a.has_shared ? Ly.shared : Ly.experts);
+      load_rows(std::integral_constant<int, kPolShared>{}, K, a.has_shared ? Ly.shared : Ly.experts);
     };
     prefetch(0);
 
@@ -345,11 +370,14 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
       const int buf = l & 1;
       if (RES) {
         gather_r(l, s_epoch + (uint32_t)l);  // (s_epoch is read only for l > 0)
+        if (wave == 0) MOE_TRACE(27);
         norm_x(l);
+        if (wave == 0) MOE_TRACE(28);
         rx2[0] = rx_own;
         rx2[1] = s_xn[tid + HALF];
 #pragma unroll
         for (int t = 0; t < Gm::XLD; ++t) xr[t] = s_xn[(xs % Gm::SEG_X) * (COLS / 8) + t];
+        if (wave == 0) MOE_TRACE(30);
       }
       // router partials, reduced as k_layer1's waves `wave` and `wave + 4`
 #pragma unroll
@@ -366,6 +394,7 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
           if (lane == 0) s_red[wave + kGuWaves * c][row] = v;
         }
       }
+      if (wave == 0) MOE_TRACE(31);
       // x pairs and per-segment corrections, one code word at a time, to LDS
       if (xs < Gm::SEG_X) {
         float C = 0.f, X = 0.f;
@@ -427,6 +456,7 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
         pu = wave_sum64(pu);
         return pg / (1.f + expf(-pg)) * pu;
       };
+      if (wave == 0) MOE_TRACE(29);
       lds_barrier();  // (A) router partials, x pairs, epoch
       if (wave == 0) MOE_TRACE(8);
       const uint32_t epoch = s_epoch + 1u + (uint32_t)l;
@@ -450,8 +480,13 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
         eid[k] = __builtin_amdgcn_readfirstlane(s_ids[k]);
         const bool ok = eid[k] >= 0 && eid[k] < a.E;
         // an invalid id reads expert 0 and contributes 0
-        load_rows(k, Ly.experts + (size_t)(ok ? eid[k] : 0) * Ly.stride);
+        load_rows(std::integral_constant<int, kPolRouted>{}, k,
+                  Ly.experts + (size_t)(ok ? eid[k] : 0) * Ly.stride);
       }
+      // the down rows' loads go after these (the activations, which every
+      // down row waits for, come from these bytes)
+      if (lane == 0)
+        __hip_atomic_fetch_add(&s_gu_issued, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       if (MOE_STACK_PF == 1 && l + 1 < NL) prefetch(l + 1);
       if (wave == 0) MOE_TRACE(10);
 #pragma unroll
@@ -503,12 +538,20 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
         static_assert(256 * RR <= kMaxE, "tag copy holds 256 RR entries");
         float v[NV];
         MOE_TRACE(1);
-        __builtin_amdgcn_s_sleep(19);
+        __builtin_amdgcn_s_sleep(MOE_STACK_SLEEP0);
+#ifdef MOE_STACK_TRACE
+        int npoll = 0;
+#endif
         while (true) {
           uint4 t[NV / 2];
 #pragma unroll
           for (int i = 0; i < NV / 2; ++i)
             t[i] = ld_coh16(tags_mine, (uint32_t)(128 * i + 2 * lane) * 8u);
+#ifdef MOE_STACK_TRACE
+          if (npoll++ == 0) MOE_TRACE(25);
+          if (trace && lane == 0)
+            trace[((size_t)b * kMaxStackLayers + l) * 32 + 26] = (uint64_t)npoll * 100;
+#endif
           bool ok = true;
 #pragma unroll
           for (int i = 0; i < NV / 2; ++i) {
@@ -602,7 +645,7 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
         lds_release();
         if (lane == 0) *lds(&s_hready[slot]) = want;
         if (slot == K) MOE_TRACE(3);
-        if (slot == K - 1) MOE_TRACE(4);
+        else if (slot < 4) MOE_TRACE(slot == K - 1 ? 4 : 16 + slot);
       }
     }
     // every workgroup has passed the first layer's barrier, where it read the
@@ -630,11 +673,6 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
     auto o_dsb = [&](int row) -> uint32_t {
       return (uint32_t)(a.off_dsb + ((int64_t)row * groups + seg * Gm::DCOLS / kGroup) * 4);
     };
-    auto ld_codes = [&](__amdgpu_buffer_rsrc_t rs, int row) -> uint4 {
-      if (Gm::DWORDS == 4) return bld16(rs, o_dq(row));
-      const uint2 v = bld8(rs, o_dq(row));
-      return make_uint4(v.x, v.y, 0u, 0u);
-    };
     auto row_wave = [&](auto n_tag, int row0) {
       constexpr int N = decltype(n_tag)::value;  // wave-wide loads (row pairs) per slot
       int rows[N];
@@ -648,12 +686,18 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
       }
       uint4 dq[NSL][N];
       uint32_t dsb[NSL][N];
-      auto load_slot = [&](int slot, const uint8_t *bl) {
+      auto load_slot = [&](auto pol_tag, int slot, const uint8_t *bl) {
+        constexpr int P = decltype(pol_tag)::value;
         const __amdgpu_buffer_rsrc_t rs = blob_rsrc(bl);
 #pragma unroll
         for (int ld = 0; ld < N; ++ld) {
-          dq[slot][ld] = ld_codes(rs, rows[ld]);
-          dsb[slot][ld] = bld4(rs, o_dsb(rows[ld]));
+          if (Gm::DWORDS == 4) {
+            dq[slot][ld] = bld16<P>(rs, o_dq(rows[ld]));
+          } else {
+            const uint2 v = bld8<P>(rs, o_dq(rows[ld]));
+            dq[slot][ld] = make_uint4(v.x, v.y, 0u, 0u);
+          }
+          dsb[slot][ld] = bld4<P>(rs, o_dsb(rows[ld]));
         }
         __builtin_amdgcn_sched_barrier(0);
       };
@@ -665,12 +709,14 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
         }
         // the shared expert's rows (without one, slot K reads expert 0 and
         // is never used)
-        load_slot(K, a.has_shared ? Ly.shared : Ly.experts);
+        load_slot(std::integral_constant<int, kPolShared>{}, K,
+                  a.has_shared ? Ly.shared : Ly.experts);
         if (l == 0 && tid == kEpochTid) s_epoch = epoch_done;
         lds_barrier();  // (A)
         const uint32_t want = (uint32_t)(l + 1);
         const uint32_t epoch = s_epoch + 1u + (uint32_t)l;
         wait_lds(&s_ready, want);
+        wait_lds(&s_gu_issued, (uint32_t)kGuWaves * want);
         int eo[K];
         float wk[K];
 #pragma unroll
@@ -679,8 +725,10 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
           const bool ok = eo[k] >= 0 && eo[k] < a.E;
           wk[k] = ok ? s_w[k] : 0.f;
           // an invalid id reads expert 0 and contributes 0
-          load_slot(k, Ly.experts + (size_t)(ok ? eo[k] : 0) * Ly.stride);
+          load_slot(std::integral_constant<int, kPolRouted>{}, k,
+                    Ly.experts + (size_t)(ok ? eo[k] : 0) * Ly.stride);
         }
+        if (cw == 0) MOE_TRACE(19);
         float v[N];
 #pragma unroll
         for (int ld = 0; ld < N; ++ld) v[ld] = 0.f;
@@ -693,6 +741,7 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
                                                      1.f, acc);
 #pragma unroll
           for (int ld = 0; ld < N; ++ld) v[ld] = lane_group_sum<Gm::LPR>(acc[ld], lane);
+          if (cw == 0) MOE_TRACE(20);
         }
 #pragma unroll
         for (int k = 0; k < K; ++k) {
@@ -704,8 +753,8 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
                                                      wk[k], acc);
 #pragma unroll
           for (int ld = 0; ld < N; ++ld) v[ld] += lane_group_sum<Gm::LPR>(acc[ld], lane);
+          if (cw == 0) MOE_TRACE(21 + k);
         }
-        if (cw == 0) MOE_TRACE(6);
 #pragma unroll
         for (int ld = 0; ld < N; ++ld) {
           if (!RES) {
@@ -724,6 +773,18 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
               a.resid[rows[ld]] = rres[ld];
             }
           }
+        }
+        if (RES && l + 1 < NL) {
+          // the last of the three row waves to have stored its rows marks the
+          // workgroup done, one copy per reader group
+          uint32_t prev = 0;
+          if (lane == 0)
+            prev = __hip_atomic_fetch_add(&s_rstored, 1u, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_WORKGROUP);
+          prev = __builtin_amdgcn_readfirstlane(prev);
+          if (prev + 1 == 3u * (uint32_t)(l + 1) && lane < kGroups)
+            __hip_atomic_store(&a.rdone[(size_t)lane * kG + b], (uint64_t)epoch << 32,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         if (cw == 0) MOE_TRACE(7);
       }
@@ -764,6 +825,7 @@ int launch_stack_fused(const moe_dims &d, const moe_layer *layers, int n_layers,
   a.tags = reinterpret_cast<uint64_t *>(base + W.logits_tag);
   a.htag = reinterpret_cast<uint64_t *>(base + W.h_tag);
   a.rtag = reinterpret_cast<uint64_t *>(base + W.r_tag);
+  a.rdone = reinterpret_cast<uint64_t *>(base + W.r_done);
   a.E = d.n_experts;
   a.has_shared = d.has_shared;
   a.off_gq = (int64_t)B.off[MOE_SEC_GATE_Q];
