@@ -18,6 +18,8 @@ MOE_OK = 0
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_UNSUPPORTED",
           -4: "MOE_ERR_ALIGN", -5: "MOE_ERR_WORKSPACE", -6: "MOE_ERR_HIP", -7: "MOE_ERR_DEVICE"}
 SEC_GATE_Q, SEC_UP_Q, SEC_DOWN_Q, SEC_GATE_SB, SEC_UP_SB, SEC_DOWN_SB = range(6)
+# bytes of the per-GPU workspace of moe_stack_decode_residual_noalloc
+NOALLOC_SCRATCH_BYTES = 2 * 1024 * 1024
 # code decoders of the kernel paths (moe_dequantize_as)
 DEQ_SCALAR, DEQ_FP16_PAIR, DEQ_FP8_PAIR, DEQ_BF16_PAIR, DEQ_BF16_SLICE = range(5)
 
@@ -29,7 +31,7 @@ EXPORTS = ("moe_abi_version", "moe_status_str", "moe_check_dims", "moe_expert_by
            "moe_tier_device_bytes", "moe_tier_workspace_bytes", "moe_tier_create",
            "moe_tier_decode", "moe_tier_plan", "moe_tier_stats", "moe_tier_destroy",
            "moe_stream_read_sink_words", "moe_stream_read", "moe_flush", "moe_stack_decode",
-           "moe_stack_decode_residual")
+           "moe_stack_decode_residual", "moe_stack_decode_residual_noalloc")
 
 
 class MoeError(RuntimeError):
@@ -111,6 +113,7 @@ def lib() -> ctypes.CDLL:
             "moe_flush": (i32, [vp, sz, vp]),
             "moe_stack_decode": (i32, [dp, lp, i32, vp, vp, vp, vp, vp, sz, vp]),
             "moe_stack_decode_residual": (i32, [dp, lp, i32, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "moe_stack_decode_residual_noalloc": (i32, [dp, lp, i32, vp, vp, vp, vp, vp, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -258,6 +261,17 @@ def moe_stack_decode_residual(d: Dims, layers, resid, x_out=None, y=None, ids=No
                                          ws_bytes if ws_bytes is not None else ws.numel(),
                                          _stream(stream))
     _check(rc, "moe_stack_decode_residual")
+
+
+def moe_stack_decode_residual_noalloc(d: Dims, layers, resid, x_out=None, y=None, ids=None,
+                                      w=None, stream=None):
+    """moe_stack_decode_residual on the library's own per-GPU workspace
+    (allocates nothing; the first call on a GPU must not be captured)."""
+    arr = _layers(layers)
+    rc = lib().moe_stack_decode_residual_noalloc(ctypes.byref(d.c()), arr, len(arr), _ptr(resid),
+                                                 _ptr(x_out), _ptr(y), _ptr(ids), _ptr(w),
+                                                 _stream(stream))
+    _check(rc, "moe_stack_decode_residual_noalloc")
 
 
 def moe_dequantize(d: Dims, blob, which: int, out, stream=None):

@@ -182,6 +182,23 @@ using namespace moe;
     if (s_ != MOE_OK) return s_;     \
   } while (0)
 
+moe_status moe::check_stack_residual(const moe_dims *dims, const moe_layer *layers,
+                                     int n_layers, const float *resid, const uint16_t *x_out,
+                                     const float *y, const int32_t *ids, const float *w) {
+  MOE_TRY(check_dims(dims));
+  if (!layers || !resid) return MOE_ERR_NULL;
+  if (n_layers < 1) return MOE_ERR_SHAPE;
+  for (int l = 0; l < n_layers; ++l) {
+    MOE_TRY(check_layer(dims, &layers[l]));
+    if (!layers[l].router) return MOE_ERR_NULL;
+    if (!aligned(layers[l].router, 16)) return MOE_ERR_ALIGN;
+  }
+  if (!aligned(resid, 16) || (x_out && !aligned(x_out, 16)) || (y && !aligned(y, 16)) ||
+      (ids && !aligned(ids, 4)) || (w && !aligned(w, 4)))
+    return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
 extern "C" {
 
 int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
@@ -354,17 +371,7 @@ moe_status moe_stack_decode_residual(const moe_dims *dims, const moe_layer *laye
                                      int32_t n_layers, float *resid, uint16_t *x_out, float *y,
                                      int32_t *ids, float *w, void *ws, size_t ws_bytes,
                                      void *stream) {
-  MOE_TRY(check_dims(dims));
-  if (!layers || !resid) return MOE_ERR_NULL;
-  if (n_layers < 1) return MOE_ERR_SHAPE;
-  for (int l = 0; l < n_layers; ++l) {
-    MOE_TRY(check_layer(dims, &layers[l]));
-    if (!layers[l].router) return MOE_ERR_NULL;
-    if (!aligned(layers[l].router, 16)) return MOE_ERR_ALIGN;
-  }
-  if (!aligned(resid, 16) || (x_out && !aligned(x_out, 16)) || (y && !aligned(y, 16)) ||
-      (ids && !aligned(ids, 4)) || (w && !aligned(w, 4)))
-    return MOE_ERR_ALIGN;
+  MOE_TRY(check_stack_residual(dims, layers, n_layers, resid, x_out, y, ids, w));
   MOE_TRY(check_ws(dims, 1, ws, ws_bytes));
   const size_t H = (size_t)dims->hidden, K = (size_t)dims->top_k;
   if (use_fused(*dims, 1) && !stack_disabled()) {

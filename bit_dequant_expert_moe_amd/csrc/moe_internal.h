@@ -123,6 +123,10 @@ inline int route_splits(const moe_dims &d, int T) {
 // Kernel launchers (moe_kernels.hip).  Each returns hipSuccess (0) or the
 // HIP error of the launch.
 int launch_ws_init(void *ws, size_t bytes, void *stream);
+// Argument checks of moe_stack_decode_residual other than the workspace's.
+moe_status check_stack_residual(const moe_dims *dims, const moe_layer *layers, int n_layers,
+                                const float *resid, const uint16_t *x_out, const float *y,
+                                const int32_t *ids, const float *w);
 int launch_route(const moe_dims &d, const uint16_t *router, const uint16_t *x, int T,
                  int32_t *ids, float *w, float *logits, void *ws, void *stream);
 int launch_expert_forward(const moe_dims &d, const moe_layer &L, const uint16_t *x, int T,

@@ -262,6 +262,26 @@ moe_status moe_stack_decode_residual(const moe_dims *dims, const moe_layer *laye
                                      int32_t *ids, float *w, void *ws, size_t ws_bytes,
                                      void *stream);
 
+/* For callers that cannot allocate device memory (code under graph capture,
+ * serving loops that must not call an allocator): moe_stack_decode_residual
+ * with no workspace argument.  Its workspace is an array of
+ * MOE_NOALLOC_SCRATCH_BYTES in the library's device memory, one per GPU,
+ * held until the process ends; this call allocates nothing.  Arguments,
+ * results and errors are those of moe_stack_decode_residual, plus
+ * MOE_ERR_WORKSPACE when the dims need a larger workspace than the array
+ * (moe_workspace_bytes(dims, 1) > MOE_NOALLOC_SCRATCH_BYTES; no valid dims
+ * do today).  The first call on a GPU looks up the array's address and
+ * enqueues its initialisation on `stream`, so it must not be made under
+ * graph capture (MOE_ERR_UNSUPPORTED if it is); later calls may be.  All
+ * calls on one GPU share the array and carry state from one call to the
+ * next: calls whose kernels overlap on one GPU (on different streams,
+ * or from different threads) race and give undefined results.  The GPU is
+ * the current device of the calling thread. */
+#define MOE_NOALLOC_SCRATCH_BYTES (2u * 1024u * 1024u)
+moe_status moe_stack_decode_residual_noalloc(const moe_dims *dims, const moe_layer *layers,
+                                             int32_t n_layers, float *resid, uint16_t *x_out,
+                                             float *y, int32_t *ids, float *w, void *stream);
+
 /* ---------------------------------------------------------------------------
  * Off-HBM expert tier ([HL], "How the SSD expert streaming pipeline works":
  * per token only the K routed experts of a layer are read from the slow tier,

@@ -166,3 +166,62 @@ def test_layer_decode_residual_validation():
     assert _status(f, **{**args, "d": moe.Dims(bits=3)}) == -3
     assert _status(f, **{**args, "ws_bytes": 256}) == -5
     assert _status(f, **{**args, "T": 4}) == -5   # workspace sized for T=1
+
+
+def test_stack_decode_validation():
+    f = moe.moe_stack_decode
+    args = dict(d=D, layers=[L_OK, L_OK], x=A, y=A + 65536, ids=None, w=None, ws=WS,
+                ws_bytes=moe.moe_workspace_bytes(D, 1), stream=0)
+    assert _status(f, **{**args, "x": None}) == -1
+    assert _status(f, **{**args, "layers": [L_OK, moe.make_layer(None, A, 7_077_888, A)]}) == -1
+    assert _status(f, **{**args, "layers": [L_OK, moe.make_layer(A + 8, A, 7_077_888, A)]}) == -4
+    assert _status(f, **{**args, "layers": []}) == -2
+    assert _status(f, **{**args, "y": A + 4}) == -4
+    assert _status(f, **{**args, "ws_bytes": 256}) == -5
+    assert _status(f, **{**args, "d": moe.Dims(bits=3)}) == -3
+
+
+@pytest.mark.parametrize("fn", ["moe_stack_decode_residual", "moe_stack_decode_residual_noalloc"])
+def test_stack_decode_residual_validation(fn):
+    # every check runs before the no-allocation variant's first HIP call
+    f = getattr(moe, fn)
+    args = dict(d=D, layers=[L_OK] * 3, resid=A, x_out=None, y=None, ids=None, w=None, stream=0)
+    if fn == "moe_stack_decode_residual":
+        args.update(ws=WS, ws_bytes=moe.moe_workspace_bytes(D, 1))
+    assert _status(f, **{**args, "resid": None}) == -1
+    assert _status(f, **{**args, "layers": [L_OK, moe.make_layer(A, None, 7_077_888, A)]}) == -1
+    assert _status(f, **{**args, "layers": []}) == -2
+    assert _status(f, **{**args, "resid": A + 4}) == -4
+    assert _status(f, **{**args, "x_out": A + 2}) == -4
+    assert _status(f, **{**args, "ids": A + 1}) == -4
+    assert _status(f, **{**args, "d": moe.Dims(group=32)}) == -3
+    nosh = moe.Dims(has_shared=0)
+    assert _status(f, **{**args, "d": nosh}) == -2   # layer has a shared blob
+
+
+def test_noalloc_scratch_covers_every_valid_dims():
+    # the one-token workspace of the largest dims fits the per-GPU array
+    worst = 0
+    for H in (256, 4096, 16384):
+        for I in (256, 1024, 16384):
+            for E in (1, 512, 1024):
+                for K in (1, 8):
+                    for bits in (2, 4):
+                        d = moe.Dims(hidden=H, inter=I, n_experts=E, top_k=min(K, E), bits=bits)
+                        worst = max(worst, moe.moe_workspace_bytes(d, 1))
+    assert 0 < worst <= moe.NOALLOC_SCRATCH_BYTES
+    hdr = open(HDR).read()
+    assert "#define MOE_NOALLOC_SCRATCH_BYTES (2u * 1024u * 1024u)" in hdr
+    assert moe.NOALLOC_SCRATCH_BYTES == 2 * 1024 * 1024
+
+
+def test_stream_read_and_flush_validation():
+    assert moe.moe_stream_read_sink_words(1 << 20) > 0
+    assert _status(moe.moe_stream_read, src=None, nbytes=4096, sink=A, stream=0) == -1
+    assert _status(moe.moe_stream_read, src=A, nbytes=4096, sink=None, stream=0) == -1
+    assert _status(moe.moe_stream_read, src=A, nbytes=0, sink=A, stream=0) == -2
+    assert _status(moe.moe_stream_read, src=A, nbytes=4100, sink=A, stream=0) == -2
+    assert _status(moe.moe_stream_read, src=A + 8, nbytes=4096, sink=A, stream=0) == -4
+    assert _status(moe.moe_flush, dst=None, nbytes=4096, stream=0) == -1
+    assert _status(moe.moe_flush, dst=A, nbytes=24, stream=0) == -2
+    assert _status(moe.moe_flush, dst=A + 4, nbytes=4096, stream=0) == -4
