@@ -283,6 +283,7 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
     if (xs < Gm::SEG_X) {
       float C = 0.f, X = 0.f;
       const uint32_t *xw = reinterpret_cast<const uint32_t *>(&xr[0]);
+      const int xkey = xp_key<PAIRS>(xs);
 #pragma unroll
       for (int wd = 0; wd < 4; ++wd) {
         constexpr int CPW = 32 / BITS;  // columns per code word
@@ -300,7 +301,7 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
           for (int p = 0; p < 4; ++p) {
             const float sc = (p & 1) ? 0.0625f : 1.f;
             const uint32_t pr = pack_h2(v[p] * sc, v[p + 4] * sc);
-            s_xp[xs][4 * wd + p] = pr;
+            s_xp[xs][(4 * wd + p) ^ xkey] = pr;
             C += h2_sum(pr);
           }
         } else {
@@ -309,7 +310,7 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
             const int e = k < 5 ? k : k - 5;
             const float sc = 1.f / (float)(1 << (2 * e));
             const uint32_t pr = pack_h2(v[k] * sc, v[k + 8] * sc);
-            s_xp[xs][8 * wd + k] = pr;
+            s_xp[xs][(8 * wd + k) ^ xkey] = pr;
             C += h2_sum(pr);
           }
         }
@@ -321,10 +322,11 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
 #pragma unroll
       for (int j = 0; j < LSEG; ++j) {
         const int sg = lane + 64 * j;
+        const int xk = xp_key<PAIRS>(sg);
         uint32_t xp[PAIRS];
 #pragma unroll
         for (int p = 0; p < PAIRS; p += 4) {
-          const uint4 q = *reinterpret_cast<const uint4 *>(&s_xp[sg][p]);
+          const uint4 q = *reinterpret_cast<const uint4 *>(&s_xp[sg][p ^ xk]);
           xp[p] = q.x;
           xp[p + 1] = q.y;
           xp[p + 2] = q.z;
@@ -440,7 +442,7 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
       if (!__all(ok)) return false;
 #pragma unroll
       for (int i = 0; i < NLD; ++i)
-        *reinterpret_cast<float2 *>(&s_hb[dst][128 * i + 2 * lane]) =
+        *reinterpret_cast<float2 *>(&s_hb[dst][hb_pos(128 * i + 2 * lane)]) =
             make_float2(__uint_as_float(t[i].x), __uint_as_float(t[i].z));
       lds_release();
       if (lane == 0) *lds(&s_hready[dst]) = 1u;
@@ -605,7 +607,8 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
     for (int ld = 0; ld < Gm::DLD; ++ld) accs[ld] = 0.f;
     if (a.has_shared) {
       if (!xchg) wait_lds(&s_hready[0], 1u);
-      down_rows<BITS, Gm::DLD, Gm::DWORDS, Gm::DCOLS>(dqs, dsbs, &s_hb[0][seg * Gm::DCOLS], 1.f, accs);
+      down_rows<BITS, Gm::DLD, Gm::DWORDS, Gm::DCOLS>(dqs, dsbs, &s_hb[0][seg * Gm::DCOLS],
+                                                      hb_key(seg), 1.f, accs);
     }
     // own routed rows, then their sums to the workgroups that own the rows:
     // lane 2 ld + j of the wave stores row obase + 2 ld + j
@@ -615,7 +618,8 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
       float acco[Gm::RDLD];
 #pragma unroll
       for (int ld = 0; ld < Gm::RDLD; ++ld) acco[ld] = 0.f;
-      down_rows<BITS, Gm::RDLD, Gm::DWORDS, Gm::DCOLS>(dqr, dsbr, &s_hb[1][seg * Gm::DCOLS], wko, acco);
+      down_rows<BITS, Gm::RDLD, Gm::DWORDS, Gm::DCOLS>(dqr, dsbr, &s_hb[1][seg * Gm::DCOLS],
+                                                       hb_key(seg), wko, acco);
       static_assert(Gm::RPL == 2 && Gm::LPR == 32, "two rows per wave-wide load");
       float pv = 0.f;
 #pragma unroll

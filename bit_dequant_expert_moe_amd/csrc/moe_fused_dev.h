@@ -24,6 +24,30 @@ constexpr int kNT = 64 * (kGuWaves + kDownWaves);
 constexpr long kSpinMax = 1L << 18;
 constexpr float kRmsEps = 1e-6f;  // epsilon of the pre-MoE RMS norm
 
+// LDS layouts of the activations h and the packed x pairs, swizzled per
+// 16-byte chunk (1) or plain (0).  A reader lane takes one run of 16-byte
+// chunks (h: 32 values of one down lane; x pairs: one gate/up segment) and the
+// runs of neighbouring lanes are 64 or 128 bytes apart, so the lanes of one
+// ds_read_b128 would all hit the same banks; storing chunk c of run n at
+// chunk position c ^ key(n) spreads them over all banks.  Only addresses
+// change: every value is read into the same register as before.
+#ifndef MOE_LDS_SWIZZLE
+#define MOE_LDS_SWIZZLE 1
+#endif
+// Float position of element i of one slot's h (runs of 32 floats = 8 chunks).
+__device__ __forceinline__ int hb_pos(int i) {
+  return MOE_LDS_SWIZZLE ? (i ^ (((i >> 5) & 7) << 2)) : i;
+}
+// XOR applied to the float offsets within down lane `seg`'s run of h.
+__device__ __forceinline__ int hb_key(int seg) { return MOE_LDS_SWIZZLE ? (seg & 7) << 2 : 0; }
+// Word position of pair j of x segment sg (PAIRS words per segment).
+template <int PAIRS>
+__device__ __forceinline__ int xp_key(int sg) {
+  static_assert(PAIRS == 16 || PAIRS == 32, "4 or 8 chunks per segment");
+  if (!MOE_LDS_SWIZZLE) return 0;
+  return (PAIRS == 32 ? (sg & 7) : ((sg >> 1) & 3)) << 2;
+}
+
 typedef __attribute__((address_space(3))) volatile uint32_t lds_u32;
 
 __device__ __forceinline__ lds_u32 *lds(uint32_t *p) { return (lds_u32 *)(p); }
@@ -58,6 +82,81 @@ __device__ __forceinline__ uint4 ld_coh16(const void *base, uint32_t byte_off) {
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, 0x7fffffff, 0x00020000);
   const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 16 /* sc1 */);
   return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// Polling with NP requests in flight.  A coherent poll takes about a
+// microsecond to come back; one that finds the data incomplete would cost a
+// whole round trip more.  Here the first M polls are issued GAP sleep units
+// (64 clocks each) apart with NP of them in flight: they are checked in
+// issue order and each incomplete one is followed at once by the next, so
+// completion is seen about one round trip after it happens, plus up to one
+// gap.  (The M polls are straight-line code: the compiler keeps no load in
+// flight across a loop back-edge, where it would copy the registers and wait
+// for the load first.)  After them, one poll at a time until the budget runs
+// out.
+//   issue(u): loads one poll's words into u (NW 16-byte words per lane)
+//   ok(u):    whether they are complete (the same on every lane)
+//   take(u):  consumes them
+// Returns false when the spin budget runs out (take() then gets the last,
+// incomplete, words).  Polls still in flight at the return are left to
+// complete; the compiler waits for them before it reuses their registers.
+template <int NW>
+__device__ __forceinline__ void launder(uint4 (&u)[NW]) {
+  // an empty volatile asm that reads and writes the words (each 16-byte word
+  // as one 128-bit register operand): the wait for their load lands here,
+  // and nothing computed from them moves above it
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    u32x4 v = {u[i].x, u[i].y, u[i].z, u[i].w};
+    __asm__ volatile("" : "+v"(v));
+    u[i] = make_uint4(v[0], v[1], v[2], v[3]);
+  }
+}
+template <int NP, int M, int GAP, int NW, typename Issue, typename Ok, typename Take>
+__device__ __forceinline__ bool poll_pipe(Issue &&issue, Ok &&ok, Take &&take, long &spins) {
+  static_assert(NP >= 1 && M >= NP, "M polls, NP of them in flight");
+  uint4 u[NP][NW];
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    if (j) __builtin_amdgcn_s_sleep(GAP);
+    // (the barrier keeps the compiler from merging a poll with an earlier
+    // one of the same words)
+    __asm__ volatile("" ::: "memory");
+    issue(u[j]);
+  }
+  // (a complete poll returns at once: a path that went on would meet the
+  // path that issued a poll again, and the compiler would copy the words in
+  // flight there, waiting for them)
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int j = m % NP;
+    launder(u[j]);
+    if (ok(u[j])) {
+      take(u[j]);
+      return true;
+    }
+    if (m + NP < M) {
+      __asm__ volatile("" ::: "memory");
+      issue(u[j]);
+    }
+  }
+  spins += M;
+  uint4 w[NW];
+  while (true) {
+    __builtin_amdgcn_s_sleep(1);
+    __asm__ volatile("" ::: "memory");
+    issue(w);
+    launder(w);
+    if (ok(w)) {
+      take(w);
+      return true;
+    }
+    if (++spins > kSpinMax) {
+      take(w);
+      return false;
+    }
+  }
 }
 
 // 8-byte coherent load, the same policy.
@@ -199,12 +298,12 @@ __device__ __forceinline__ float word_dot_f32(uint32_t u, const float *hv, float
 }
 
 // Lane partial sums of N down rows, one code load per row and lane, against
-// the activations of the lane's DCOLS columns (hb, in LDS):
+// the activations of the lane's DCOLS columns (hb, in LDS, offsets XOR key):
 // acc += wk (s sum_c q_c h_c + z sum_c h_c) with the row's group scale s and
 // bias z.  One code word's activations are read from LDS at a time.
 template <int BITS, int N, int DWORDS, int DCOLS>
 __device__ __forceinline__ void down_rows(const uint4 (&dq)[N], const uint32_t (&dsb)[N],
-                                          const float *hb, float wk, float (&acc)[N]) {
+                                          const float *hb, int key, float wk, float (&acc)[N]) {
   constexpr int CPW = 32 / BITS;  // codes per word
   uint32_t m = BITS == 4 ? 0x0F0F0F0Fu : 0x03030303u;
   asm volatile("" : "+s"(m));
@@ -218,7 +317,7 @@ __device__ __forceinline__ void down_rows(const uint4 (&dq)[N], const uint32_t (
     float hv[CPW];
 #pragma unroll
     for (int t = 0; t < CPW / 4; ++t) {
-      const float4 v = *reinterpret_cast<const float4 *>(hb + CPW * wd + 4 * t);
+      const float4 v = *reinterpret_cast<const float4 *>(hb + ((CPW * wd + 4 * t) ^ key));
       hv[4 * t] = v.x;
       hv[4 * t + 1] = v.y;
       hv[4 * t + 2] = v.z;

@@ -95,12 +95,12 @@ struct StackArgs {
 // Timestamps of the layer's steps, per workgroup, for a build with
 // MOE_STACK_TRACE defined (the trace buffer's device address sits in the
 // workspace control block); empty otherwise.
+// They are kept in LDS and copied out when the kernel ends, so that taking
+// them adds no global store for a later wait on the vector memory counter.
 #ifdef MOE_STACK_TRACE
-#define MOE_TRACE(ev)                                                              \
-  do {                                                                             \
-    if (trace && lane == 0)                                                        \
-      trace[((size_t)b * kMaxStackLayers + l) * 32 + (ev)] =                       \
-          __builtin_amdgcn_s_memrealtime();                                         \
+#define MOE_TRACE(ev)                                                          \
+  do {                                                                         \
+    if (lane == 0) s_tr[l * 32 + (ev)] = __builtin_amdgcn_s_memrealtime();     \
   } while (0)
 #else
 #define MOE_TRACE(ev) \
@@ -108,11 +108,46 @@ struct StackArgs {
   } while (0)
 #endif
 
+// Which rows of each matrix a workgroup owns: 0 a contiguous block (rows
+// b n .. b n + n - 1), 1 every 256th row from b (rows b, b + 256, ...), which
+// spreads each workgroup's bytes over the whole matrix.
+#ifndef MOE_STACK_ILV
+#define MOE_STACK_ILV 0
+#endif
+
 // When the gate/up waves request the next layer's routing-independent bytes:
 // 0 right after the shared expert's gate/up products (during the logits
 // exchange), 1 right after the routed loads, 2 after the routed products.
 #ifndef MOE_STACK_PF
-#define MOE_STACK_PF 0
+#define MOE_STACK_PF 2
+#endif
+
+// When the down-row waves load the next layer's shared-expert rows: 0 at the
+// start of that layer (just before its routing), 1 as soon as they have
+// computed the current layer's shared rows (their registers are free then),
+// so that those loads are not in the memory pipeline when the logits poll
+// of the next layer is issued (measured: no faster).
+#ifndef MOE_STACK_RPF
+#define MOE_STACK_RPF 0
+#endif
+
+// Polls in flight and their spacing (sleep units of 64 clocks) of the
+// exchange wave's three waits: every workgroup's logits, one slot's
+// activations, and (residual mode) every workgroup's done word.
+// (Measured: one poll at a time is fastest.  With more in flight, a poll
+// that succeeds waits for the later ones before their registers are reused,
+// and the extra coherent reads of the same lines slow every poll.)
+#ifndef MOE_STACK_LOGIT_POLLS
+#define MOE_STACK_LOGIT_POLLS 1
+#endif
+#ifndef MOE_STACK_H_POLLS
+#define MOE_STACK_H_POLLS 1
+#endif
+#ifndef MOE_STACK_R_POLLS
+#define MOE_STACK_R_POLLS 1
+#endif
+#ifndef MOE_STACK_POLL_GAP
+#define MOE_STACK_POLL_GAP 8
 #endif
 
 // A layer's pointers read from LDS, made wave-uniform (scalar registers), so
@@ -185,6 +220,9 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
   // load of a later layer's entry from the argument segment can miss the
   // scalar cache and cost a memory round trip on the routing path)
   __shared__ StackLayer s_L[kMaxStackLayers];
+#ifdef MOE_STACK_TRACE
+  __shared__ uint64_t s_tr[kMaxStackLayers * 32];
+#endif
 
   const int b = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int grp = b % kGroups;
@@ -193,7 +231,10 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
 
 #ifdef MOE_STACK_TRACE
   uint64_t *trace = *reinterpret_cast<uint64_t *const *>(&a.ctrl->pad[0]);
+  for (int i = tid; i < kMaxStackLayers * 32; i += kNT) s_tr[i] = 0;
 #endif
+  // the router row `row` of this workgroup (an expert index)
+  auto router_row = [&](int row) -> int { return MOE_STACK_ILV ? row * kG + b : b * RR + row; };
   constexpr int kEpochTid = kNT - 64;
   uint32_t epoch_done = (uint32_t)a.E;
   if (tid == kEpochTid) epoch_done = ld_rlx(&a.fc->epoch[grp][0]);
@@ -215,7 +256,7 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
   // ---- residual mode: r of this thread's chunk (8 columns) and the norm ----
   // layer 0 reads the caller's r; layer l > 0 gathers r + y of layer l-1
   // from the row owners' tagged words (this group's copy)
-  float4 rf[RES ? 2 : 1];
+  float4 rf[2];  // (used in residual mode only)
   uint4 rx_own;  // bf16 x of chunk tid (residual mode)
   auto gather_r = [&](int l, uint32_t epoch_prev) {
     if (l == 0) {
@@ -231,20 +272,21 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
     if (wave == kGuWaves) {
       long spins = 0;
       const uint32_t base = (uint32_t)((size_t)grp * kG * 8);
-      while (true) {
-        bool ok = true;
+      constexpr int NWD = kG / 128;
+      const bool done = poll_pipe<MOE_STACK_R_POLLS, 8, MOE_STACK_POLL_GAP, NWD>(
+          [&](uint4 (&u)[NWD]) {
 #pragma unroll
-        for (int i = 0; i < kG / 128; ++i) {
-          const uint4 t = ld_coh16(a.rdone, base + (uint32_t)(128 * i + 2 * lane) * 8u);
-          ok &= t.y == epoch_prev && t.w == epoch_prev;
-        }
-        if (__all(ok)) break;
-        if (++spins > kSpinMax) {
-          if (lane == 0) atomicOr(&a.ctrl->err, 2u);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
-      }
+            for (int i = 0; i < NWD; ++i)
+              u[i] = ld_coh16(a.rdone, base + (uint32_t)(128 * i + 2 * lane) * 8u);
+          },
+          [&](const uint4 (&u)[NWD]) {
+            bool ok = true;
+#pragma unroll
+            for (int i = 0; i < NWD; ++i) ok &= u[i].y == epoch_prev && u[i].w == epoch_prev;
+            return __all(ok) != 0;
+          },
+          [&](const uint4 (&)[NWD]) {}, spins);
+      if (!done && lane == 0) atomicOr(&a.ctrl->err, 2u);
       lds_release();
       if (lane == 0) *lds(&s_rseen) = (uint32_t)l;
     }
@@ -304,7 +346,8 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
     // thread t holds the router rows' chunks t and t + kNT / 2 (x columns
     // 8 t .. 8 t + 7 and the same 2048 columns further), i.e. the chunks of
     // the threads t of waves `wave` and `wave + 4` of k_layer1
-    const int r = b * Gm::GU_ROWS + wave;  // this wave's row of every slot
+    // this wave's row of every slot
+    const int r = MOE_STACK_ILV ? wave * kG + b : b * Gm::GU_ROWS + wave;
     const size_t rbytes = (size_t)H * BITS / 8;
     const int groups = H / kGroup;
     const int xs = tid;  // x segment staged by this thread (if < SEG_X)
@@ -338,7 +381,7 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
       const StackLayer Ly = uniform_layer(s_L[l]);
 #pragma unroll
       for (int row = 0; row < RR; ++row) {
-        const int e = b * rr + row;
+        const int e = router_row(row);
         // rows past E read row E-1 and are never published
         const int ec = e < a.E ? e : a.E - 1;
 #pragma unroll
@@ -399,6 +442,7 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
       if (xs < Gm::SEG_X) {
         float C = 0.f, X = 0.f;
         const uint32_t *xw = reinterpret_cast<const uint32_t *>(&xr[0]);
+        const int xkey = xp_key<PAIRS>(xs);
 #pragma unroll
         for (int wd = 0; wd < 4; ++wd) {
           constexpr int CPW = 32 / BITS;
@@ -416,7 +460,7 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
             for (int p = 0; p < 4; ++p) {
               const float sc = (p & 1) ? 0.0625f : 1.f;
               const uint32_t pr = pack_h2(v[p] * sc, v[p + 4] * sc);
-              s_xp[buf][xs][4 * wd + p] = pr;
+              s_xp[buf][xs][(4 * wd + p) ^ xkey] = pr;
               C += h2_sum(pr);
             }
           } else {
@@ -425,7 +469,7 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
               const int e = k < 5 ? k : k - 5;
               const float sc = 1.f / (float)(1 << (2 * e));
               const uint32_t pr = pack_h2(v[k] * sc, v[k + 8] * sc);
-              s_xp[buf][xs][8 * wd + k] = pr;
+              s_xp[buf][xs][(8 * wd + k) ^ xkey] = pr;
               C += h2_sum(pr);
             }
           }
@@ -437,10 +481,11 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
 #pragma unroll
         for (int j = 0; j < LSEG; ++j) {
           const int sg = lane + 64 * j;
+          const int xk = xp_key<PAIRS>(sg);
           uint32_t xp[PAIRS];
 #pragma unroll
           for (int p = 0; p < PAIRS; p += 4) {
-            const uint4 q = *reinterpret_cast<const uint4 *>(&s_xp[buf][sg][p]);
+            const uint4 q = *reinterpret_cast<const uint4 *>(&s_xp[buf][sg][p ^ xk]);
             xp[p] = q.x;
             xp[p + 1] = q.y;
             xp[p + 2] = q.z;
@@ -462,7 +507,7 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
       const uint32_t epoch = s_epoch + 1u + (uint32_t)l;
       auto publish = [&](int slot, float hv) {
         if (lane < kGroups)
-          __hip_atomic_store(&a.htag[((size_t)lane * NSL + slot) * I + b * Gm::GU_ROWS + wave],
+          __hip_atomic_store(&a.htag[((size_t)lane * NSL + slot) * I + r],
                              ((uint64_t)epoch << 32) | (uint64_t)__float_as_uint(hv),
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (lane == 0)
@@ -519,7 +564,7 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
       // 1. this workgroup's logits, one copy per reader group (the sums of
       //    the eight partials in wave order)
       if (lane < kGroups * rr) {
-        const int rep = lane / rr, row = lane % rr, e = b * rr + row;
+        const int rep = lane / rr, row = lane % rr, e = router_row(row);
         if (e < a.E) {
           float lg = 0.f;
 #pragma unroll
@@ -542,31 +587,35 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
 #ifdef MOE_STACK_TRACE
         int npoll = 0;
 #endif
-        while (true) {
-          uint4 t[NV / 2];
+        const bool done = poll_pipe<MOE_STACK_LOGIT_POLLS, 8, MOE_STACK_POLL_GAP, NV / 2>(
+            [&](uint4 (&t)[NV / 2]) {
 #pragma unroll
-          for (int i = 0; i < NV / 2; ++i)
-            t[i] = ld_coh16(tags_mine, (uint32_t)(128 * i + 2 * lane) * 8u);
+              for (int i = 0; i < NV / 2; ++i)
+                t[i] = ld_coh16(tags_mine, (uint32_t)(128 * i + 2 * lane) * 8u);
 #ifdef MOE_STACK_TRACE
-          if (npoll++ == 0) MOE_TRACE(25);
-          if (trace && lane == 0)
-            trace[((size_t)b * kMaxStackLayers + l) * 32 + 26] = (uint64_t)npoll * 100;
+              if (npoll++ == 0) MOE_TRACE(25);
+              if (lane == 0) s_tr[l * 32 + 26] = (uint64_t)npoll * 100;
 #endif
-          bool ok = true;
+            },
+            [&](const uint4 (&t)[NV / 2]) {
+              bool ok = true;
 #pragma unroll
-          for (int i = 0; i < NV / 2; ++i) {
-            const int idx = 128 * i + 2 * lane;
-            ok &= (idx >= a.E || t[i].y == epoch) && (idx + 1 >= a.E || t[i].w == epoch);
-            v[2 * i] = idx < a.E ? __uint_as_float(t[i].x) : __builtin_nanf("");
-            v[2 * i + 1] = idx + 1 < a.E ? __uint_as_float(t[i].z) : __builtin_nanf("");
-          }
-          if (__all(ok)) break;
-          if (++xspins > kSpinMax) {
-            if (lane == 0) atomicOr(&a.ctrl->err, 2u);
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
-        }
+              for (int i = 0; i < NV / 2; ++i) {
+                const int idx = 128 * i + 2 * lane;
+                ok &= (idx >= a.E || t[i].y == epoch) && (idx + 1 >= a.E || t[i].w == epoch);
+              }
+              return __all(ok) != 0;
+            },
+            [&](const uint4 (&t)[NV / 2]) {
+#pragma unroll
+              for (int i = 0; i < NV / 2; ++i) {
+                const int idx = 128 * i + 2 * lane;
+                v[2 * i] = idx < a.E ? __uint_as_float(t[i].x) : __builtin_nanf("");
+                v[2 * i + 1] = idx + 1 < a.E ? __uint_as_float(t[i].z) : __builtin_nanf("");
+              }
+            },
+            xspins);
+        if (!done && lane == 0) atomicOr(&a.ctrl->err, 2u);
         // key = (order-preserving logit bits, ~index): the largest key is the
         // largest logit, and among equal logits the lowest index
         uint64_t key[NV];
@@ -610,38 +659,41 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
         MOE_TRACE(2);
       }
       // 3. activations of slot `slot` from this group's copy into s_hb[slot]
-      //    once every entry carries this layer's epoch
-      auto try_consume = [&](int slot) -> bool {
-        constexpr int NLD = I / 128;  // 16-byte loads per lane (two entries each)
-        uint4 t[NLD];
-        const uint32_t base = (uint32_t)(((size_t)grp * NSL + slot) * I * 8);
-#pragma unroll
-        for (int i = 0; i < NLD; ++i)
-          t[i] = ld_coh16(a.htag, base + (uint32_t)(128 * i + 2 * lane) * 8u);
-        bool ok = true;
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) ok &= t[i].y == epoch && t[i].w == epoch;
-        if (!__all(ok)) return false;
-#pragma unroll
-        for (int i = 0; i < NLD; ++i)
-          *reinterpret_cast<float2 *>(&s_hb[slot][128 * i + 2 * lane]) =
-              make_float2(__uint_as_float(t[i].x), __uint_as_float(t[i].z));
-        return true;
-      };
-      // a routed slot is polled only once this workgroup has published its
-      // own rows of it (the others publish at about the same time)
+      //    once every entry carries this layer's epoch; a routed slot is
+      //    polled only once this workgroup has published its own rows of it
+      //    (the others publish at about the same time)
       for (int j = 0; j < NSL; ++j) {
         const int slot = j == 0 ? K : j - 1;
         if (slot == K && !a.has_shared) continue;
-        while (true) {
-          const bool own = slot == K || *lds(&s_cnt[slot]) >= (uint32_t)kGuWaves * want;
-          if (own && try_consume(slot)) break;
-          if (++xspins > kSpinMax) {
-            if (lane == 0) atomicOr(&a.ctrl->err, 2u);
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
-        }
+        if (slot != K) wait_lds(&s_cnt[slot], (uint32_t)kGuWaves * want);
+        constexpr int NLD = I / 128;  // 16-byte loads per lane (two entries each)
+        const uint32_t base = (uint32_t)(((size_t)grp * NSL + slot) * I * 8);
+        const bool done = poll_pipe<MOE_STACK_H_POLLS, 6, MOE_STACK_POLL_GAP, NLD>(
+            [&](uint4 (&t)[NLD]) {
+#pragma unroll
+              for (int i = 0; i < NLD; ++i)
+                t[i] = ld_coh16(a.htag, base + (uint32_t)(128 * i + 2 * lane) * 8u);
+            },
+            [&](const uint4 (&t)[NLD]) {
+              bool ok = true;
+#pragma unroll
+              for (int i = 0; i < NLD; ++i) ok &= t[i].y == epoch && t[i].w == epoch;
+              return __all(ok) != 0;
+            },
+            [&](const uint4 (&t)[NLD]) {
+              // two 4-byte stores per word (one 8-byte store would need the
+              // two values in adjacent registers, and the compiler would move
+              // them there right after the load, waiting for it)
+              volatile float *hs = &s_hb[slot][0];
+#pragma unroll
+              for (int i = 0; i < NLD; ++i) {
+                const int e = hb_pos(128 * i + 2 * lane);
+                hs[e] = __uint_as_float(t[i].x);
+                hs[e + 1] = __uint_as_float(t[i].z);
+              }
+            },
+            xspins);
+        if (!done && lane == 0) atomicOr(&a.ctrl->err, 2u);
         lds_release();
         if (lane == 0) *lds(&s_hready[slot]) = want;
         if (slot == K) MOE_TRACE(3);
@@ -655,9 +707,10 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
                          __HIP_MEMORY_SCOPE_AGENT);
   } else {
     // =========================== down-row waves ===============================
-    // The workgroup owns y rows b D_ROWS .. + D_ROWS (16); waves 5, 6, 7 take
-    // 6, 6 and 4 of them, two rows per wave-wide load (32 lanes each, 32
-    // codes per lane), and compute those rows of every slot: the shared
+    // The workgroup owns 16 y rows (a block, or every 256th row: the
+    // MOE_STACK_ILV choice); waves 5, 6, 7 take 6, 6 and 4 of them, two rows
+    // per wave-wide load (32 lanes each, 32 codes per lane), and compute
+    // those rows of every slot: the shared
     // expert's as soon as its activations are in, then routed slot k's as
     // soon as slot k's are.  Each row's sum is formed as in k_layer1 (the
     // same lanes, products and reductions): y = shared + slot 0 + .. +
@@ -673,11 +726,14 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
     auto o_dsb = [&](int row) -> uint32_t {
       return (uint32_t)(a.off_dsb + ((int64_t)row * groups + seg * Gm::DCOLS / kGroup) * 4);
     };
-    auto row_wave = [&](auto n_tag, int row0) {
+    auto row_wave = [&](auto n_tag, int j0) {
       constexpr int N = decltype(n_tag)::value;  // wave-wide loads (row pairs) per slot
       int rows[N];
 #pragma unroll
-      for (int ld = 0; ld < N; ++ld) rows[ld] = row0 + 2 * ld + lane / Gm::LPR;
+      for (int ld = 0; ld < N; ++ld) {
+        const int j = j0 + 2 * ld + lane / Gm::LPR;  // the workgroup's j-th row
+        rows[ld] = MOE_STACK_ILV ? j * kG + b : b * Gm::D_ROWS + j;
+      }
       // residual mode: r of this lane's rows, kept across layers
       float rres[RES ? N : 1];
       if (RES) {
@@ -709,8 +765,9 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
         }
         // the shared expert's rows (without one, slot K reads expert 0 and
         // is never used)
-        load_slot(std::integral_constant<int, kPolShared>{}, K,
-                  a.has_shared ? Ly.shared : Ly.experts);
+        if (MOE_STACK_RPF == 0 || l == 0)
+          load_slot(std::integral_constant<int, kPolShared>{}, K,
+                    a.has_shared ? Ly.shared : Ly.experts);
         if (l == 0 && tid == kEpochTid) s_epoch = epoch_done;
         lds_barrier();  // (A)
         const uint32_t want = (uint32_t)(l + 1);
@@ -738,10 +795,15 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
 #pragma unroll
           for (int ld = 0; ld < N; ++ld) acc[ld] = 0.f;
           down_rows<BITS, N, Gm::DWORDS, Gm::DCOLS>(dq[K], dsb[K], &s_hb[K][seg * Gm::DCOLS],
+                                                     hb_key(seg),
                                                      1.f, acc);
 #pragma unroll
           for (int ld = 0; ld < N; ++ld) v[ld] = lane_group_sum<Gm::LPR>(acc[ld], lane);
           if (cw == 0) MOE_TRACE(20);
+        }
+        if (MOE_STACK_RPF == 1 && l + 1 < NL && a.has_shared) {
+          const StackLayer Ln = uniform_layer(s_L[l + 1]);
+          load_slot(std::integral_constant<int, kPolShared>{}, K, Ln.shared);
         }
 #pragma unroll
         for (int k = 0; k < K; ++k) {
@@ -750,6 +812,7 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
 #pragma unroll
           for (int ld = 0; ld < N; ++ld) acc[ld] = 0.f;
           down_rows<BITS, N, Gm::DWORDS, Gm::DCOLS>(dq[k], dsb[k], &s_hb[k][seg * Gm::DCOLS],
+                                                     hb_key(seg),
                                                      wk[k], acc);
 #pragma unroll
           for (int ld = 0; ld < N; ++ld) v[ld] += lane_group_sum<Gm::LPR>(acc[ld], lane);
@@ -789,9 +852,14 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
         if (cw == 0) MOE_TRACE(7);
       }
     };
-    if (cw < 2) row_wave(std::integral_constant<int, 3>{}, b * Gm::D_ROWS + 6 * cw);
-    else row_wave(std::integral_constant<int, 2>{}, b * Gm::D_ROWS + 12);
+    if (cw < 2) row_wave(std::integral_constant<int, 3>{}, 6 * cw);
+    else row_wave(std::integral_constant<int, 2>{}, 12);
   }
+#ifdef MOE_STACK_TRACE
+  __syncthreads();
+  if (trace)
+    for (int i = tid; i < NL * 32; i += kNT) trace[(size_t)b * kMaxStackLayers * 32 + i] = s_tr[i];
+#endif
 }
 
 inline hipStream_t S(void *s) { return static_cast<hipStream_t>(s); }
