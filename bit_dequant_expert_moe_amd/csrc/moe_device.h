@@ -114,6 +114,32 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
   return m;
 }
 
+// Maximum of a 32-bit value over the wave (wave-uniform result).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t k) {
+  k = max(k, dpp_u<0xB1>(k));
+  k = max(k, dpp_u<0x4E>(k));
+  k = max(k, dpp_u<0x141>(k));
+  k = max(k, dpp_u<0x140>(k));
+  uint32_t m = (uint32_t)__builtin_amdgcn_readlane(k, 0);
+  m = max(m, (uint32_t)__builtin_amdgcn_readlane(k, 16));
+  m = max(m, (uint32_t)__builtin_amdgcn_readlane(k, 32));
+  m = max(m, (uint32_t)__builtin_amdgcn_readlane(k, 48));
+  return m;
+}
+
+// Minimum of a 32-bit value over the wave (wave-uniform result).
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t k) {
+  k = min(k, dpp_u<0xB1>(k));
+  k = min(k, dpp_u<0x4E>(k));
+  k = min(k, dpp_u<0x141>(k));
+  k = min(k, dpp_u<0x140>(k));
+  uint32_t m = (uint32_t)__builtin_amdgcn_readlane(k, 0);
+  m = min(m, (uint32_t)__builtin_amdgcn_readlane(k, 16));
+  m = min(m, (uint32_t)__builtin_amdgcn_readlane(k, 32));
+  m = min(m, (uint32_t)__builtin_amdgcn_readlane(k, 48));
+  return m;
+}
+
 // Order-preserving map of an fp32 value to uint32 (NaN -> 0, i.e. below all).
 __device__ __forceinline__ uint32_t f32_order_key(float f) {
   if (f != f) return 0u;

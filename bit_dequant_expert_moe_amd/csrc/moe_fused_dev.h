@@ -97,6 +97,8 @@ __device__ __forceinline__ uint4 ld_coh16(const void *base, uint32_t byte_off) {
 //   issue(u): loads one poll's words into u (NW 16-byte words per lane)
 //   ok(u):    whether they are complete (the same on every lane)
 //   take(u):  consumes them
+//   first():  runs once, right after the first poll is issued (e.g. to let
+//             other waves queue their loads behind it)
 // Returns false when the spin budget runs out (take() then gets the last,
 // incomplete, words).  Polls still in flight at the return are left to
 // complete; the compiler waits for them before it reuses their registers.
@@ -113,8 +115,10 @@ __device__ __forceinline__ void launder(uint4 (&u)[NW]) {
     u[i] = make_uint4(v[0], v[1], v[2], v[3]);
   }
 }
-template <int NP, int M, int GAP, int NW, typename Issue, typename Ok, typename Take>
-__device__ __forceinline__ bool poll_pipe(Issue &&issue, Ok &&ok, Take &&take, long &spins) {
+template <int NP, int M, int GAP, int NW, typename Issue, typename Ok, typename Take,
+          typename First>
+__device__ __forceinline__ bool poll_pipe(Issue &&issue, Ok &&ok, Take &&take, long &spins,
+                                          First &&first) {
   static_assert(NP >= 1 && M >= NP, "M polls, NP of them in flight");
   uint4 u[NP][NW];
 #pragma unroll
@@ -124,6 +128,7 @@ __device__ __forceinline__ bool poll_pipe(Issue &&issue, Ok &&ok, Take &&take, l
     // one of the same words)
     __asm__ volatile("" ::: "memory");
     issue(u[j]);
+    if (j == 0) first();
   }
   // (a complete poll returns at once: a path that went on would meet the
   // path that issued a poll again, and the compiler would copy the words in
@@ -157,6 +162,11 @@ __device__ __forceinline__ bool poll_pipe(Issue &&issue, Ok &&ok, Take &&take, l
       return false;
     }
   }
+}
+
+template <int NP, int M, int GAP, int NW, typename Issue, typename Ok, typename Take>
+__device__ __forceinline__ bool poll_pipe(Issue &&issue, Ok &&ok, Take &&take, long &spins) {
+  return poll_pipe<NP, M, GAP, NW>(issue, ok, take, spins, [] {});
 }
 
 // 8-byte coherent load, the same policy.

@@ -97,10 +97,11 @@ struct StackArgs {
 // workspace control block); empty otherwise.
 // They are kept in LDS and copied out when the kernel ends, so that taking
 // them adds no global store for a later wait on the vector memory counter.
+constexpr int kTrEv = 48;  // events per (workgroup, layer)
 #ifdef MOE_STACK_TRACE
 #define MOE_TRACE(ev)                                                          \
   do {                                                                         \
-    if (lane == 0) s_tr[l * 32 + (ev)] = __builtin_amdgcn_s_memrealtime();     \
+    if (lane == 0) s_tr[l * kTrEv + (ev)] = __builtin_amdgcn_s_memrealtime();  \
   } while (0)
 #else
 #define MOE_TRACE(ev) \
@@ -130,6 +131,15 @@ struct StackArgs {
 #ifndef MOE_STACK_RPF
 #define MOE_STACK_RPF 0
 #endif
+
+// Copies of every exchanged datum (logits, activations, r + y, done words):
+// a reader reads copy b % kCopies, a writer stores into all of them.  The
+// workgroups b with the same b % 8 share an XCD (and its L2).
+#ifndef MOE_STACK_COPIES
+#define MOE_STACK_COPIES 8
+#endif
+constexpr int kCopies = MOE_STACK_COPIES;
+static_assert(kCopies >= 1 && kCopies <= kGroups && kGroups % kCopies == 0, "copies");
 
 // Polls in flight and their spacing (sleep units of 64 clocks) of the
 // exchange wave's three waits: every workgroup's logits, one slot's
@@ -221,23 +231,23 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
   // scalar cache and cost a memory round trip on the routing path)
   __shared__ StackLayer s_L[kMaxStackLayers];
 #ifdef MOE_STACK_TRACE
-  __shared__ uint64_t s_tr[kMaxStackLayers * 32];
+  __shared__ uint64_t s_tr[kMaxStackLayers * kTrEv];
 #endif
 
   const int b = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int grp = b % kGroups;
+  const int grp = b % kCopies;  // the exchange copy this workgroup reads
   const int NL = a.n_layers;
   constexpr int rr = RR;  // router rows per workgroup (E <= RR * kG)
 
 #ifdef MOE_STACK_TRACE
   uint64_t *trace = *reinterpret_cast<uint64_t *const *>(&a.ctrl->pad[0]);
-  for (int i = tid; i < kMaxStackLayers * 32; i += kNT) s_tr[i] = 0;
+  for (int i = tid; i < kMaxStackLayers * kTrEv; i += kNT) s_tr[i] = 0;
 #endif
   // the router row `row` of this workgroup (an expert index)
   auto router_row = [&](int row) -> int { return MOE_STACK_ILV ? row * kG + b : b * RR + row; };
   constexpr int kEpochTid = kNT - 64;
   uint32_t epoch_done = (uint32_t)a.E;
-  if (tid == kEpochTid) epoch_done = ld_rlx(&a.fc->epoch[grp][0]);
+  if (tid == kEpochTid) epoch_done = ld_rlx(&a.fc->epoch[b % kGroups][0]);
   if (tid < NSL) {
     s_cnt[tid] = 0u;
     s_hready[tid] = 0u;
@@ -506,7 +516,7 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
       if (wave == 0) MOE_TRACE(8);
       const uint32_t epoch = s_epoch + 1u + (uint32_t)l;
       auto publish = [&](int slot, float hv) {
-        if (lane < kGroups)
+        if (lane < kCopies)
           __hip_atomic_store(&a.htag[((size_t)lane * NSL + slot) * I + r],
                              ((uint64_t)epoch << 32) | (uint64_t)__float_as_uint(hv),
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -561,19 +571,9 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
       const uint32_t epoch = s_epoch + 1u + (uint32_t)l;
       const uint32_t want = (uint32_t)(l + 1);  // LDS flag value of this layer
       long xspins = 0;  // one poll budget per layer
-      // 1. this workgroup's logits, one copy per reader group (the sums of
-      //    the eight partials in wave order)
-      if (lane < kGroups * rr) {
-        const int rep = lane / rr, row = lane % rr, e = router_row(row);
-        if (e < a.E) {
-          float lg = 0.f;
-#pragma unroll
-          for (int w = 0; w < NW; ++w) lg += s_red[w][row];
-          const uint64_t v = ((uint64_t)epoch << 32) | (uint64_t)__float_as_uint(lg);
-          __hip_atomic_store(&a.tags[(size_t)rep * kMaxE + e], v, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-        }
-      }
+      // 1. (this workgroup's logits are published by the last down-row
+      //    wave: this wave issues no stores, since a later wait of its
+      //    memory counter would also wait for a store's acknowledgement)
       // 2. routing: every workgroup's logits of this layer in this group's
       //    copy, then the top-K (the selection is deterministic, so all
       //    workgroups agree)
@@ -582,7 +582,6 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
         constexpr int NV = 4 * RR;
         static_assert(256 * RR <= kMaxE, "tag copy holds 256 RR entries");
         float v[NV];
-        MOE_TRACE(1);
         __builtin_amdgcn_s_sleep(MOE_STACK_SLEEP0);
 #ifdef MOE_STACK_TRACE
         int npoll = 0;
@@ -594,10 +593,13 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
                 t[i] = ld_coh16(tags_mine, (uint32_t)(128 * i + 2 * lane) * 8u);
 #ifdef MOE_STACK_TRACE
               if (npoll++ == 0) MOE_TRACE(25);
-              if (lane == 0) s_tr[l * 32 + 26] = (uint64_t)npoll * 100;
+              if (lane == 0) s_tr[l * kTrEv + 26] = (uint64_t)npoll * 100;
 #endif
             },
             [&](const uint4 (&t)[NV / 2]) {
+#ifdef MOE_STACK_TRACE
+              if (npoll == 1) MOE_TRACE(5);
+#endif
               bool ok = true;
 #pragma unroll
               for (int i = 0; i < NV / 2; ++i) {
@@ -616,88 +618,158 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
             },
             xspins);
         if (!done && lane == 0) atomicOr(&a.ctrl->err, 2u);
-        // key = (order-preserving logit bits, ~index): the largest key is the
-        // largest logit, and among equal logits the lowest index
-        uint64_t key[NV];
+        // selection order: the largest logit first, equal logits by lower
+        // index; NaN logits (and the entries past E, NaN here) rank below
+        // every number, among themselves again by lower index.  Entry j of a
+        // lane is logit 128 (j / 2) + 2 lane + (j & 1).  Each round takes the
+        // wave maximum M of the keys of the entries not taken yet, then the
+        // wave minimum of the position (j / 2, lane, j & 1) -- the index
+        // order -- over the entries holding M, and marks that entry taken.
+        // (Branch-free: this runs on one wave between the logits poll and
+        // the routed loads, where every instruction is on the critical path.)
+        MOE_TRACE(34);
+        // key: the order key plus one (at most 0xFF800001), 0 once taken
+        uint32_t key[NV], pos[NV];  // pos: (j / 2) << 8 | lane << 1 | (j & 1)
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
-          const uint32_t idx = 128u * (j / 2) + 2u * lane + (j & 1);
-          key[j] = ((uint64_t)f32_order_key(v[j]) << 32) | (0xFFFFFFFFu - idx);
+          key[j] = f32_order_key(v[j]) + 1u;
+          pos[j] = ((uint32_t)(j >> 1) << 8) | ((uint32_t)lane << 1) | (j & 1);
         }
         float sel_v[K];
         int sel_i[K];
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-          uint64_t best = 0;
+          uint32_t m = 0;
 #pragma unroll
-          for (int j = 0; j < NV; ++j) best = key[j] > best ? key[j] : best;
-          const uint64_t m = wave_max_u64(best);
-          const uint32_t k32 = (uint32_t)(m >> 32);
-          sel_i[k] = (int)(0xFFFFFFFFu - (uint32_t)m);
-          sel_v[k] = __uint_as_float((k32 & 0x80000000u) ? (k32 & 0x7FFFFFFFu) : ~k32);
-          if (m == 0) sel_i[k] = -1;  // fewer than K finite logits
+          for (int j = 0; j < NV; ++j) m = max(m, key[j]);
+          const uint32_t M = wave_max_u32(m);  // >= 1: fewer than K entries are taken
+          uint32_t c = 0xFFFFFFFFu;
 #pragma unroll
-          for (int j = 0; j < NV; ++j) key[j] = key[j] == m ? 0 : key[j];
+          for (int j = 0; j < NV; ++j) c = min(c, key[j] == M ? pos[j] : 0xFFFFFFFFu);
+          const uint32_t P = wave_min_u32(c);
+#pragma unroll
+          for (int j = 0; j < NV; ++j) key[j] = pos[j] == P ? 0u : key[j];
+          sel_i[k] = (int)((P >> 8) * 128u + (P & 255u));
+          const uint32_t ok = M - 1u;
+          sel_v[k] = __uint_as_float((ok & 0x80000000u) ? (ok & 0x7FFFFFFFu) : ~ok);
         }
-        if (lane == 0) {
-          float den = 0.f, p[K];
+        MOE_TRACE(32);
+        // the weights, lane k computing w_k (den summed in slot order)
+        {
+          float sv = sel_v[0];
+          int si = sel_i[0];
 #pragma unroll
-          for (int k = 0; k < K; ++k) {
-            p[k] = expf(sel_v[k] - sel_v[0]);
-            den += p[k];
+          for (int k = 1; k < K; ++k) {
+            sv = lane == k ? sel_v[k] : sv;
+            si = lane == k ? sel_i[k] : si;
           }
+          const float p = expf(sv - sel_v[0]);
+          float den = 0.f;
 #pragma unroll
-          for (int k = 0; k < K; ++k) {
-            s_ids[k] = sel_i[k];
-            s_w[k] = p[k] / den;
-            if (b == 0 && a.ids_out) a.ids_out[(size_t)l * K + k] = sel_i[k];
-            if (b == 0 && a.w_out) a.w_out[(size_t)l * K + k] = p[k] / den;
+          for (int k = 0; k < K; ++k)
+            den += __uint_as_float((uint32_t)__builtin_amdgcn_readlane(__float_as_uint(p), k));
+          if (lane < K) {
+            s_ids[lane] = si;
+            s_w[lane] = p / den;
           }
         }
+      }
+      // 3. activations h from this group's copy into s_hb: a slot is complete
+      //    once every entry carries this layer's epoch.  A poll waits behind
+      //    every load this CU has issued before it, so the shared slot's poll
+      //    is issued before the routing is handed to the other waves (their
+      //    routed loads then queue behind it), and the routed slots are read
+      //    in rounds: each round polls every slot that this workgroup has
+      //    published its own rows of (the others publish at about the same
+      //    time) and that is not read yet.
+      constexpr int NLD = I / 128;  // 16-byte loads per lane (two entries each)
+      auto h_issue = [&](int slot, uint4 (&t)[NLD]) {
+        const uint32_t base = (uint32_t)(((size_t)grp * NSL + slot) * I * 8);
+#pragma unroll
+        for (int i = 0; i < NLD; ++i)
+          t[i] = ld_coh16(a.htag, base + (uint32_t)(128 * i + 2 * lane) * 8u);
+      };
+      auto h_ok = [&](const uint4 (&t)[NLD]) -> bool {
+        bool ok = true;
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) ok &= t[i].y == epoch && t[i].w == epoch;
+        return __all(ok) != 0;
+      };
+      auto h_take = [&](int slot, const uint4 (&t)[NLD]) {
+        // two 4-byte stores per word (one 8-byte store would need the two
+        // values in adjacent registers, and the compiler would move them
+        // there right after the load, waiting for it)
+        volatile float *hs = &s_hb[slot][0];
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+          const int e = hb_pos(128 * i + 2 * lane);
+          hs[e] = __uint_as_float(t[i].x);
+          hs[e + 1] = __uint_as_float(t[i].z);
+        }
+      };
+      auto release_routing = [&] {
         lds_release();
         if (lane == 0) *lds(&s_ready) = want;
         MOE_TRACE(2);
-      }
-      // 3. activations of slot `slot` from this group's copy into s_hb[slot]
-      //    once every entry carries this layer's epoch; a routed slot is
-      //    polled only once this workgroup has published its own rows of it
-      //    (the others publish at about the same time)
-      for (int j = 0; j < NSL; ++j) {
-        const int slot = j == 0 ? K : j - 1;
-        if (slot == K && !a.has_shared) continue;
-        if (slot != K) wait_lds(&s_cnt[slot], (uint32_t)kGuWaves * want);
-        constexpr int NLD = I / 128;  // 16-byte loads per lane (two entries each)
-        const uint32_t base = (uint32_t)(((size_t)grp * NSL + slot) * I * 8);
-        const bool done = poll_pipe<MOE_STACK_H_POLLS, 6, MOE_STACK_POLL_GAP, NLD>(
-            [&](uint4 (&t)[NLD]) {
-#pragma unroll
-              for (int i = 0; i < NLD; ++i)
-                t[i] = ld_coh16(a.htag, base + (uint32_t)(128 * i + 2 * lane) * 8u);
-            },
+      };
+      if (a.has_shared) {
+#ifdef MOE_STACK_TRACE
+        int nsh = 0;
+#endif
+        const bool done = poll_pipe<1, 8, 0, NLD>(
+            [&](uint4 (&t)[NLD]) { h_issue(K, t); },
             [&](const uint4 (&t)[NLD]) {
-              bool ok = true;
-#pragma unroll
-              for (int i = 0; i < NLD; ++i) ok &= t[i].y == epoch && t[i].w == epoch;
-              return __all(ok) != 0;
+#ifdef MOE_STACK_TRACE
+              if (nsh++ == 0) MOE_TRACE(6);
+#endif
+              return h_ok(t);
             },
-            [&](const uint4 (&t)[NLD]) {
-              // two 4-byte stores per word (one 8-byte store would need the
-              // two values in adjacent registers, and the compiler would move
-              // them there right after the load, waiting for it)
-              volatile float *hs = &s_hb[slot][0];
-#pragma unroll
-              for (int i = 0; i < NLD; ++i) {
-                const int e = hb_pos(128 * i + 2 * lane);
-                hs[e] = __uint_as_float(t[i].x);
-                hs[e + 1] = __uint_as_float(t[i].z);
-              }
-            },
-            xspins);
+            [&](const uint4 (&t)[NLD]) { h_take(K, t); }, xspins, release_routing);
         if (!done && lane == 0) atomicOr(&a.ctrl->err, 2u);
         lds_release();
-        if (lane == 0) *lds(&s_hready[slot]) = want;
-        if (slot == K) MOE_TRACE(3);
-        else if (slot < 4) MOE_TRACE(slot == K - 1 ? 4 : 16 + slot);
+        if (lane == 0) *lds(&s_hready[K]) = want;
+        MOE_TRACE(3);
+      } else {
+        release_routing();
+      }
+      uint32_t need = (1u << K) - 1u;  // routed slots not read yet
+      while (need) {
+        uint32_t pub = 0;
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+          if (((need >> k) & 1u) && *lds(&s_cnt[k]) >= (uint32_t)kGuWaves * want) pub |= 1u << k;
+        pub = __builtin_amdgcn_readfirstlane(pub);
+        if (pub) {
+          // the two lowest such slots (two polls' words fit the registers)
+          const int s0 = __builtin_ctz(pub);
+          const uint32_t rest = pub & (pub - 1u);
+          const int s1 = rest ? __builtin_ctz(rest) : -1;
+          uint4 t0[NLD], t1[NLD];
+          __asm__ volatile("" ::: "memory");
+          h_issue(s0, t0);
+          if (s1 >= 0) h_issue(s1, t1);
+          auto settle = [&](int sl, uint4 (&t)[NLD]) {
+            launder(t);
+            if (h_ok(t)) {
+              h_take(sl, t);
+              lds_release();
+              if (lane == 0) *lds(&s_hready[sl]) = want;
+#ifdef MOE_STACK_TRACE
+              if (lane == 0) s_tr[l * kTrEv + (sl < 3 ? 16 + sl : 4)] = __builtin_amdgcn_s_memrealtime();
+#endif
+              need &= ~(1u << sl);
+            }
+          };
+          settle(s0, t0);
+          if (s1 >= 0) settle(s1, t1);
+        }
+        if (need) {
+          if (++xspins > kSpinMax) {
+            if (lane == 0) atomicOr(&a.ctrl->err, 2u);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
       }
     }
     // every workgroup has passed the first layer's barrier, where it read the
@@ -772,7 +844,27 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
         lds_barrier();  // (A)
         const uint32_t want = (uint32_t)(l + 1);
         const uint32_t epoch = s_epoch + 1u + (uint32_t)l;
+        if (cw == 2) {
+          // this workgroup's logits, one copy per reader group (the sums of
+          // the eight partials in wave order)
+          if (lane < kCopies * rr) {
+            const int rep = lane / rr, row = lane % rr, e = router_row(row);
+            if (e < a.E) {
+              float lg = 0.f;
+#pragma unroll
+              for (int w = 0; w < NW; ++w) lg += s_red[w][row];
+              const uint64_t v = ((uint64_t)epoch << 32) | (uint64_t)__float_as_uint(lg);
+              __hip_atomic_store(&a.tags[(size_t)rep * kMaxE + e], v, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+            }
+          }
+          MOE_TRACE(1);
+        }
         wait_lds(&s_ready, want);
+        if (cw == 2 && b == 0 && lane < K) {
+          if (a.ids_out) a.ids_out[(size_t)l * K + lane] = s_ids[lane];
+          if (a.w_out) a.w_out[(size_t)l * K + lane] = s_w[lane];
+        }
         wait_lds(&s_gu_issued, (uint32_t)kGuWaves * want);
         int eo[K];
         float wk[K];
@@ -828,7 +920,7 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
             if (l + 1 < NL) {
               // r + y of this row for the next layer's norm, one copy per
               // reader group (lanes seg 0..7 of the row's lane group)
-              if (seg < kGroups)
+              if (seg < kCopies)
                 __hip_atomic_store(&a.rtag[(size_t)seg * H + rows[ld]],
                                    ((uint64_t)epoch << 32) | (uint64_t)__float_as_uint(rres[ld]),
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -845,7 +937,7 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
             prev = __hip_atomic_fetch_add(&s_rstored, 1u, __ATOMIC_RELAXED,
                                           __HIP_MEMORY_SCOPE_WORKGROUP);
           prev = __builtin_amdgcn_readfirstlane(prev);
-          if (prev + 1 == 3u * (uint32_t)(l + 1) && lane < kGroups)
+          if (prev + 1 == 3u * (uint32_t)(l + 1) && lane < kCopies)
             __hip_atomic_store(&a.rdone[(size_t)lane * kG + b], (uint64_t)epoch << 32,
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -858,7 +950,7 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
 #ifdef MOE_STACK_TRACE
   __syncthreads();
   if (trace)
-    for (int i = tid; i < NL * 32; i += kNT) trace[(size_t)b * kMaxStackLayers * 32 + i] = s_tr[i];
+    for (int i = tid; i < NL * kTrEv; i += kNT) trace[(size_t)b * kMaxStackLayers * kTrEv + i] = s_tr[i];
 #endif
 }
 
