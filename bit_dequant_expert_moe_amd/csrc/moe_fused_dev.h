@@ -51,6 +51,8 @@ __device__ __forceinline__ int xp_key(int sg) {
 typedef __attribute__((address_space(3))) volatile uint32_t lds_u32;
 
 __device__ __forceinline__ lds_u32 *lds(uint32_t *p) { return (lds_u32 *)(p); }
+typedef __attribute__((address_space(3))) volatile float lds_f32;
+__device__ __forceinline__ lds_f32 *lds(float *p) { return (lds_f32 *)(p); }
 
 // Ordering of LDS accesses between waves of the workgroup only: these wait
 // for outstanding LDS operations, never for global loads.

@@ -118,9 +118,10 @@ constexpr int kTrEv = 48;  // events per (workgroup, layer)
 
 // When the gate/up waves request the next layer's routing-independent bytes:
 // 0 right after the shared expert's gate/up products (during the logits
-// exchange), 1 right after the routed loads, 2 after the routed products.
+// exchange), 1 right after the routed loads, 2 after the routed products,
+// 3 in four parts, one after each routed slot's products.
 #ifndef MOE_STACK_PF
-#define MOE_STACK_PF 2
+#define MOE_STACK_PF 3
 #endif
 
 // When the down-row waves load the next layer's shared-expert rows: 0 at the
@@ -211,6 +212,7 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
   static_assert(NSL == kFusedSlots && I == kFusedI && H == kFusedH, "exchange arrays' sizes");
   static_assert(Gm::RXC == 1, "one 8-column x chunk per thread of the workgroup");
   static_assert(NW == 2 * kGuWaves, "the gate/up waves hold the router chunks of two waves");
+  static_assert(MOE_STACK_PF != 3 || K == 4, "four prefetch parts, one per routed slot");
   __shared__ float s_red[NW][RR];
   __shared__ uint32_t s_xp[2][Gm::SEG_X][PAIRS];  // packed x pairs, by layer parity
   __shared__ float2 s_cx[2][Gm::SEG_X];           // (1024 * sum of pairs, sum of x)
@@ -387,8 +389,12 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     };
     // the bytes of layer l that do not depend on its routing
-    auto prefetch = [&](int l) {
-      const StackLayer Ly = uniform_layer(s_L[l]);
+    // (router rows and x through buffer resources: a load through a generic
+    // pointer is a FLAT load, which also counts on the LDS counter, so the
+    // next LDS read would wait for it)
+    auto load_router = [&](const StackLayer &Ly) {
+      const __amdgpu_buffer_rsrc_t rr_rs =
+          blob_rsrc(reinterpret_cast<const uint8_t *>(Ly.router));
 #pragma unroll
       for (int row = 0; row < RR; ++row) {
         const int e = router_row(row);
@@ -396,25 +402,50 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
         const int ec = e < a.E ? e : a.E - 1;
 #pragma unroll
         for (int c = 0; c < 2; ++c)
-        {
-          typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-          const u32x4 *p = reinterpret_cast<const u32x4 *>(Ly.router + (size_t)ec * H +
-                                                           (size_t)(tid + HALF * c) * 8);
-          const u32x4 v = kPolShared ? __builtin_nontemporal_load(p) : *p;
-          rw[row][c] = make_uint4(v[0], v[1], v[2], v[3]);
-        }
+          rw[row][c] = bld16<kPolShared>(rr_rs, (uint32_t)(((size_t)ec * H +
+                                                            (size_t)(tid + HALF * c) * 8) * 2));
       }
-      if (!RES) {
-        const uint16_t *xl = a.x + (size_t)l * H;
+    };
+    auto load_x = [&](int l) {
+      const __amdgpu_buffer_rsrc_t x_rs = blob_rsrc(reinterpret_cast<const uint8_t *>(a.x));
+      const uint32_t xo = (uint32_t)((size_t)l * H * 2);
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
-          rx2[c] = *reinterpret_cast<const uint4 *>(xl + (size_t)(tid + HALF * c) * 8);
+      for (int c = 0; c < 2; ++c) rx2[c] = bld16(x_rs, xo + (uint32_t)((tid + HALF * c) * 16));
 #pragma unroll
-        for (int t = 0; t < Gm::XLD; ++t)
-          xr[t] = *reinterpret_cast<const uint4 *>(xl + (size_t)(xs % Gm::SEG_X) * COLS + 8 * t);
-      }
+      for (int t = 0; t < Gm::XLD; ++t)
+        xr[t] = bld16(x_rs, xo + (uint32_t)(((xs % Gm::SEG_X) * COLS + 8 * t) * 2));
+    };
+    // the bytes of layer l that do not depend on its routing
+    auto prefetch = [&](int l) {
+      const StackLayer Ly = uniform_layer(s_L[l]);
+      load_router(Ly);
+      if (!RES) load_x(l);
       // without a shared expert slot K reads expert 0 and is never used
       load_rows(std::integral_constant<int, kPolShared>{}, K, a.has_shared ? Ly.shared : Ly.experts);
+    };
+    // the same bytes in four parts (MOE_STACK_PF 3: one part after each routed
+    // slot's products, so that little of it is queued ahead of a poll)
+    auto prefetch_part = [&](int l, int part) {
+      const StackLayer Ly = uniform_layer(s_L[l]);
+      if (part == 0) {
+        load_router(Ly);
+        return;
+      }
+      const __amdgpu_buffer_rsrc_t rs = blob_rsrc(a.has_shared ? Ly.shared : Ly.experts);
+      if (part == 1) {
+        if (!RES) load_x(l);
+#pragma unroll
+        for (int j = 0; j < LSEG; ++j) gq[K][j] = bld16<kPolShared>(rs, o_gq[j]);
+      } else if (part == 2) {
+#pragma unroll
+        for (int j = 0; j < LSEG; ++j) uq[K][j] = bld16<kPolShared>(rs, o_uq[j]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < LSEG; ++j) {
+          gsb[K][j] = bld4<kPolShared>(rs, o_gsb[j]);
+          usb[K][j] = bld4<kPolShared>(rs, o_usb[j]);
+        }
+      }
     };
     prefetch(0);
 
@@ -549,6 +580,9 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
         const bool ok = eid[k] >= 0 && eid[k] < a.E;
         publish(k, ok ? gateup(k) : 0.f);
         if (wave == 0 && k < 4) MOE_TRACE(11 + k);
+        // (issued on the last layer too, again for that layer: a load under
+        // a condition makes the compiler's later waits count conservatively)
+        if (MOE_STACK_PF == 3) prefetch_part(l + 1 < NL ? l + 1 : l, k);
       }
       if (MOE_STACK_PF == 2 && l + 1 < NL) prefetch(l + 1);
     }
@@ -696,10 +730,10 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
         return __all(ok) != 0;
       };
       auto h_take = [&](int slot, const uint4 (&t)[NLD]) {
-        // two 4-byte stores per word (one 8-byte store would need the two
-        // values in adjacent registers, and the compiler would move them
+        // two 4-byte LDS stores per word (one 8-byte store would need the
+        // two values in adjacent registers, and the compiler would move them
         // there right after the load, waiting for it)
-        volatile float *hs = &s_hb[slot][0];
+        lds_f32 *hs = lds(&s_hb[slot][0]);
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
           const int e = hb_pos(128 * i + 2 * lane);
