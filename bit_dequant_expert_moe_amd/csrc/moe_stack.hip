@@ -124,6 +124,13 @@ constexpr int kTrEv = 48;  // events per (workgroup, layer)
 #define MOE_STACK_PF 3
 #endif
 
+// When the down-row waves issue their routed rows' loads: -1 as soon as the
+// gate/up waves have issued theirs, k >= 0 once this workgroup has
+// published its activations of routed slot k.
+#ifndef MOE_STACK_RDELAY
+#define MOE_STACK_RDELAY 0
+#endif
+
 // When the down-row waves load the next layer's shared-expert rows: 0 at the
 // start of that layer (just before its routing), 1 as soon as they have
 // computed the current layer's shared rows (their registers are free then),
@@ -899,22 +906,18 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
           if (a.ids_out) a.ids_out[(size_t)l * K + lane] = s_ids[lane];
           if (a.w_out) a.w_out[(size_t)l * K + lane] = s_w[lane];
         }
-        wait_lds(&s_gu_issued, (uint32_t)kGuWaves * want);
         int eo[K];
         float wk[K];
 #pragma unroll
         for (int k = 0; k < K; ++k) {
           eo[k] = __builtin_amdgcn_readfirstlane(s_ids[k]);
-          const bool ok = eo[k] >= 0 && eo[k] < a.E;
-          wk[k] = ok ? s_w[k] : 0.f;
-          // an invalid id reads expert 0 and contributes 0
-          load_slot(std::integral_constant<int, kPolRouted>{}, k,
-                    Ly.experts + (size_t)(ok ? eo[k] : 0) * Ly.stride);
+          wk[k] = eo[k] >= 0 && eo[k] < a.E ? s_w[k] : 0.f;
         }
-        if (cw == 0) MOE_TRACE(19);
         float v[N];
 #pragma unroll
         for (int ld = 0; ld < N; ++ld) v[ld] = 0.f;
+        // the shared rows first: their activations come before any routed
+        // slot's
         if (a.has_shared) {
           wait_lds(&s_hready[K], want);
           float acc[N];
@@ -931,6 +934,21 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
           const StackLayer Ln = uniform_layer(s_L[l + 1]);
           load_slot(std::integral_constant<int, kPolShared>{}, K, Ln.shared);
         }
+        // the routed rows' loads go after the gate/up waves' (the
+        // activations, which every down row waits for, come from those
+        // bytes), and only once this workgroup has published routed slot
+        // MOE_STACK_RDELAY: until then the gate/up loads have the memory
+        // pipeline to themselves
+        if (MOE_STACK_RDELAY < 0) wait_lds(&s_gu_issued, (uint32_t)kGuWaves * want);
+        else wait_lds(&s_cnt[MOE_STACK_RDELAY < K ? MOE_STACK_RDELAY : K - 1], (uint32_t)kGuWaves * want);
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          // an invalid id reads expert 0 and contributes 0
+          const bool ok = eo[k] >= 0 && eo[k] < a.E;
+          load_slot(std::integral_constant<int, kPolRouted>{}, k,
+                    Ly.experts + (size_t)(ok ? eo[k] : 0) * Ly.stride);
+        }
+        if (cw == 0) MOE_TRACE(19);
 #pragma unroll
         for (int k = 0; k < K; ++k) {
           wait_lds(&s_hready[k], want);
