@@ -162,7 +162,7 @@ def main():
     if chain:
         # the residual stream of each token before layer 0; every layer forms
         # its x from it (written to x[t][l]) and adds its y into it
-        r0_h = synth.residual(wl.seed, ntok, wl.H, wl.rho)
+        r0_h = synth.residual(wl.seed, ntok, wl.H, wl.rho) * np.float32(wl.resid_scale)
         r0 = torch.from_numpy(r0_h).to(dev)                     # [ntok][H] fp32
         r = torch.empty_like(r0)
     y = torch.empty((ntok, nl, wl.H), dtype=torch.float32, device=dev)

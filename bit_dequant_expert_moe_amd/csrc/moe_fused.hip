@@ -531,43 +531,17 @@ __global__ void __launch_bounds__(kNT, 1) k_layer1(FusedArgs a) {
           }
           __builtin_amdgcn_s_sleep(1);
         }
-        // key = (order-preserving logit bits, ~index): the largest key is the
-        // largest logit, and among equal logits the lowest index
-        uint64_t key[NV];
-#pragma unroll
-        for (int j = 0; j < NV; ++j) {
-          const uint32_t idx = 128u * (j / 2) + 2u * lane + (j & 1);
-          key[j] = ((uint64_t)f32_order_key(v[j]) << 32) | (0xFFFFFFFFu - idx);
-        }
         float sel_v[K];
         int sel_i[K];
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-          uint64_t best = 0;
-#pragma unroll
-          for (int j = 0; j < NV; ++j) best = key[j] > best ? key[j] : best;
-          const uint64_t m = wave_max_u64(best);
-          const uint32_t k32 = (uint32_t)(m >> 32);
-          sel_i[k] = (int)(0xFFFFFFFFu - (uint32_t)m);
-          sel_v[k] = __uint_as_float((k32 & 0x80000000u) ? (k32 & 0x7FFFFFFFu) : ~k32);
-          if (m == 0) sel_i[k] = -1;  // fewer than K finite logits
-#pragma unroll
-          for (int j = 0; j < NV; ++j) key[j] = key[j] == m ? 0 : key[j];
-        }
-        if (lane == 0) {
-          float den = 0.f, p[K];
-#pragma unroll
-          for (int k = 0; k < K; ++k) {
-            p[k] = expf(sel_v[k] - sel_v[0]);
-            den += p[k];
-          }
-#pragma unroll
-          for (int k = 0; k < K; ++k) {
-            s_ids[k] = sel_i[k];
-            s_w[k] = p[k] / den;
-            if (b == 0 && a.ids_out) a.ids_out[k] = sel_i[k];
-            if (b == 0 && a.w_out) a.w_out[k] = p[k] / den;
-          }
+        topk_select<K, NV>(v, lane, sel_v, sel_i);
+        int id;
+        float wk;
+        topk_weights<K>(sel_v, sel_i, lane, id, wk);
+        if (lane < K) {
+          s_ids[lane] = id;
+          s_w[lane] = wk;
+          if (b == 0 && a.ids_out) a.ids_out[lane] = id;
+          if (b == 0 && a.w_out) a.w_out[lane] = wk;
         }
       } else if (lane < K) {
         const int e = a.ids_in[lane];

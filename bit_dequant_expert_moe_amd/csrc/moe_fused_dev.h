@@ -171,6 +171,63 @@ __device__ __forceinline__ bool poll_pipe(Issue &&issue, Ok &&ok, Take &&take, l
   return poll_pipe<NP, M, GAP, NW>(issue, ok, take, spins, [] {});
 }
 
+// Top-K over the wave's logits.  Entry j of lane `lane` holds logit
+// 128 (j / 2) + 2 lane + (j & 1), value v[j] (NaN, also for padding, ranks
+// below every number).  Order: the largest value first, equal values by
+// lower index (NaNs among themselves too).  Each round takes the wave maximum
+// M of (order key + 1) over the entries not taken yet (a taken entry's key
+// is 0), then the wave minimum of the position (j / 2, lane, j & 1) -- the
+// index order -- over the entries holding M, and marks that one taken.
+// Branch-free: it runs on one wave between the logits poll and the routed
+// loads, where every instruction is on the critical path.
+template <int K, int NV>
+__device__ __forceinline__ void topk_select(const float (&v)[NV], int lane, float (&sel_v)[K],
+                                            int (&sel_i)[K]) {
+  uint32_t key[NV], pos[NV];  // pos: (j / 2) << 8 | lane << 1 | (j & 1)
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    key[j] = f32_order_key(v[j]) + 1u;  // at most 0xFF800001
+    pos[j] = ((uint32_t)(j >> 1) << 8) | ((uint32_t)lane << 1) | (j & 1);
+  }
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) m = max(m, key[j]);
+    const uint32_t M = wave_max_u32(m);  // >= 1: fewer than K entries are taken
+    uint32_t c = 0xFFFFFFFFu;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) c = min(c, key[j] == M ? pos[j] : 0xFFFFFFFFu);
+    const uint32_t P = wave_min_u32(c);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) key[j] = pos[j] == P ? 0u : key[j];
+    sel_i[k] = (int)((P >> 8) * 128u + (P & 255u));
+    const uint32_t ok = M - 1u;
+    sel_v[k] = __uint_as_float((ok & 0x80000000u) ? (ok & 0x7FFFFFFFu) : ~ok);
+  }
+}
+
+// Routing weights of the selection, lane k (< K) computing slot k's:
+// w_k = p_k / (p_0 + .. + p_{K-1}), p_k = exp(v_k - v_0), the sum in slot
+// order.  id and w are those of slot `lane` on lanes < K.
+template <int K>
+__device__ __forceinline__ void topk_weights(const float (&sel_v)[K], const int (&sel_i)[K],
+                                             int lane, int &id, float &w) {
+  float sv = sel_v[0];
+  id = sel_i[0];
+#pragma unroll
+  for (int k = 1; k < K; ++k) {
+    sv = lane == k ? sel_v[k] : sv;
+    id = lane == k ? sel_i[k] : id;
+  }
+  const float p = expf(sv - sel_v[0]);
+  float den = 0.f;
+#pragma unroll
+  for (int k = 0; k < K; ++k)
+    den += __uint_as_float((uint32_t)__builtin_amdgcn_readlane(__float_as_uint(p), k));
+  w = p / den;
+}
+
 // 8-byte coherent load, the same policy.
 __device__ __forceinline__ uint2 ld_coh8(const void *base, uint32_t byte_off) {
   const __amdgpu_buffer_rsrc_t r =

@@ -659,60 +659,17 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
             },
             xspins);
         if (!done && lane == 0) atomicOr(&a.ctrl->err, 2u);
-        // selection order: the largest logit first, equal logits by lower
-        // index; NaN logits (and the entries past E, NaN here) rank below
-        // every number, among themselves again by lower index.  Entry j of a
-        // lane is logit 128 (j / 2) + 2 lane + (j & 1).  Each round takes the
-        // wave maximum M of the keys of the entries not taken yet, then the
-        // wave minimum of the position (j / 2, lane, j & 1) -- the index
-        // order -- over the entries holding M, and marks that entry taken.
-        // (Branch-free: this runs on one wave between the logits poll and
-        // the routed loads, where every instruction is on the critical path.)
         MOE_TRACE(34);
-        // key: the order key plus one (at most 0xFF800001), 0 once taken
-        uint32_t key[NV], pos[NV];  // pos: (j / 2) << 8 | lane << 1 | (j & 1)
-#pragma unroll
-        for (int j = 0; j < NV; ++j) {
-          key[j] = f32_order_key(v[j]) + 1u;
-          pos[j] = ((uint32_t)(j >> 1) << 8) | ((uint32_t)lane << 1) | (j & 1);
-        }
         float sel_v[K];
         int sel_i[K];
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-          uint32_t m = 0;
-#pragma unroll
-          for (int j = 0; j < NV; ++j) m = max(m, key[j]);
-          const uint32_t M = wave_max_u32(m);  // >= 1: fewer than K entries are taken
-          uint32_t c = 0xFFFFFFFFu;
-#pragma unroll
-          for (int j = 0; j < NV; ++j) c = min(c, key[j] == M ? pos[j] : 0xFFFFFFFFu);
-          const uint32_t P = wave_min_u32(c);
-#pragma unroll
-          for (int j = 0; j < NV; ++j) key[j] = pos[j] == P ? 0u : key[j];
-          sel_i[k] = (int)((P >> 8) * 128u + (P & 255u));
-          const uint32_t ok = M - 1u;
-          sel_v[k] = __uint_as_float((ok & 0x80000000u) ? (ok & 0x7FFFFFFFu) : ~ok);
-        }
+        topk_select<K, NV>(v, lane, sel_v, sel_i);
         MOE_TRACE(32);
-        // the weights, lane k computing w_k (den summed in slot order)
-        {
-          float sv = sel_v[0];
-          int si = sel_i[0];
-#pragma unroll
-          for (int k = 1; k < K; ++k) {
-            sv = lane == k ? sel_v[k] : sv;
-            si = lane == k ? sel_i[k] : si;
-          }
-          const float p = expf(sv - sel_v[0]);
-          float den = 0.f;
-#pragma unroll
-          for (int k = 0; k < K; ++k)
-            den += __uint_as_float((uint32_t)__builtin_amdgcn_readlane(__float_as_uint(p), k));
-          if (lane < K) {
-            s_ids[lane] = si;
-            s_w[lane] = p / den;
-          }
+        int id;
+        float wk;
+        topk_weights<K>(sel_v, sel_i, lane, id, wk);
+        if (lane < K) {
+          s_ids[lane] = id;
+          s_w[lane] = wk;
         }
       }
       // 3. activations h from this group's copy into s_hb: a slot is complete
