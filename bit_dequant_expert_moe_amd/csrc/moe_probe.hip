@@ -19,14 +19,22 @@ constexpr size_t kStreamBlocks = 2048;
 // Reads `n16` 16-byte words; workgroup b reads the b-th of gridDim.x
 // contiguous ranges, kLoadsInFlight coalesced 4 KB blocks per round, and
 // writes the XOR of what it read to sink[b] (so that no load can be dropped).
-// The loads carry the non-temporal hint, as the decode kernels' loads of
-// bytes read once do (with it a long stream runs at ~7 TB/s on this GPU,
-// without it at ~5 TB/s).
+// NT: the loads carry the non-temporal hint.  Measured on this GPU: a
+// 2.4 GB stream runs at 6.9 TB/s with it and 5.2 TB/s without, a 40 MB one at
+// 2.5 TB/s with it and 4.1 TB/s without; the launcher takes the faster form
+// for the size.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint32_t nt_xor(const uint4 *p) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-  return v[0] ^ v[1] ^ v[2] ^ v[3];
+template <bool NT>
+__device__ __forceinline__ uint32_t ld_xor(const uint4 *p) {
+  if (NT) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  const uint4 v = *p;
+  return v.x ^ v.y ^ v.z ^ v.w;
 }
+constexpr size_t kNtMinBytes = (size_t)256 << 20;  // non-temporal from this size on
+template <bool NT>
 __global__ void __launch_bounds__(kProbeThreads) k_stream_read(const uint4 *__restrict__ src,
                                                                size_t n16, uint32_t *sink) {
   __shared__ uint32_t s_x[kProbeThreads / 64];
@@ -38,11 +46,11 @@ __global__ void __launch_bounds__(kProbeThreads) k_stream_read(const uint4 *__re
   for (; i + (kLoadsInFlight - 1) * kProbeThreads < b1; i += kLoadsInFlight * kProbeThreads) {
     uint32_t v[kLoadsInFlight];
 #pragma unroll
-    for (int k = 0; k < kLoadsInFlight; ++k) v[k] = nt_xor(src + i + k * kProbeThreads);
+    for (int k = 0; k < kLoadsInFlight; ++k) v[k] = ld_xor<NT>(src + i + k * kProbeThreads);
 #pragma unroll
     for (int k = 0; k < kLoadsInFlight; ++k) acc ^= v[k];
   }
-  for (; i < b1; i += kProbeThreads) acc ^= nt_xor(src + i);
+  for (; i < b1; i += kProbeThreads) acc ^= ld_xor<NT>(src + i);
   for (int off = 32; off > 0; off >>= 1) acc ^= __shfl_xor(acc, off, 64);
   if ((threadIdx.x & 63) == 0) s_x[threadIdx.x >> 6] = acc;
   __syncthreads();
@@ -73,8 +81,12 @@ int stream_read_blocks(size_t bytes) {
 }
 
 int launch_stream_read(const void *src, size_t bytes, uint32_t *sink, void *stream) {
-  hipLaunchKernelGGL(k_stream_read, dim3(stream_read_blocks(bytes)), dim3(kProbeThreads), 0,
-                     S(stream), static_cast<const uint4 *>(src), bytes / 16, sink);
+  if (bytes >= kNtMinBytes)
+    hipLaunchKernelGGL(k_stream_read<true>, dim3(stream_read_blocks(bytes)), dim3(kProbeThreads),
+                       0, S(stream), static_cast<const uint4 *>(src), bytes / 16, sink);
+  else
+    hipLaunchKernelGGL(k_stream_read<false>, dim3(stream_read_blocks(bytes)), dim3(kProbeThreads),
+                       0, S(stream), static_cast<const uint4 *>(src), bytes / 16, sink);
   return (int)hipGetLastError();
 }
 

@@ -403,7 +403,9 @@ size_t moe_stream_read_sink_words(size_t bytes);
  * 16-byte loads spread over up to 2048 workgroups and writes an XOR of what
  * each workgroup read to sink[0 .. moe_stream_read_sink_words(bytes) - 1]:
  * the streaming read rate a single launch reaches at that size, the
- * achievable counterpart of the HBM peak for the layer's byte counts.
+ * achievable counterpart of the HBM peak for the layer's byte counts.  From
+ * 256 MiB on the loads carry the non-temporal hint (faster there on this GPU),
+ * below it they are plain loads (faster there).
  * src 16-byte aligned, bytes a nonzero multiple of 16, sink device uint32. */
 moe_status moe_stream_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
 
