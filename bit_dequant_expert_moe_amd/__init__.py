@@ -12,7 +12,8 @@ import os
 from dataclasses import dataclass
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe.so")
+# MOE_LIB: another build of the library to load (the sanitizer test's)
+LIB_PATH = os.environ.get("MOE_LIB") or os.path.join(_HERE, "libmoe.so")
 
 MOE_OK = 0
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_UNSUPPORTED",

@@ -23,18 +23,20 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
-def build(force: bool = True, extra=None) -> str:
+def build(force: bool = True, extra=None, out=None) -> str:
+    """Builds libmoe.so, or `out` with the extra hipcc flags `extra`."""
+    dst = out or LIB
     srcs = SOURCES + HEADERS
-    if not force and os.path.exists(LIB) and all(
-            os.path.getmtime(s) <= os.path.getmtime(LIB) for s in srcs):
-        return LIB
-    tmp = LIB + ".tmp%d" % os.getpid()
+    if not force and os.path.exists(dst) and all(
+            os.path.getmtime(s) <= os.path.getmtime(dst) for s in srcs):
+        return dst
+    tmp = dst + ".tmp%d" % os.getpid()
     cmd = [HIPCC, *FLAGS, *(extra or []), "-o", tmp, *SOURCES]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, dst)
+    return dst
 
 
 if __name__ == "__main__":

@@ -203,7 +203,7 @@ extern "C" {
 
 int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
 
-const char *moe_status_str(moe_status s) {
+const char *moe_status_str(int32_t s) {
   switch (s) {
     case MOE_OK: return "ok";
     case MOE_ERR_NULL: return "null pointer";

@@ -147,8 +147,9 @@ enum {
 /* Library ABI version (MOE_ABI_VERSION). */
 int32_t moe_abi_version(void);
 
-/* Human-readable name of a status code (static string, never NULL). */
-const char *moe_status_str(moe_status s);
+/* Human-readable name of a status code (static string, never NULL).  Takes
+ * any int, so a value outside moe_status yields "unknown status". */
+const char *moe_status_str(int32_t s);
 
 /* Checks dims against the constraints above.  Host only. */
 moe_status moe_check_dims(const moe_dims *dims);

@@ -51,15 +51,18 @@ class Dims:
         return _Dims(self.H, self.I, self.E, self.K, self.bits, self.group, self.has_shared)
 
 
-def build(force: bool = True) -> str:
-    """Compiles oracle.c with gcc (no fast-math, no FMA contraction)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp%d" % os.getpid()
+def build(force: bool = True, out: str = None, extra=None) -> str:
+    """Compiles oracle.c with gcc (no fast-math, no FMA contraction) into
+    liboracle.so, or into `out` with the extra flags `extra` (e.g. a
+    sanitizer build)."""
+    dst = out or _LIB
+    if force or not os.path.exists(dst) or os.path.getmtime(dst) < os.path.getmtime(_SRC):
+        tmp = dst + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", "-O2", "-std=c99", "-Wall", "-ffp-contract=off",
-                               "-fno-fast-math", "-fopenmp", "-fPIC", "-shared", "-o", tmp,
-                               _SRC, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+                               "-fno-fast-math", "-fopenmp", "-fPIC", "-shared", *(extra or []),
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, dst)
+    return dst
 
 
 _lib = None
@@ -68,8 +71,10 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        build(force=False)
-        L = ctypes.CDLL(_LIB)
+        # MOE_ORACLE_LIB: a prebuilt oracle library to load instead (the
+        # sanitizer test builds one)
+        path = os.environ.get("MOE_ORACLE_LIB") or build(force=False)
+        L = ctypes.CDLL(path)
         dp = ctypes.POINTER(_Dims)
         L.or_set_threads.restype = None
         L.or_set_threads.argtypes = [ctypes.c_int]
