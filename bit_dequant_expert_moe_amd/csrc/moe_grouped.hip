@@ -204,6 +204,7 @@ struct GroupArgs {
   int E, maxB, K1;     // K1 = K + 1 (pair code = token K1 + slot)
   int pair_cap;        // T (K + 1): size of the pair-code list
   int64_t off_q0, off_q1, off_sb0, off_sb1;  // second matrix unused for down
+  uint32_t bop_bytes, bsum_bytes;  // sizes of the bop and bsum areas (< kNoLoad)
 };
 
 template <int BITS, bool DOWN>
@@ -277,6 +278,35 @@ __device__ __forceinline__ bf16x8 a_slice(uint32_t word, int half, const Unpack 
   return __builtin_bit_cast(bf16x8, u);
 }
 
+// Loads through buffer resources: 32-bit unsigned byte offsets from a base
+// held in scalar registers, range-checked against the resource's size.  An
+// offset at or past the size returns zeros without a memory access, which is
+// how a padding column or an idle thread issues its load: every load of the
+// pipeline is issued on every path.
+constexpr uint32_t kNoLoad = 0xFFFFFF00u;  // past every area (sizes are checked on the host)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t area_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ float bload4f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+
+// An empty volatile asm that reads and writes a loaded value: the wait for
+// its load lands here, on every path, and not inside a conditional store that
+// uses it (a wait inside a branch leaves the register pending on the other
+// path, and the next load into it then waits for every load in flight).
+__device__ __forceinline__ void settle(uint4 &u) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 v = {u.x, u.y, u.z, u.w};
+  __asm__ volatile("" : "+v"(v));
+  u = make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void settle(float &f) { __asm__ volatile("" : "+v"(f)); }
+
 // (x0..x7 as pairs (x0,x1),(x2,x3),(x4,x5),(x6,x7)) -> (x0,x4),(x1,x5),(x2,x6),(x3,x7)
 __device__ __forceinline__ uint4 b_order(uint4 q) {
   uint4 r;
@@ -312,8 +342,15 @@ __global__ void __launch_bounds__(256) k_xprep(XPrepArgs a) {
   if (in && (i & 7) == 0) a.xs[i >> 3] = part;
 }
 
+// Minimum waves per SIMD the register allocation must allow: three, so that
+// three blocks of either pass fit a compute unit where LDS allows (the down
+// pass's does; with its 53 KB a 170-register allocation would cost one block).
+#ifndef MOE_GROUPED_MINW
+#define MOE_GROUPED_MINW 3
+#endif
+
 template <int BITS, bool DOWN>
-__global__ void __launch_bounds__(256) k_grouped(GroupArgs a) {
+__global__ void __launch_bounds__(256, MOE_GROUPED_MINW) k_grouped(GroupArgs a) {
   using G = GL<BITS, DOWN>;
   extern __shared__ __align__(16) uint32_t lds[];
   __shared__ float s_hsum[4][16];
@@ -349,50 +386,62 @@ __global__ void __launch_bounds__(256) k_grouped(GroupArgs a) {
     uint4 rb[G::BPT];
     float rxs;
   };
-  // B rows of this thread's pieces, resolved once: a load whose address
-  // depends on another load inside the pipeline would wait for every load
-  // issued before it (loads complete in order)
-  int brow_b[G::BPT], brow_s = -1;
+  // Byte offsets of this thread's loads at chunk 0, resolved once (a load
+  // whose address depends on another load inside the pipeline would wait
+  // for every load issued before it; loads complete in order).  Every load
+  // of the pipeline is issued unconditionally, so that the wait before a
+  // chunk is staged counts only the loads issued before it: a padding
+  // column, or a thread with no scale word or group sum, loads at kNoLoad
+  // and stages zeros.
+  const __amdgpu_buffer_rsrc_t rs_blob = area_rsrc(blob, 0x7FFFFFFFu);
+  const __amdgpu_buffer_rsrc_t rs_b = area_rsrc(a.bop, a.bop_bytes);
+  const __amdgpu_buffer_rsrc_t rs_s = area_rsrc(a.bsum, a.bsum_bytes);
+  uint32_t aoff[G::APT];
+#pragma unroll
+  for (int i = 0; i < G::APT; ++i) {
+    const int pc = tid + 256 * i;
+    const int mat = pc / (kRT * G::PPR), rr = (pc / G::PPR) % kRT, c16 = pc % G::PPR;
+    aoff[i] = (uint32_t)((mat ? a.off_q1 : a.off_q0) + (int64_t)(row0 + rr) * (int64_t)rbytes) +
+              c16 * 16;
+  }
+  uint32_t boff[G::BPT];
 #pragma unroll
   for (int i = 0; i < G::BPT; ++i) {
-    const int bc = (tid + 256 * i) / (kSl * G::BV);
-    brow_b[i] = -1;
+    const int bc = (tid + 256 * i) / (kSl * G::BV), rest = (tid + 256 * i) % (kSl * G::BV);
+    boff[i] = kNoLoad;
     if (bc < nn) {
       const int pcode = pairs[bc];
-      brow_b[i] = DOWN ? pcode : pcode / a.K1;
+      const uint32_t brow = DOWN ? pcode : pcode / a.K1;
+      boff[i] = (brow * (uint32_t)nslices * G::BV + rest) * 16u;
     }
   }
+  uint32_t soff = kNoLoad;
   if (tid < kNC * kGC && tid / kGC < nn) {
     const int pcode = pairs[tid / kGC];
-    brow_s = DOWN ? pcode : pcode / a.K1;
+    const uint32_t brow = DOWN ? pcode : pcode / a.K1;
+    soff = (brow * (uint32_t)groups + tid % kGC) * 4u;
   }
+  const bool sbok = tid < G::NMAT * kRT;
+  uint32_t sboff = kNoLoad;
+  if (sbok) {
+    const int mat = tid / kRT, rr = tid % kRT;
+    sboff = (uint32_t)((mat ? a.off_sb1 : a.off_sb0) + (int64_t)(row0 + rr) * groups * 4);
+  }
+  // chunk c's offsets: the chunk-0 offset plus the chunk's, or kNoLoad
+  auto at = [](uint32_t off0, uint32_t step) { return off0 == kNoLoad ? kNoLoad : off0 + step; };
   auto load_chunk = [&](int c, Regs &R) {
 #pragma unroll
-    for (int i = 0; i < G::APT; ++i) {
-      const int pc = tid + 256 * i;
-      const int mat = pc / (kRT * G::PPR), rr = (pc / G::PPR) % kRT, c16 = pc % G::PPR;
-      const int64_t off = mat ? a.off_q1 : a.off_q0;
-      R.ra[i] = *reinterpret_cast<const uint4 *>(blob + off + (size_t)(row0 + rr) * rbytes +
-                                                (size_t)c * (kKC * BITS / 8) + c16 * 16);
-    }
-    R.rsb = make_uint4(0, 0, 0, 0);
-    if (tid < G::NMAT * kRT) {
-      const int mat = tid / kRT, rr = tid % kRT;
-      const int64_t off = mat ? a.off_sb1 : a.off_sb0;
-      R.rsb = *reinterpret_cast<const uint4 *>(blob + off +
-                                              ((size_t)(row0 + rr) * groups + (size_t)c * kGC) * 4);
-    }
+    for (int i = 0; i < G::APT; ++i) R.ra[i] = bload16(rs_blob, aoff[i] + c * (kKC * BITS / 8));
+    R.rsb = bload16(rs_blob, at(sboff, c * kGC * 4));
 #pragma unroll
-    for (int i = 0; i < G::BPT; ++i) {
-      const int rest = (tid + 256 * i) % (kSl * G::BV);
-      R.rb[i] = make_uint4(0, 0, 0, 0);
-      if (brow_b[i] >= 0)
-        R.rb[i] = a.bop[((size_t)brow_b[i] * nslices + (size_t)c * kSl) * G::BV + rest];
-    }
-    R.rxs = 0.f;
-    if (brow_s >= 0) R.rxs = a.bsum[(size_t)brow_s * groups + c * kGC + tid % kGC];
+    for (int i = 0; i < G::BPT; ++i) R.rb[i] = bload16(rs_b, at(boff[i], c * kSl * G::BV * 16));
+    R.rxs = bload4f(rs_s, at(soff, c * kGC * 4));
   };
-  auto store_chunk = [&](int buf, const Regs &R) {
+  auto store_chunk = [&](int buf, Regs &R) {
+    settle(R.rsb);
+#pragma unroll
+    for (int i = 0; i < G::BPT; ++i) settle(R.rb[i]);
+    settle(R.rxs);
     uint32_t *A = lds + (size_t)buf * G::BUF_U32;
     uint32_t *SB = A + G::A_U32;
     uint4 *Bq = reinterpret_cast<uint4 *>(SB + G::SB_U32);
@@ -409,7 +458,7 @@ __global__ void __launch_bounds__(256) k_grouped(GroupArgs a) {
     }
     if (DOWN) {
       if (tid < kRT) *reinterpret_cast<uint4 *>(SB + tid * kGC) = R.rsb;
-    } else if (tid < G::NMAT * kRT) {
+    } else if (sbok) {
       // per group (s, z - 128 s): the MFMA sums (128 + q) b, so
       // s sum q b + z sum b = s P + (z - 128 s) X
       const uint32_t w4[4] = {R.rsb.x, R.rsb.y, R.rsb.z, R.rsb.w};
@@ -501,22 +550,38 @@ __global__ void __launch_bounds__(256) k_grouped(GroupArgs a) {
 
   // ---- software pipeline over the column chunks ----------------------------
   // chunk c is computed from LDS buffer c & 1 while chunks c + 1 and c + 2
-  // are in flight in the register sets (nchunks is even)
+  // are in flight in the register sets.  The steady-state loop issues its
+  // loads unconditionally, and so does the prologue (a row of one chunk loads
+  // chunk 0 twice): with a load skipped on some path, the wait before a chunk
+  // is staged would have to count as if no later load were in flight, which
+  // drains the pipeline to one chunk.
   Regs R0, R1;
   load_chunk(0, R0);
-  if (nchunks > 1) load_chunk(1, R1);
+  load_chunk(nchunks > 1 ? 1 : 0, R1);
   store_chunk(0, R0);
   __syncthreads();
-  for (int c = 0; c < nchunks; c += 2) {
-    if (c + 2 < nchunks) load_chunk(c + 2, R0);
+  int c = 0;
+  for (; c + 3 < nchunks; c += 2) {
+    load_chunk(c + 2, R0);
     compute_chunk(0);
-    if (c + 1 < nchunks) store_chunk(1, R1);
+    store_chunk(1, R1);
     __syncthreads();
-    if (c + 1 < nchunks) {
-      if (c + 3 < nchunks) load_chunk(c + 3, R1);
-      compute_chunk(1);
-      if (c + 2 < nchunks) store_chunk(0, R0);
+    load_chunk(c + 3, R1);
+    compute_chunk(1);
+    store_chunk(0, R0);
+    __syncthreads();
+  }
+  // the last one to three chunks: c is in buffer 0, c + 1 in R1
+  if (c + 2 < nchunks) load_chunk(c + 2, R0);
+  compute_chunk(0);
+  if (c + 1 < nchunks) {
+    store_chunk(1, R1);
+    __syncthreads();
+    compute_chunk(1);
+    if (c + 2 < nchunks) {
+      store_chunk(0, R0);
       __syncthreads();
+      compute_chunk(0);
     }
   }
 
@@ -727,9 +792,18 @@ int launch_expert_forward_grouped(const moe_dims &d, const moe_layer &L, const u
   gu.off_q1 = (int64_t)B.off[MOE_SEC_UP_Q];
   gu.off_sb0 = (int64_t)B.off[MOE_SEC_GATE_SB];
   gu.off_sb1 = (int64_t)B.off[MOE_SEC_UP_SB];
+  const size_t P = (size_t)T * (d.top_k + 1);
+  const size_t area[4] = {(size_t)T * d.hidden * 2, (size_t)T * (d.hidden / kGroup) * 4,
+                          P * d.inter * 4, P * (d.inter / kGroup) * 4};
+  for (size_t v : area)
+    if (v >= kNoLoad) return (int)hipErrorInvalidValue;  // beyond 32-bit buffer offsets
+  gu.bop_bytes = (uint32_t)area[0];
+  gu.bsum_bytes = (uint32_t)area[1];
   GroupArgs dn = gu;
   dn.bop = hb;
   dn.bsum = hs;
+  dn.bop_bytes = (uint32_t)area[2];
+  dn.bsum_bytes = (uint32_t)area[3];
   dn.hb = nullptr;
   dn.hs = nullptr;
   dn.yd = yd;
