@@ -110,13 +110,22 @@ inline RowGeo row_geo(int cols, int bits) {
   return g;
 }
 
-// Column splits of the router for T tokens: blocks of 16 experts x 16 tokens
-// are split along the hidden dimension until about 256 blocks stream the
-// router (each wave keeps whole 32-column steps).
+// From this many tokens the router runs in 64-token x 64-expert tiles with
+// both operands staged in LDS (k_router_tiled); below, in 16 x 16 tiles that
+// read their operands straight from memory (k_router).
+constexpr int kRouteTiledT = 512;
+inline bool route_tiled(int T) { return T >= kRouteTiledT; }
+
+// Column splits of the router for T tokens: the blocks (16 x 16 or 64 x 64
+// tiles) are split along the hidden dimension until about 256 blocks stream
+// the router (16 x 16: each wave keeps whole 32-column steps; 64 x 64: each
+// split whole 64-column steps).
 inline int route_splits(const moe_dims &d, int T) {
-  const int blocks = ((d.n_experts + 15) / 16) * ((T + 15) / 16);
+  const int tile = route_tiled(T) ? 64 : 16;
+  const int per_split = route_tiled(T) ? 64 : 128;
+  const int blocks = ((d.n_experts + tile - 1) / tile) * ((T + tile - 1) / tile);
   int s = 1;
-  while (s < kMaxRouteSplits && blocks * s < 256 && d.hidden % (128 * 2 * s) == 0) s *= 2;
+  while (s < kMaxRouteSplits && blocks * s < 256 && d.hidden % (per_split * 2 * s) == 0) s *= 2;
   return s;
 }
 

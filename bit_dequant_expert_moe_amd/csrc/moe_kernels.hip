@@ -10,7 +10,8 @@
 //
 // Kernels
 //   k_router       router logits for T tokens on the matrix cores (bf16 x
-//                  bf16 -> fp32, v_mfma_f32_16x16x32_bf16).
+//                  bf16 -> fp32, v_mfma_f32_16x16x32_bf16), 16 x 16 tiles.
+//   k_router_tiled the same for a large T, 64 x 64 tiles staged in LDS.
 //   k_topk         one wave per token: top-K and the renormalised weights.
 //   k_gateup       gate and up rows of the selected experts and the shared
 //                  expert, SwiGLU epilogue; activations h to the workspace.
@@ -160,6 +161,102 @@ __global__ void __launch_bounds__(256) k_router(RouteArgs a) {
       }
     }
   }
+}
+
+// Many tokens: a block computes a 64-token x 64-expert tile of the logits
+// over one of S column ranges.  The x and router rows of each 64-column step
+// are staged in LDS once per block (the 16 x 16 tiles above read each row
+// once per tile, which makes a large batch bound by cache traffic); wave w
+// computes the 32 x 32 quarter of tokens 32 (w & 1) .. and experts
+// 32 (w >> 1) .. of the tile.
+// v, or zeros where !ok (per component: a select of the whole struct goes
+// through memory)
+__device__ __forceinline__ uint4 keep_if(bool ok, uint4 v) {
+  return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
+}
+
+constexpr int kRtTile = 64;  // tokens and experts per block
+constexpr int kRtStep = 64;  // columns per staged step
+
+__global__ void __launch_bounds__(256) k_router_tiled(RouteArgs a) {
+  constexpr int SEG = kRtStep / 8;  // 16-byte segments per staged row
+  constexpr int LD = SEG + 1;       // row pitch in uint4 (+1 against bank conflicts)
+  __shared__ uint4 s_x[2][kRtTile * LD];
+  __shared__ uint4 s_r[2][kRtTile * LD];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int q = lane >> 4, c16 = lane & 15;
+  const int t0 = kRtTile * blockIdx.y, e0 = kRtTile * blockIdx.x;
+  const int kw = a.H / a.S;
+  const size_t kb = (size_t)blockIdx.z * kw;
+  const int nst = kw / kRtStep;
+  // this thread's two pieces of each operand per step: row p / SEG, segment
+  // p % SEG (p = tid, tid + 256); rows past T or E read the tile's first row
+  // and stage zeros (the loads are issued on every path)
+  const int pr0 = tid / SEG, pr1 = pr0 + 256 / SEG, ps = tid % SEG;
+  const bool xok0 = t0 + pr0 < a.T, xok1 = t0 + pr1 < a.T;
+  const bool rok0 = e0 + pr0 < a.E, rok1 = e0 + pr1 < a.E;
+  const uint4 *xp0 = reinterpret_cast<const uint4 *>(a.x + (size_t)(xok0 ? t0 + pr0 : t0) * a.H + kb) + ps;
+  const uint4 *xp1 = reinterpret_cast<const uint4 *>(a.x + (size_t)(xok1 ? t0 + pr1 : t0) * a.H + kb) + ps;
+  const uint4 *rp0 = reinterpret_cast<const uint4 *>(a.router + (size_t)(rok0 ? e0 + pr0 : e0) * a.H + kb) + ps;
+  const uint4 *rp1 = reinterpret_cast<const uint4 *>(a.router + (size_t)(rok1 ? e0 + pr1 : e0) * a.H + kb) + ps;
+  const int so0 = pr0 * LD + ps, so1 = pr1 * LD + ps;
+  const int wt = wave & 1, we = wave >> 1;
+  f32x4_t acc[2][2];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  uint4 x0 = xp0[0], x1 = xp1[0], r0 = rp0[0], r1 = rp1[0];
+  s_x[0][so0] = keep_if(xok0, x0);
+  s_x[0][so1] = keep_if(xok1, x1);
+  s_r[0][so0] = keep_if(rok0, r0);
+  s_r[0][so1] = keep_if(rok1, r1);
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < nst) {
+      x0 = xp0[(st + 1) * SEG];
+      x1 = xp1[(st + 1) * SEG];
+      r0 = rp0[(st + 1) * SEG];
+      r1 = rp1[(st + 1) * SEG];
+    }
+    // A operand: token rows (lane: row c16, columns 8 q .. of a 32-column
+    // half step); B operand: expert rows, the same columns
+#pragma unroll
+    for (int kk = 0; kk < kRtStep / 32; ++kk) {
+      bf16x8_t av[2], bv[2];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+        av[mi] = __builtin_bit_cast(bf16x8_t, s_x[buf][(32 * wt + 16 * mi + c16) * LD + 4 * kk + q]);
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+        bv[ni] = __builtin_bit_cast(bf16x8_t, s_r[buf][(32 * we + 16 * ni + c16) * LD + 4 * kk + q]);
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mi], bv[ni], acc[mi][ni], 0, 0, 0);
+    }
+    if (st + 1 < nst) {
+      s_x[buf ^ 1][so0] = keep_if(xok0, x0);
+      s_x[buf ^ 1][so1] = keep_if(xok1, x1);
+      s_r[buf ^ 1][so0] = keep_if(rok0, r0);
+      s_r[buf ^ 1][so1] = keep_if(rok1, r1);
+    }
+    __syncthreads();
+  }
+  // element v of acc[mi][ni]: token 32 wt + 16 mi + 4 q + v, expert
+  // 32 we + 16 ni + c16 of the tile
+  float *lp = a.logits + (size_t)blockIdx.z * a.T * a.E;
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int t = t0 + 32 * wt + 16 * mi + 4 * q + v, e = e0 + 32 * we + 16 * ni + c16;
+        if (t < a.T && e < a.E) lp[(size_t)t * a.E + e] = acc[mi][ni][v];
+      }
 }
 
 // One block per token: the 4 waves add the S partial logits in order (all
@@ -548,8 +645,13 @@ int launch_route(const moe_dims &d, const uint16_t *router, const uint16_t *x, i
   a.K = d.top_k;
   a.T = T;
   a.S = route_splits(d, T);
-  hipLaunchKernelGGL(k_router, dim3((d.n_experts + 15) / 16, (T + 15) / 16, a.S), dim3(256), 0,
-                     S(stream), a);
+  if (route_tiled(T))
+    hipLaunchKernelGGL(k_router_tiled,
+                       dim3((d.n_experts + kRtTile - 1) / kRtTile, (T + kRtTile - 1) / kRtTile, a.S),
+                       dim3(256), 0, S(stream), a);
+  else
+    hipLaunchKernelGGL(k_router, dim3((d.n_experts + 15) / 16, (T + 15) / 16, a.S), dim3(256), 0,
+                       S(stream), a);
   hipLaunchKernelGGL(k_topk, dim3(T), dim3(256), 0, S(stream), a);
   return (int)hipGetLastError();
 }

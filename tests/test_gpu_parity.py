@@ -90,7 +90,10 @@ def test_dequantize_shared_tiny(tiny):
 
 # ---- routing ------------------------------------------------------------------
 
-@pytest.mark.parametrize("which,T", [("tiny", 1), ("tiny", 37), ("full", 1), ("full", 64)])
+# T >= 512 takes the 64 x 64 tiled router (600 tokens and the tiny layer's 16
+# experts: ragged in both; 1024 tokens: split along the hidden dimension)
+@pytest.mark.parametrize("which,T", [("tiny", 1), ("tiny", 37), ("full", 1), ("full", 64),
+                                     ("tiny", 600), ("full", 1024)])
 def test_route_parity(which, T, tiny, full):
     L = tiny if which == "tiny" else full
     _say("route", which, T)
