@@ -131,7 +131,6 @@ __global__ void __launch_bounds__(256) k_router(RouteArgs a) {
                                                     c0 + 8 * q);
   const bool ev = e < a.E, tv = t < a.T;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
   for (int k = 0; k < kw / 32; ++k) {
     uint4 av = wr[4 * k], bv = xr[4 * k];
     if (!ev) av = make_uint4(0, 0, 0, 0);

@@ -97,8 +97,8 @@ struct StackArgs {
 // workspace control block); empty otherwise.
 // They are kept in LDS and copied out when the kernel ends, so that taking
 // them adds no global store for a later wait on the vector memory counter.
-constexpr int kTrEv = 48;  // events per (workgroup, layer)
 #ifdef MOE_STACK_TRACE
+constexpr int kTrEv = 48;  // events per (workgroup, layer)
 #define MOE_TRACE(ev)                                                          \
   do {                                                                         \
     if (lane == 0) s_tr[l * kTrEv + (ev)] = __builtin_amdgcn_s_memrealtime();  \
@@ -733,7 +733,6 @@ __global__ void __launch_bounds__(kNT, 1) k_stack(StackArgs a) {
       uint32_t need = (1u << K) - 1u;  // routed slots not read yet
       while (need) {
         uint32_t pub = 0;
-#pragma unroll
         for (int k = 0; k < K; ++k)
           if (((need >> k) & 1u) && *lds(&s_cnt[k]) >= (uint32_t)kGuWaves * want) pub |= 1u << k;
         pub = __builtin_amdgcn_readfirstlane(pub);
