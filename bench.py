@@ -53,6 +53,10 @@ def parse():
                          "per token")
     ap.add_argument("--compare-paths", type=int, default=1,
                     help="also time the other path on a few tokens (0: skip)")
+    ap.add_argument("--timing", action="store_true",
+                    help="after the timed region, a per-stage breakdown of a few eager steps "
+                         "(moe_timing_*; the stack workloads: the multi-layer and the per-layer "
+                         "path) in the JSON line's \"stages\"")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB megabytes (calibrates the HBM "
                          "byte counters of the profiler) and exit")
@@ -401,10 +405,41 @@ def main():
         "parity_ok": check["ok"],
         "cpu_baseline": cpu,
     }
+    if args.timing:
+        out["stages"] = {}
+        for name, stk in (("multi-layer", True), ("per-layer", False)):
+            if stk and not fused:
+                continue
+            st = stage_breakdown(torch, moe, lambda i, stk=stk: enqueue_token(i % ntok, sp, stk), 4)
+            log_stages(name, st)
+            out["stages"][name] = st
     print(json.dumps(out), flush=True)
     if not check["ok"] or err:
         log("PARITY FAILED (or device error): see the parity object")
         sys.exit(3)
+
+
+def stage_breakdown(torch, moe, step, n):
+    """Per-stage times of n eager steps (HIP events the library records while
+    moe_timing is on), microseconds and calls per step.  Outside the timed
+    region: the events add host work to every stage."""
+    torch.cuda.synchronize()
+    moe.moe_timing_set(True)
+    try:
+        moe.moe_timing_read(reset=True)
+        for i in range(n):
+            step(i)
+        torch.cuda.synchronize()
+        t = moe.moe_timing_read(reset=True)
+    finally:
+        moe.moe_timing_set(False)
+    return {k: {"us_per_step": ms * 1e3 / n, "calls_per_step": c / n} for k, (ms, c) in t.items()}
+
+
+def log_stages(name, st):
+    log("stages (%s): %s" % (name, ", ".join("%s %.1f us x %.0f" % (k, v["us_per_step"],
+                                                                   v["calls_per_step"])
+                                             for k, v in st.items())))
 
 
 def spread(vals):
@@ -900,6 +935,11 @@ def bench_batch(args, wl):
         "flops_per_call": flops, "TFLOPs": tflops, "frac_bf16_peak": tflops / BF16_PEAK_TFLOPS,
         "cpu_baseline": None,
     }
+    if args.timing:
+        st = stage_breakdown(torch, moe, lambda i: moe.moe_layer_decode(
+            dims, L, xs[i % nb], wl.T, y, ids[i % nb], wts[i % nb], ws, wsb, sp), 4)
+        log_stages("moe_layer_decode", st)
+        out["stages"] = st
     print(json.dumps(out), flush=True)
 
 

@@ -32,7 +32,8 @@ EXPORTS = ("moe_abi_version", "moe_status_str", "moe_check_dims", "moe_expert_by
            "moe_tier_device_bytes", "moe_tier_workspace_bytes", "moe_tier_create",
            "moe_tier_decode", "moe_tier_plan", "moe_tier_stats", "moe_tier_destroy",
            "moe_stream_read_sink_words", "moe_stream_read", "moe_flush", "moe_stack_decode",
-           "moe_stack_decode_residual", "moe_stack_decode_residual_noalloc")
+           "moe_stack_decode_residual", "moe_stack_decode_residual_noalloc", "moe_timing_set",
+           "moe_timing_read")
 
 
 class MoeError(RuntimeError):
@@ -49,6 +50,15 @@ class moe_dims(ctypes.Structure):
 class moe_layer(ctypes.Structure):
     _fields_ = [("router", ctypes.c_void_p), ("experts", ctypes.c_void_p),
                 ("expert_stride", ctypes.c_int64), ("shared", ctypes.c_void_p)]
+
+
+# per-stage timing: stage names in MOE_ST_* order
+TIMING_STAGES = ("norm", "route", "bucket", "gateup", "down", "combine", "resid", "layer", "stack")
+
+
+class moe_timing(ctypes.Structure):
+    _fields_ = [("ms", ctypes.c_double * len(TIMING_STAGES)),
+                ("count", ctypes.c_int64 * len(TIMING_STAGES))]
 
 
 class moe_tier_config(ctypes.Structure):
@@ -115,6 +125,8 @@ def lib() -> ctypes.CDLL:
             "moe_stack_decode": (i32, [dp, lp, i32, vp, vp, vp, vp, vp, sz, vp]),
             "moe_stack_decode_residual": (i32, [dp, lp, i32, vp, vp, vp, vp, vp, vp, sz, vp]),
             "moe_stack_decode_residual_noalloc": (i32, [dp, lp, i32, vp, vp, vp, vp, vp, vp]),
+            "moe_timing_set": (i32, [i32]),
+            "moe_timing_read": (i32, [ctypes.POINTER(moe_timing), i32]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -382,6 +394,19 @@ def moe_stream_read(src, nbytes: int, sink, stream=None):
     moe_stream_read_sink_words(nbytes) words."""
     _check(lib().moe_stream_read(_ptr(src), nbytes, _ptr(sink), _stream(stream)),
            "moe_stream_read")
+
+
+def moe_timing_set(on: bool):
+    """Switches per-stage timing on or off."""
+    _check(lib().moe_timing_set(1 if on else 0), "moe_timing_set")
+
+
+def moe_timing_read(reset: bool = True) -> dict:
+    """Per-stage totals since the last reset: {stage: (ms, count)} for the
+    stages that ran (waits for the recorded events)."""
+    t = moe_timing()
+    _check(lib().moe_timing_read(ctypes.byref(t), 1 if reset else 0), "moe_timing_read")
+    return {n: (t.ms[i], t.count[i]) for i, n in enumerate(TIMING_STAGES) if t.count[i]}
 
 
 def moe_flush(dst, nbytes: int, stream=None):

@@ -8,7 +8,8 @@ LIB = os.path.join(HERE, "libmoe.so")
 SOURCES = [os.path.join(CSRC, "moe_host.cpp"), os.path.join(CSRC, "moe_kernels.hip"),
            os.path.join(CSRC, "moe_fused.hip"), os.path.join(CSRC, "moe_grouped.hip"),
            os.path.join(CSRC, "moe_tier.cpp"), os.path.join(CSRC, "moe_probe.hip"),
-           os.path.join(CSRC, "moe_stack.hip"), os.path.join(CSRC, "moe_noalloc.hip")]
+           os.path.join(CSRC, "moe_stack.hip"), os.path.join(CSRC, "moe_noalloc.hip"),
+           os.path.join(CSRC, "moe_timing.cpp")]
 HEADERS = [os.path.join(CSRC, "moe_internal.h"), os.path.join(CSRC, "moe_device.h"),
            os.path.join(CSRC, "moe_fused_dev.h"),
            os.path.join(os.path.dirname(HERE), "include", "moe.h")]

@@ -709,7 +709,9 @@ int launch_gemms(const GroupArgs &gu, const GroupArgs &dn, dim3 grid_gu, dim3 gr
   using DN = GL<BITS, true>;
   if (allow_lds(k_grouped<BITS, false>, GU::BYTES) || allow_lds(k_grouped<BITS, true>, DN::BYTES))
     return (int)hipErrorInvalidValue;
+  timing::mark(MOE_ST_GATEUP);
   hipLaunchKernelGGL((k_grouped<BITS, false>), grid_gu, dim3(256), GU::BYTES, st, gu);
+  timing::mark(MOE_ST_DOWN);
   hipLaunchKernelGGL((k_grouped<BITS, true>), grid_dn, dim3(256), DN::BYTES, st, dn);
   return 0;
 }
@@ -760,6 +762,7 @@ int launch_expert_forward_grouped(const moe_dims &d, const moe_layer &L, const u
   ba.has_shared = d.has_shared;
   ba.maxB = maxB;
   ba.pair_cap = T * (d.top_k + 1);
+  timing::mark(MOE_ST_BUCKET);
   hipLaunchKernelGGL(k_bucket, dim3(1), dim3(1024), 0, st, ba);
 
   XPrepArgs xa;
@@ -817,6 +820,7 @@ int launch_expert_forward_grouped(const moe_dims &d, const moe_layer &L, const u
                        : launch_gemms<2>(gu, dn, grid_gu, grid_dn, st);
   if (rc) return rc;
 
+  timing::mark(MOE_ST_COMBINE);
   CombineArgs ca;
   ca.yd = yd;
   ca.ids = ids;

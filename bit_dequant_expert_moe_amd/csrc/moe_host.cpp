@@ -129,6 +129,7 @@ static int fused_tokens(const moe_dims &d, const moe_layer &L, const uint16_t *x
                         void *stream) {
   const size_t H = (size_t)d.hidden, K = (size_t)d.top_k;
   for (int t = 0; t < T; ++t) {
+    timing::mark(MOE_ST_LAYER);
     const int rc = launch_layer_fused(
         d, L, x ? x + t * H : nullptr, ids_in ? ids_in + t * K : nullptr,
         w_in ? w_in + t * K : nullptr, ids_out ? ids_out + t * K : nullptr,
@@ -254,6 +255,8 @@ moe_status moe_route(const moe_dims *dims, const uint16_t *router, const uint16_
       (logits && !aligned(logits, 4)))
     return MOE_ERR_ALIGN;
   MOE_TRY(check_ws(dims, T, ws, ws_bytes));
+  timing::Scope timed(stream);
+  timing::mark(MOE_ST_ROUTE);
   return launch_route(*dims, router, x, T, ids, w, logits, ws, stream) == 0 ? MOE_OK
                                                                             : MOE_ERR_HIP;
 }
@@ -268,6 +271,7 @@ moe_status moe_expert_forward(const moe_dims *dims, const moe_layer *layer, cons
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ids, 4) || !aligned(w, 4))
     return MOE_ERR_ALIGN;
   MOE_TRY(check_ws(dims, T, ws, ws_bytes));
+  timing::Scope timed(stream);
   if (use_fused(*dims, T))
     return fused_tokens(*dims, *layer, x, T, ids, w, nullptr, nullptr, y, nullptr, nullptr, ws,
                         stream) == 0
@@ -288,6 +292,7 @@ moe_status moe_layer_decode(const moe_dims *dims, const moe_layer *layer, const 
   MOE_TRY(check_ws(dims, T, ws, ws_bytes));
   if (!layer->router) return MOE_ERR_NULL;
   if (!aligned(layer->router, 16)) return MOE_ERR_ALIGN;
+  timing::Scope timed(stream);
   if (use_fused(*dims, T))
     return fused_tokens(*dims, *layer, x, T, nullptr, nullptr, ids, w, y, nullptr, nullptr, ws,
                         stream) == 0
@@ -297,6 +302,7 @@ moe_status moe_layer_decode(const moe_dims *dims, const moe_layer *layer, const 
   uint8_t *base = static_cast<uint8_t *>(ws);
   int32_t *ids_d = ids ? ids : reinterpret_cast<int32_t *>(base + W.ids);
   float *w_d = w ? w : reinterpret_cast<float *>(base + W.w);
+  timing::mark(MOE_ST_ROUTE);
   if (launch_route(*dims, layer->router, x, T, ids_d, w_d, nullptr, ws, stream) != 0)
     return MOE_ERR_HIP;
   if (expert_forward(*dims, *layer, x, T, ids_d, w_d, y, ws, stream) != 0) return MOE_ERR_HIP;
@@ -314,6 +320,7 @@ moe_status moe_layer_decode_residual(const moe_dims *dims, const moe_layer *laye
       (ids && !aligned(ids, 4)) || (w && !aligned(w, 4)) || !aligned(layer->router, 16))
     return MOE_ERR_ALIGN;
   MOE_TRY(check_ws(dims, T, ws, ws_bytes));
+  timing::Scope timed(stream);
   if (use_fused(*dims, T))
     return fused_tokens(*dims, *layer, nullptr, T, nullptr, nullptr, ids, w, y, resid, x_out, ws,
                         stream) == 0
@@ -325,10 +332,13 @@ moe_status moe_layer_decode_residual(const moe_dims *dims, const moe_layer *laye
   float *y_d = y ? y : reinterpret_cast<float *>(base + W.yr);
   int32_t *ids_d = ids ? ids : reinterpret_cast<int32_t *>(base + W.ids);
   float *w_d = w ? w : reinterpret_cast<float *>(base + W.w);
+  timing::mark(MOE_ST_NORM);
   if (launch_rmsnorm(*dims, resid, T, x_d, stream) != 0) return MOE_ERR_HIP;
+  timing::mark(MOE_ST_ROUTE);
   if (launch_route(*dims, layer->router, x_d, T, ids_d, w_d, nullptr, ws, stream) != 0)
     return MOE_ERR_HIP;
   if (expert_forward(*dims, *layer, x_d, T, ids_d, w_d, y_d, ws, stream) != 0) return MOE_ERR_HIP;
+  timing::mark(MOE_ST_RESID);
   if (launch_resid_add(*dims, resid, y_d, T, stream) != 0) return MOE_ERR_HIP;
   return MOE_OK;
 }
@@ -347,10 +357,12 @@ moe_status moe_stack_decode(const moe_dims *dims, const moe_layer *layers, int32
   if (!aligned(x, 16) || !aligned(y, 16) || (ids && !aligned(ids, 4)) || (w && !aligned(w, 4)))
     return MOE_ERR_ALIGN;
   MOE_TRY(check_ws(dims, 1, ws, ws_bytes));
+  timing::Scope timed(stream);
   const size_t H = (size_t)dims->hidden, K = (size_t)dims->top_k;
   if (use_fused(*dims, 1) && !stack_disabled()) {
     for (int l0 = 0; l0 < n_layers; l0 += kMaxStackLayers) {
       const int n = n_layers - l0 < kMaxStackLayers ? n_layers - l0 : kMaxStackLayers;
+      timing::mark(MOE_ST_STACK);
       if (launch_stack_fused(*dims, layers + l0, n, x + l0 * H, y + l0 * H,
                              ids ? ids + l0 * K : nullptr, w ? w + l0 * K : nullptr, nullptr,
                              nullptr, ws, stream) != 0)
@@ -373,10 +385,12 @@ moe_status moe_stack_decode_residual(const moe_dims *dims, const moe_layer *laye
                                      void *stream) {
   MOE_TRY(check_stack_residual(dims, layers, n_layers, resid, x_out, y, ids, w));
   MOE_TRY(check_ws(dims, 1, ws, ws_bytes));
+  timing::Scope timed(stream);
   const size_t H = (size_t)dims->hidden, K = (size_t)dims->top_k;
   if (use_fused(*dims, 1) && !stack_disabled()) {
     for (int l0 = 0; l0 < n_layers; l0 += kMaxStackLayers) {
       const int n = n_layers - l0 < kMaxStackLayers ? n_layers - l0 : kMaxStackLayers;
+      timing::mark(MOE_ST_STACK);
       if (launch_stack_fused(*dims, layers + l0, n, nullptr, y ? y + l0 * H : nullptr,
                              ids ? ids + l0 * K : nullptr, w ? w + l0 * K : nullptr, resid,
                              x_out ? x_out + l0 * H : nullptr, ws, stream) != 0)
@@ -421,6 +435,16 @@ moe_status moe_stream_read(const void *src, size_t bytes, uint32_t *sink, void *
   if (bytes == 0 || bytes % 16 != 0) return MOE_ERR_SHAPE;
   if (!aligned(src, 16) || !aligned(sink, 4)) return MOE_ERR_ALIGN;
   return launch_stream_read(src, bytes, sink, stream) == 0 ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_timing_set(int32_t on) {
+  timing::set(on != 0);
+  return MOE_OK;
+}
+
+moe_status moe_timing_read(moe_timing *out, int32_t reset) {
+  if (!out) return MOE_ERR_NULL;
+  return timing::read(out->ms, out->count, reset != 0) == 0 ? MOE_OK : MOE_ERR_HIP;
 }
 
 moe_status moe_flush(void *dst, size_t bytes, void *stream) {

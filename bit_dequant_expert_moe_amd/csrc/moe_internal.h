@@ -129,6 +129,28 @@ inline int route_splits(const moe_dims &d, int T) {
   return s;
 }
 
+// Per-stage timing (moe_timing.cpp): an entry point opens a call on its
+// stream, marks the start of each stage (MOE_ST_*) and closes the call; all
+// no-ops while timing is off or the stream is being captured.  Calls nest:
+// only the outermost records.
+namespace timing {
+bool on();
+void set(bool enable);
+void begin(void *stream);
+void mark(int stage);
+void end();
+// waits for the closed calls' events and adds them to the totals; copies the
+// totals out (and zeroes them with reset); -1 if an event call failed
+int read(double *ms, int64_t *count, bool reset);
+// opens a call for the lifetime of the object
+struct Scope {
+  explicit Scope(void *stream) { begin(stream); }
+  ~Scope() { end(); }
+  Scope(const Scope &) = delete;
+  Scope &operator=(const Scope &) = delete;
+};
+}  // namespace timing
+
 // Kernel launchers (moe_kernels.hip).  Each returns hipSuccess (0) or the
 // HIP error of the launch.
 int launch_ws_init(void *ws, size_t bytes, void *stream);

@@ -718,12 +718,16 @@ int launch_expert_forward(const moe_dims &d, const moe_layer &L, const uint16_t 
   if (d.bits == 4) {
     if (allow_lds(k_gateup<4>, lds_gu) || allow_lds(k_down<4>, lds_dn))
       return (int)hipErrorInvalidValue;
+    timing::mark(MOE_ST_GATEUP);
     hipLaunchKernelGGL(k_gateup<4>, grid_gu, dim3(256), lds_gu, S(stream), g);
+    timing::mark(MOE_ST_DOWN);
     hipLaunchKernelGGL(k_down<4>, grid_dn, dim3(256), lds_dn, S(stream), dn);
   } else {
     if (allow_lds(k_gateup<2>, lds_gu) || allow_lds(k_down<2>, lds_dn))
       return (int)hipErrorInvalidValue;
+    timing::mark(MOE_ST_GATEUP);
     hipLaunchKernelGGL(k_gateup<2>, grid_gu, dim3(256), lds_gu, S(stream), g);
+    timing::mark(MOE_ST_DOWN);
     hipLaunchKernelGGL(k_down<2>, grid_dn, dim3(256), lds_dn, S(stream), dn);
   }
   return (int)hipGetLastError();

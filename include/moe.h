@@ -416,6 +416,52 @@ moe_status moe_stream_read(const void *src, size_t bytes, uint32_t *sink, void *
  * cached. */
 moe_status moe_flush(void *dst, size_t bytes, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * Per-stage timing: the per-layer breakdown that the pages' timing flag
+ * prints ("Flash-MoE: Running a 397B Parameter Model on a Laptop",
+ * hysenlabs.com, section "Install"; the stage times of section "How the SSD
+ * expert streaming pipeline works"), taken with HIP events.
+ *
+ * While timing is on, every decode entry point (moe_route,
+ * moe_expert_forward, moe_layer_decode, moe_layer_decode_residual,
+ * moe_stack_decode, moe_stack_decode_residual) records an event on its
+ * stream before each of its stages and one after its last; moe_timing_read
+ * waits for the events recorded so far and adds each stage's elapsed time
+ * to the stage's total.  Timing starts on when the environment variable
+ * MOE_TIMING is set to anything but "0" at the library's first timed call,
+ * and moe_timing_set switches it.  A call whose stream is being captured
+ * into a graph records nothing.  Recorded events are held until the next
+ * moe_timing_read, so a long run reads from time to time.  The events add a
+ * few microseconds of host work per stage; the numbers are for breakdowns,
+ * not for the benchmark's figures.
+ * ------------------------------------------------------------------------- */
+enum {
+  MOE_ST_NORM = 0,    /* RMS norm of the residual (moe_layer_decode_residual) */
+  MOE_ST_ROUTE = 1,   /* router logits, top-K and weights */
+  MOE_ST_BUCKET = 2,  /* pairs grouped by expert, x staged (T >= 4) */
+  MOE_ST_GATEUP = 3,  /* gate and up products, SwiGLU (unfused kernels) */
+  MOE_ST_DOWN = 4,    /* down products (unfused kernels; T <= 3: and combine) */
+  MOE_ST_COMBINE = 5, /* weighted combine (T >= 4) */
+  MOE_ST_RESID = 6,   /* residual add (moe_layer_decode_residual) */
+  MOE_ST_LAYER = 7,   /* the whole layer in one kernel (single-token path) */
+  MOE_ST_STACK = 8,   /* layers of one token in one kernel (per launch) */
+  MOE_TIMING_STAGES = 9
+};
+
+typedef struct {
+  double ms[MOE_TIMING_STAGES];    /* total time per stage, milliseconds */
+  int64_t count[MOE_TIMING_STAGES]; /* times each stage ran */
+} moe_timing;
+
+/* Switches timing on (on != 0) or off.  Host only; always MOE_OK. */
+moe_status moe_timing_set(int32_t on);
+
+/* Waits for the events recorded so far (synchronises the host with them),
+ * writes the totals since the last reset to *out and, if reset != 0, sets
+ * them to zero.  MOE_ERR_NULL for out == NULL; MOE_ERR_HIP if an event call
+ * failed since the last read (the totals then miss those stages). */
+moe_status moe_timing_read(moe_timing *out, int32_t reset);
+
 #ifdef __cplusplus
 }
 #endif

@@ -225,3 +225,12 @@ def test_stream_read_and_flush_validation():
     assert _status(moe.moe_flush, dst=None, nbytes=4096, stream=0) == -1
     assert _status(moe.moe_flush, dst=A, nbytes=24, stream=0) == -2
     assert _status(moe.moe_flush, dst=A + 4, nbytes=4096, stream=0) == -4
+
+
+def test_timing_switch_and_empty_read():
+    # no GPU call: with nothing recorded a read only copies the totals
+    moe.moe_timing_set(True)
+    assert moe.moe_timing_read(reset=True) == {}
+    moe.moe_timing_set(False)
+    assert moe.moe_timing_read() == {}
+    assert moe.lib().moe_timing_read(None, 0) == -1  # MOE_ERR_NULL
