@@ -216,7 +216,10 @@ struct GL {  // LDS geometry
   static constexpr int BPT = kNC * kSl * BV / 256;  // B pieces per thread
   static constexpr int A_U32 = NMAT * kRT * RW;
   // gate/up: float2 (s, z - 128 s) per row and group; down: the (s, z) words
-  // (the smaller area keeps three down blocks within a compute unit's LDS)
+  // (the smaller area keeps three down blocks within a compute unit's LDS);
+  // group-major ([matrix][group][row]), so that a lane's four output rows are
+  // 16 or 32 contiguous bytes and the four row quads of a wave fall in
+  // different banks
   static constexpr int SB_U32 = NMAT * kRT * kGC * (DOWN ? 1 : 2);
   static constexpr int B_U32 = kNC * BCS * 4;
   static constexpr int XS_U32 = kNC * kGC;
@@ -456,22 +459,22 @@ __global__ void __launch_bounds__(256, MOE_GROUPED_MINW) k_grouped(GroupArgs a) 
       dst[2] = R.ra[i].z;
       dst[3] = R.ra[i].w;
     }
+    const uint32_t w4[4] = {R.rsb.x, R.rsb.y, R.rsb.z, R.rsb.w};
     if (DOWN) {
-      if (tid < kRT) *reinterpret_cast<uint4 *>(SB + tid * kGC) = R.rsb;
+      if (tid < kRT) {
+#pragma unroll
+        for (int g = 0; g < kGC; ++g) SB[g * kRT + tid] = w4[g];
+      }
     } else if (sbok) {
       // per group (s, z - 128 s): the MFMA sums (128 + q) b, so
       // s sum q b + z sum b = s P + (z - 128 s) X
-      const uint32_t w4[4] = {R.rsb.x, R.rsb.y, R.rsb.z, R.rsb.w};
-      float f[8];
+      const int mat = tid / kRT, rr = tid % kRT;
+      float2 *dst = reinterpret_cast<float2 *>(SB);
 #pragma unroll
       for (int g = 0; g < kGC; ++g) {
         const float sc = bf16f(w4[g] & 0xFFFFu), zb = bf16f(w4[g] >> 16);
-        f[2 * g] = sc;
-        f[2 * g + 1] = fmaf(-128.f, sc, zb);
+        dst[(mat * kGC + g) * kRT + rr] = make_float2(sc, fmaf(-128.f, sc, zb));
       }
-      float4 *dst = reinterpret_cast<float4 *>(SB + tid * kGC * 2);
-      dst[0] = make_float4(f[0], f[1], f[2], f[3]);
-      dst[1] = make_float4(f[4], f[5], f[6], f[7]);
     }
 #pragma unroll
     for (int i = 0; i < G::BPT; ++i) {
@@ -517,18 +520,26 @@ __global__ void __launch_bounds__(256, MOE_GROUPED_MINW) k_grouped(GroupArgs a) 
       // element v of this lane: row 4 q + v of the wave's 16, B column col;
       // the scale term here, the bias term once per chunk below
 #pragma unroll
-      for (int m = 0; m < G::NMAT; ++m)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          if (DOWN) {
-            const uint32_t sb = SB[(wave * 16 + 4 * q + v) * kGC + gi];
-            acc[m][v] = fmaf(bf16f(sb & 0xFFFFu), P[m][v], acc[m][v]);
-          } else {
-            const float2 sz =
-                reinterpret_cast<const float2 *>(SB)[(m * kRT + wave * 16 + 4 * q + v) * kGC + gi];
-            acc[m][v] = fmaf(sz.x, P[m][v], acc[m][v]);
-          }
+      for (int m = 0; m < G::NMAT; ++m) {
+        float sc[4];
+        if (DOWN) {
+          const uint4 sb = *reinterpret_cast<const uint4 *>(SB + gi * kRT + wave * 16 + 4 * q);
+          sc[0] = bf16f(sb.x & 0xFFFFu);
+          sc[1] = bf16f(sb.y & 0xFFFFu);
+          sc[2] = bf16f(sb.z & 0xFFFFu);
+          sc[3] = bf16f(sb.w & 0xFFFFu);
+        } else {
+          const float4 *sz = reinterpret_cast<const float4 *>(
+              reinterpret_cast<const float2 *>(SB) + (m * kGC + gi) * kRT + wave * 16 + 4 * q);
+          const float4 s01 = sz[0], s23 = sz[1];
+          sc[0] = s01.x;
+          sc[1] = s01.z;
+          sc[2] = s23.x;
+          sc[3] = s23.z;
         }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[m][v] = fmaf(sc[v], P[m][v], acc[m][v]);
+      }
     }
     // bias term of the chunk's kGC groups, sum_g (z - 128 s)[row][g] X[g][col],
     // as one fp32 16x16x4 product: lane l supplies row l % 16, group l / 16 of
@@ -539,10 +550,10 @@ __global__ void __launch_bounds__(256, MOE_GROUPED_MINW) k_grouped(GroupArgs a) 
     for (int m = 0; m < G::NMAT; ++m) {
       float zp;
       if (DOWN) {
-        const uint32_t sb = SB[(wave * 16 + col) * kGC + q];
+        const uint32_t sb = SB[q * kRT + wave * 16 + col];
         zp = fmaf(-128.f, bf16f(sb & 0xFFFFu), bf16f(sb >> 16));
       } else {
-        zp = reinterpret_cast<const float2 *>(SB)[(m * kRT + wave * 16 + col) * kGC + q].y;
+        zp = reinterpret_cast<const float2 *>(SB)[(m * kGC + q) * kRT + wave * 16 + col].y;
       }
       acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(zp, xg, acc[m], 0, 0, 0);
     }
