@@ -76,10 +76,11 @@
  * - Results are deterministic: identical inputs give bitwise-identical
  *   outputs (no floating-point atomics; fixed reduction orders).
  * - The workspace `ws` (device memory, caller-owned, moe_workspace_bytes
- *   bytes, 256-byte aligned) must be initialised once with
- *   moe_workspace_init before its first use; every call leaves it
- *   initialised again.  Two calls that overlap in time must not share a
- *   workspace.
+ *   bytes, 256-byte aligned) must be initialised once before its first use:
+ *   with moe_workspace_init, or by allocating it zero-filled (a workspace
+ *   whose bytes are all zero is initialised; moe_workspace_init zeroes its
+ *   control words).  Every call leaves it initialised again.  Two calls that
+ *   overlap in time must not share a workspace.
  * - A call of 1 to 3 tokens on a GPU with 256 compute units, hidden 4096,
  *   intermediate 1024 and top-4 runs as one launch per token of 256
  *   workgroups, one per compute unit, that exchange data while running: it
@@ -164,7 +165,8 @@ moe_status moe_blob_layout(const moe_dims *dims, size_t out_offsets[6]);
 /* Workspace bytes needed for calls with T tokens (0 if invalid).  Host only. */
 size_t moe_workspace_bytes(const moe_dims *dims, int32_t T);
 
-/* Enqueues the one-time initialisation of a workspace of ws_bytes bytes. */
+/* Enqueues the one-time initialisation of a workspace of ws_bytes bytes
+ * (zeroes its control words; not needed for a zero-filled workspace). */
 moe_status moe_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
 /* Routing ([HL], "How the SSD expert streaming pipeline works": the router

@@ -263,6 +263,34 @@ def test_batched_equals_single_and_deterministic(full):
             assert gu.max_rel_err(o1["y"][0], ob["y"][t]) <= gu.Y_TOL
 
 
+def test_zero_filled_workspace_needs_no_init(full):
+    # a zero-filled workspace is an initialised one: the same outputs bit for
+    # bit as a workspace set up by moe_workspace_init (one token: the fused
+    # kernel; eight tokens: the grouped path)
+    import torch
+    for T in (1, 8):
+        x = full.x_dev(synth.tokens(1001, 70 + T, T, 4096))
+        outs = []
+        for zero in (False, True):
+            if zero:
+                n = moe.moe_workspace_bytes(full.dims, T)
+                buf = torch.zeros(n + 256, dtype=torch.uint8, device="cuda")
+                off = (-buf.data_ptr()) % 256
+                ws = buf[off:off + n]
+            else:
+                ws = moe.alloc_workspace(full.dims, T)
+            y = torch.empty((T, 4096), dtype=torch.float32, device="cuda")
+            ids = torch.empty((T, 4), dtype=torch.int32, device="cuda")
+            for _ in range(2):  # first call and a second on the same workspace
+                moe.moe_layer_decode(full.dims, full.L, x, T, y, ids, None, ws)
+                torch.cuda.synchronize()
+                assert moe.moe_get_device_error(ws) == 0
+                outs.append((y.cpu().numpy().copy(), ids.cpu().numpy().copy()))
+        for a, b in zip(outs[:2], outs[2:]):
+            np.testing.assert_array_equal(a[0], b[0])
+            np.testing.assert_array_equal(a[1], b[1])
+
+
 # ---- single-token fused path: repeated calls, graphs, error word ----------------
 
 @pytest.mark.parametrize("T", [2, 3])
