@@ -57,6 +57,11 @@ def parse():
                     help="after the timed region, a per-stage breakdown of a few eager steps "
                          "(moe_timing_*; the stack workloads: the multi-layer and the per-layer "
                          "path) in the JSON line's \"stages\"")
+    ap.add_argument("--layer-trace", action="store_true",
+                    help="after the timed region, one token's per-layer step times from the "
+                         "multi-layer kernel's own timestamps (needs a library built with "
+                         "-DMOE_STACK_TRACE, loaded through MOE_LIB) in the JSON line's "
+                         "\"layer_trace\"")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB megabytes (calibrates the HBM "
                          "byte counters of the profiler) and exit")
@@ -405,6 +410,16 @@ def main():
         "parity_ok": check["ok"],
         "cpu_baseline": cpu,
     }
+    if args.layer_trace and stack_path and fused:
+        tr = layer_trace(torch, ws, nl, lambda: enqueue_token(0, sp, True))
+        if tr is None:
+            log("layer trace: the library was built without MOE_STACK_TRACE")
+        else:
+            for name, v in tr["steps"].items():
+                log("  %-26s median %6.2f  p90 %6.2f us" % (name, v["median_us"], v["p90_us"]))
+            log("  layer period %.2f us, logits polls per layer %.1f" % (
+                tr["layer_period_us"], tr["logits_polls_per_layer"]))
+        out["layer_trace"] = tr
     if args.timing:
         out["stages"] = {}
         for name, stk in (("multi-layer", True), ("per-layer", False)):
@@ -440,6 +455,57 @@ def log_stages(name, st):
     log("stages (%s): %s" % (name, ", ".join("%s %.1f us x %.0f" % (k, v["us_per_step"],
                                                                    v["calls_per_step"])
                                              for k, v in st.items())))
+
+
+# Steps the multi-layer kernel timestamps in a build with MOE_STACK_TRACE
+# (event number -> name); event 26 holds the logits poll count x 100.
+TRACE_EVENTS = {
+    15: "r gathered", 27: "gate/up: r read", 28: "gate/up: norm done",
+    30: "gate/up: x from LDS", 31: "gate/up: router partials", 29: "gate/up: staged",
+    0: "A (exchange)", 8: "A (gate/up)", 1: "logits published", 25: "first logits poll issued",
+    5: "first logits poll back", 34: "logits taken", 32: "top-K selected",
+    9: "shared gate/up published", 2: "top-K done", 6: "first shared h poll back",
+    10: "routed loads issued", 19: "row: routed loads issued", 3: "shared h read",
+    20: "row: shared rows done", 11: "slot 0 published", 16: "slot 0 h read",
+    21: "row: slot 0 rows done", 12: "slot 1 published", 17: "slot 1 h read",
+    22: "row: slot 1 rows done", 13: "slot 2 published", 18: "slot 2 h read",
+    23: "row: slot 2 rows done", 14: "slot 3 published", 4: "slot 3 h read",
+    24: "row: slot 3 rows done", 7: "layer end (y)"}
+
+
+def layer_trace(torch, ws, nl, run):
+    """One token's per-layer step times from the multi-layer kernel's
+    timestamps.  The trace buffer's device address goes into the workspace's
+    control block (bytes 8..15) for one call and is cleared after it.  Per
+    step: median and 90th percentile over workgroups and the inner layers of
+    the time since the layer's first barrier (earliest workgroup), in us; the
+    device clock counts at 100 MHz.  None when the library was built without
+    the timestamps."""
+    nev, maxl, nwg = 48, 64, 256
+    buf = torch.zeros(nwg * maxl * nev, dtype=torch.int64, device=ws.device)
+    torch.cuda.synchronize()
+    ws[8:16].copy_(torch.tensor([buf.data_ptr()], dtype=torch.int64).view(torch.uint8))
+    try:
+        run()
+        torch.cuda.synchronize()
+    finally:
+        ws[8:16].zero_()
+        torch.cuda.synchronize()
+    T = buf.cpu().numpy().reshape(nwg, maxl, nev)[:, :nl, :].astype(np.float64) * 0.01
+    if not T.any() or nl < 3:
+        return None
+    R = np.stack([np.where(T[:, l, :] > 0, T[:, l, :] - T[:, l, 0].min(), np.nan)
+                  for l in range(1, nl - 1)])
+    steps = {}
+    for ev, name in TRACE_EVENTS.items():
+        v = R[:, :, ev]
+        if np.all(np.isnan(v)):
+            continue
+        steps[name] = {"median_us": float(np.nanmedian(v)), "p90_us": float(np.nanpercentile(v, 90))}
+    starts = np.array([T[:, l, 0].min() for l in range(nl)])
+    return {"steps": dict(sorted(steps.items(), key=lambda kv: kv[1]["median_us"])),
+            "layer_period_us": float(np.median(np.diff(starts))),
+            "logits_polls_per_layer": float(np.median(T[:, 1:nl - 1, 26]))}
 
 
 def spread(vals):
