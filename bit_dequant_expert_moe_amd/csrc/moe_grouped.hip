@@ -352,9 +352,17 @@ __global__ void __launch_bounds__(256) k_xprep(XPrepArgs a) {
 #define MOE_GROUPED_MINW 3
 #endif
 
+// Row tiles per block of the down pass: its rows are short (C = I = 1024, four
+// chunks), so one block runs the chunks of consecutive row tiles as one
+// pipeline and the memory latency of a block's first chunks is paid once.
+#ifndef MOE_GROUPED_DN_TILES
+#define MOE_GROUPED_DN_TILES 2
+#endif
+
 template <int BITS, bool DOWN>
 __global__ void __launch_bounds__(256, MOE_GROUPED_MINW) k_grouped(GroupArgs a) {
   using G = GL<BITS, DOWN>;
+  constexpr int RTL = DOWN ? MOE_GROUPED_DN_TILES : 1;  // row tiles per block
   extern __shared__ __align__(16) uint32_t lds[];
   __shared__ float s_hsum[4][16];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -370,7 +378,7 @@ __global__ void __launch_bounds__(256, MOE_GROUPED_MINW) k_grouped(GroupArgs a) 
   const int nn = min(kNC, p1 - pbase);
   const int32_t *pairs = a.bk + 2 + 2 * a.maxB + pbase;
   const uint8_t *blob = e == a.E ? a.shared : a.experts + (size_t)e * a.stride;
-  const int row0 = kRT * (int)blockIdx.x;
+  const int row0 = kRT * RTL * (int)blockIdx.x;
   const size_t rbytes = (size_t)a.C * BITS / 8;
   const int groups = a.C / kGroup;
   const int nslices = a.C / 8;
@@ -432,10 +440,15 @@ __global__ void __launch_bounds__(256, MOE_GROUPED_MINW) k_grouped(GroupArgs a) 
   }
   // chunk c's offsets: the chunk-0 offset plus the chunk's, or kNoLoad
   auto at = [](uint32_t off0, uint32_t step) { return off0 == kNoLoad ? kNoLoad : off0 + step; };
-  auto load_chunk = [&](int c, Regs &R) {
+  // virtual chunk vc: column chunk vc % nchunks of row tile vc / nchunks
+  const int nv = RTL * nchunks;
+  auto load_chunk = [&](int vc, Regs &R) {
+    const int c = vc & (nchunks - 1), tile = vc / nchunks;
+    const uint32_t arow = (uint32_t)(tile * kRT) * (uint32_t)rbytes;
 #pragma unroll
-    for (int i = 0; i < G::APT; ++i) R.ra[i] = bload16(rs_blob, aoff[i] + c * (kKC * BITS / 8));
-    R.rsb = bload16(rs_blob, at(sboff, c * kGC * 4));
+    for (int i = 0; i < G::APT; ++i)
+      R.ra[i] = bload16(rs_blob, aoff[i] + arow + c * (kKC * BITS / 8));
+    R.rsb = bload16(rs_blob, at(sboff, (uint32_t)(tile * kRT * groups * 4) + c * kGC * 4));
 #pragma unroll
     for (int i = 0; i < G::BPT; ++i) R.rb[i] = bload16(rs_b, at(boff[i], c * kSl * G::BV * 16));
     R.rxs = bload4f(rs_s, at(soff, c * kGC * 4));
@@ -559,51 +572,63 @@ __global__ void __launch_bounds__(256, MOE_GROUPED_MINW) k_grouped(GroupArgs a) 
     }
   };
 
-  // ---- software pipeline over the column chunks ----------------------------
+  // ---- software pipeline over the (virtual) column chunks -------------------
   // chunk c is computed from LDS buffer c & 1 while chunks c + 1 and c + 2
   // are in flight in the register sets.  The steady-state loop issues its
   // loads unconditionally, and so does the prologue (a row of one chunk loads
   // chunk 0 twice): with a load skipped on some path, the wait before a chunk
   // is staged would have to count as if no later load were in flight, which
   // drains the pipeline to one chunk.
+  // Down pass: a row tile's outputs are written after its last chunk.
+  const int orow0 = row0 + wave * 16 + 4 * q;  // first of this lane's 4 rows (tile 0)
+  auto finish = [&](int vc) {
+    if (DOWN && ((vc + 1) & (nchunks - 1)) == 0) {
+      const int tile = vc / nchunks;
+      if (bvalid) {
+        const float4 o = make_float4(acc[0][0], acc[0][1], acc[0][2], acc[0][3]);
+        *reinterpret_cast<float4 *>(a.yd + (size_t)code * a.R + orow0 + tile * kRT) = o;
+      }
+      acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
   Regs R0, R1;
   load_chunk(0, R0);
-  load_chunk(nchunks > 1 ? 1 : 0, R1);
+  load_chunk(nv > 1 ? 1 : 0, R1);
   store_chunk(0, R0);
   __syncthreads();
   int c = 0;
-  for (; c + 3 < nchunks; c += 2) {
+  for (; c + 3 < nv; c += 2) {
     load_chunk(c + 2, R0);
     compute_chunk(0);
+    finish(c);
     store_chunk(1, R1);
     __syncthreads();
     load_chunk(c + 3, R1);
     compute_chunk(1);
+    finish(c + 1);
     store_chunk(0, R0);
     __syncthreads();
   }
   // the last one to three chunks: c is in buffer 0, c + 1 in R1
-  if (c + 2 < nchunks) load_chunk(c + 2, R0);
+  if (c + 2 < nv) load_chunk(c + 2, R0);
   compute_chunk(0);
-  if (c + 1 < nchunks) {
+  finish(c);
+  if (c + 1 < nv) {
     store_chunk(1, R1);
     __syncthreads();
     compute_chunk(1);
-    if (c + 2 < nchunks) {
+    finish(c + 1);
+    if (c + 2 < nv) {
       store_chunk(0, R0);
       __syncthreads();
       compute_chunk(0);
+      finish(c + 2);
     }
   }
 
-  // ---- epilogue -------------------------------------------------------------
-  const int orow = row0 + wave * 16 + 4 * q;  // first of this lane's 4 rows
-  if (DOWN) {
-    if (bvalid) {
-      const float4 o = make_float4(acc[0][0], acc[0][1], acc[0][2], acc[0][3]);
-      *reinterpret_cast<float4 *>(a.yd + (size_t)code * a.R + orow) = o;
-    }
-  } else {
+  // ---- epilogue (gate/up) ---------------------------------------------------
+  const int orow = orow0;
+  if (!DOWN) {
     // h for 4 rows; with the neighbour's 4 (lane + 16) they form the 8-row
     // slice that lanes with even q write as the B operand of the down pass
     float hv[4], hsum = 0.f;
@@ -826,7 +851,7 @@ int launch_expert_forward_grouped(const moe_dims &d, const moe_layer &L, const u
   dn.off_q0 = dn.off_q1 = (int64_t)B.off[MOE_SEC_DOWN_Q];
   dn.off_sb0 = dn.off_sb1 = (int64_t)B.off[MOE_SEC_DOWN_SB];
   const dim3 grid_gu((unsigned)(d.inter / kRT), (unsigned)nitems);
-  const dim3 grid_dn((unsigned)(d.hidden / kRT), (unsigned)nitems);
+  const dim3 grid_dn((unsigned)(d.hidden / (kRT * MOE_GROUPED_DN_TILES)), (unsigned)nitems);
   int rc = d.bits == 4 ? launch_gemms<4>(gu, dn, grid_gu, grid_dn, st)
                        : launch_gemms<2>(gu, dn, grid_gu, grid_dn, st);
   if (rc) return rc;
