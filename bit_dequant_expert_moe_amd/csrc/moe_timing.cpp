@@ -123,26 +123,40 @@ void end() {
 }
 
 int read(double *ms, int64_t *count, bool reset) {
-  std::lock_guard<std::mutex> g(g_mu);
-  int rc = g_failed ? -1 : 0;
-  g_failed = false;
-  for (Call &c : g_closed) {
+  // the closed calls are taken out under the lock and waited for outside it,
+  // so that other threads' timed calls do not wait on these events
+  std::vector<Call> calls;
+  bool failed;
+  {
+    std::lock_guard<std::mutex> g(g_mu);
+    calls.swap(g_closed);
+    failed = g_failed;
+    g_failed = false;
+  }
+  int rc = failed ? -1 : 0;
+  double add_ms[MOE_TIMING_STAGES] = {};
+  int64_t add_n[MOE_TIMING_STAGES] = {};
+  std::vector<hipEvent_t> used;
+  for (Call &c : calls) {
     if (hipEventSynchronize(c.end) != hipSuccess) rc = -1;
     for (size_t i = 0; i < c.marks.size(); ++i) {
       const hipEvent_t next = i + 1 < c.marks.size() ? c.marks[i + 1].ev : c.end;
       float t = 0.f;
       if (hipEventElapsedTime(&t, c.marks[i].ev, next) == hipSuccess) {
-        g_ms[c.marks[i].stage] += t;
-        g_n[c.marks[i].stage] += 1;
+        add_ms[c.marks[i].stage] += t;
+        add_n[c.marks[i].stage] += 1;
       } else {
         rc = -1;
       }
-      g_pool.push_back(c.marks[i].ev);
+      used.push_back(c.marks[i].ev);
     }
-    g_pool.push_back(c.end);
+    used.push_back(c.end);
   }
-  g_closed.clear();
+  std::lock_guard<std::mutex> g(g_mu);
+  g_pool.insert(g_pool.end(), used.begin(), used.end());
   for (int s = 0; s < MOE_TIMING_STAGES; ++s) {
+    g_ms[s] += add_ms[s];
+    g_n[s] += add_n[s];
     ms[s] = g_ms[s];
     count[s] = g_n[s];
     if (reset) {
