@@ -107,6 +107,34 @@ def test_route_parity(which, T, tiny, full):
     assert exact >= 0.8 * T
 
 
+@pytest.mark.parametrize("E,K,T", [(1000, 8, 520), (100, 4, 513), (64, 2, 4096)])
+def test_route_parity_tiled_ragged(E, K, T):
+    # the 64 x 64 tiled router (T >= 512) with expert counts off its tiles
+    # (1000 and 100: a partial last tile; 64: one tile) and K up to 8: logits
+    # within 1e-4 of float64, ids and weights as in the other routing tests;
+    # only the router is needed
+    import torch
+    H = 4096
+    dims = moe.Dims(hidden=H, inter=1024, n_experts=E, top_k=K)
+    od = oracle.Dims(H=H, I=1024, E=E, K=K)
+    router_h = synth.router_weights(2000 + E, 0, E, H)
+    x_h = synth.tokens(2000 + E, 1, T, H)
+    _say("route tiled", E, K, T)
+    r = torch.from_numpy(router_h.view(np.int16)).cuda()
+    x = torch.from_numpy(x_h.view(np.int16)).cuda()
+    ids = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    ws = moe.alloc_workspace(dims, T)
+    moe.moe_route(dims, r, x, T, ids, w, logits, ws)
+    torch.cuda.synchronize()
+    ids_o, w_o, logits_o, gap_o = oracle.route(od, router_h, x_h)
+    assert np.max(np.abs(logits.cpu().numpy() - logits_o)) < 1e-4
+    exact = gu.check_routing(od, ids.cpu().numpy(), w.cpu().numpy(), logits_o, gap_o, K)
+    _say("  tokens with exact ids:", exact, "of", T)
+    assert exact >= 0.8 * T
+
+
 # ---- full layer -----------------------------------------------------------------
 
 def _layer_check(L, x, label):
