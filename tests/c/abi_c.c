@@ -107,6 +107,81 @@ static int gpu_checks(int T) {
 }
 #endif
 
+#ifdef MOE_C_GPU
+/* Two layers of one token in the multi-layer kernel (full shape, 4 experts),
+ * plain, and chained through the residual with the entry point that takes no
+ * workspace: with zero weights y = 0, so the residual comes back unchanged. */
+static int stack_checks(void) {
+  const moe_dims d = {4096, 1024, 4, 4, 64, 4, 1};
+  const size_t blob = moe_expert_bytes(&d), H = 4096, K = 4, NL = 2;
+  const size_t wsb = moe_workspace_bytes(&d, 1);
+  void *experts = NULL, *shared = NULL, *router = NULL, *x = NULL, *y = NULL, *ids = NULL,
+       *w = NULL, *ws = NULL, *r = NULL;
+  static float yh[2 * 4096], rh[4096], rback[4096];
+  static uint16_t xh[2 * 4096];
+  float wh[2 * 4];
+  int32_t idh[2 * 4];
+  size_t i;
+  moe_layer L[2];
+  CHECK(hipMalloc(&experts, 4 * blob) == hipSuccess && hipMalloc(&shared, blob) == hipSuccess &&
+            hipMalloc(&router, 4 * H * 2) == hipSuccess && hipMalloc(&x, NL * H * 2) == hipSuccess &&
+            hipMalloc(&y, NL * H * 4) == hipSuccess && hipMalloc(&ids, NL * K * 4) == hipSuccess &&
+            hipMalloc(&w, NL * K * 4) == hipSuccess && hipMalloc(&ws, wsb) == hipSuccess &&
+            hipMalloc(&r, H * 4) == hipSuccess,
+        "hipMalloc (stack)");
+  CHECK(hipMemset(experts, 0, 4 * blob) == hipSuccess && hipMemset(shared, 0, blob) == hipSuccess &&
+            hipMemset(router, 0, 4 * H * 2) == hipSuccess && hipMemset(ws, 0, wsb) == hipSuccess,
+        "hipMemset (stack)");
+  for (i = 0; i < NL * H; ++i) xh[i] = (uint16_t)(0x3F80u + (i % 5));
+  for (i = 0; i < H; ++i) rh[i] = (float)((int)(i % 11) - 5) * 0.25f;
+  CHECK(hipMemcpy(x, xh, NL * H * 2, hipMemcpyHostToDevice) == hipSuccess &&
+            hipMemcpy(r, rh, H * 4, hipMemcpyHostToDevice) == hipSuccess,
+        "copy x, r");
+  for (i = 0; i < NL; ++i) {
+    L[i].router = (const uint16_t *)router;
+    L[i].experts = (const uint8_t *)experts;
+    L[i].expert_stride = (int64_t)blob;
+    L[i].shared = (const uint8_t *)shared;
+  }
+  CHECK(moe_stack_decode(&d, L, (int32_t)NL, (const uint16_t *)x, (float *)y, (int32_t *)ids,
+                         (float *)w, ws, wsb, NULL) == MOE_OK,
+        "moe_stack_decode");
+  CHECK(hipDeviceSynchronize() == hipSuccess, "synchronise (stack)");
+  CHECK(hipMemcpy(yh, y, NL * H * 4, hipMemcpyDeviceToHost) == hipSuccess &&
+            hipMemcpy(idh, ids, NL * K * 4, hipMemcpyDeviceToHost) == hipSuccess &&
+            hipMemcpy(wh, w, NL * K * 4, hipMemcpyDeviceToHost) == hipSuccess,
+        "copy back (stack)");
+  for (i = 0; i < NL * H; ++i) CHECK(yh[i] == 0.0f, "stack y == 0");
+  for (i = 0; i < NL * K; ++i) {
+    CHECK(idh[i] == (int32_t)(i % K), "stack ids 0..3");
+    CHECK(wh[i] == 0.25f, "stack weights 1/4");
+  }
+  CHECK(moe_stack_decode_residual_noalloc(&d, L, (int32_t)NL, (float *)r, NULL, NULL,
+                                          (int32_t *)ids, NULL, NULL) == MOE_OK,
+        "moe_stack_decode_residual_noalloc");
+  CHECK(hipDeviceSynchronize() == hipSuccess, "synchronise (residual)");
+  CHECK(hipMemcpy(rback, r, H * 4, hipMemcpyDeviceToHost) == hipSuccess &&
+            hipMemcpy(idh, ids, NL * K * 4, hipMemcpyDeviceToHost) == hipSuccess,
+        "copy back (residual)");
+  for (i = 0; i < H; ++i) CHECK(rback[i] == rh[i], "residual unchanged (r += 0)");
+  for (i = 0; i < NL * K; ++i) CHECK(idh[i] == (int32_t)(i % K), "residual ids 0..3");
+  {
+    int32_t err = -1;
+    CHECK(moe_get_device_error(ws, NULL, &err) == MOE_OK && err == 0, "no device error (stack)");
+  }
+  hipFree(experts);
+  hipFree(shared);
+  hipFree(router);
+  hipFree(x);
+  hipFree(y);
+  hipFree(ids);
+  hipFree(w);
+  hipFree(ws);
+  hipFree(r);
+  return 0;
+}
+#endif
+
 int main(int argc, char **argv) {
   if (host_checks()) return 1;
 #ifdef MOE_C_GPU
@@ -114,6 +189,7 @@ int main(int argc, char **argv) {
     int T;
     for (T = 1; T <= 4; T += 3)
       if (gpu_checks(T)) return 1;
+    if (stack_checks()) return 1;
   }
 #else
   (void)argc;

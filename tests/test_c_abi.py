@@ -2,7 +2,9 @@
 include/moe.h and libmoe.so (the header must be valid C) and run: host-only
 calls on the CPU, and one layer on all-zero weights on the GPU (closed-form
 result: ids 0 .. K-1, weights 1/K, y = 0) through the three-kernel path
-(T = 1 at these dims) and the grouped path (T = 4)."""
+(T = 1 at these dims) and the grouped path (T = 4), and two layers in the
+multi-layer kernel, plain and chained through the residual with the entry
+point that takes no workspace (the residual comes back unchanged)."""
 import os
 import subprocess
 
