@@ -508,6 +508,20 @@ def layer_trace(torch, ws, nl, run):
             "logits_polls_per_layer": float(np.median(T[:, 1:nl - 1, 26]))}
 
 
+def host_cores():
+    """Threads for the oracle: the cores this process may run on, capped by
+    OMP_NUM_THREADS when it is set (the count may exceed the host's share
+    otherwise)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return max(1, n)
+
+
 def spread(vals):
     v = np.asarray(vals, dtype=np.float64)
     return {"median": float(np.median(v)), "p10": float(np.percentile(v, 10)),
@@ -655,7 +669,7 @@ def cpu_baseline(oracle, od, wl, nl, n_single, experts, shared, routers_h, x_h, 
     ns = max(1, min(n_single, nl))
     oracle.set_threads(1)
     dt1 = run(ns)
-    cores = os.cpu_count() or 1
+    cores = host_cores()
     oracle.set_threads(cores)
     dta = run(nl)
     oracle.set_threads(1)
@@ -772,7 +786,7 @@ def bench_layer(args, wl):
         ido, _, _, _ = oracle.route(od, rh, x_h[:nt])
         blobs = {int(e): fetch(int(e)) for e in np.unique(ido)}
         shh = sh.cpu().numpy()
-        cores = os.cpu_count() or 1
+        cores = host_cores()
         oracle.set_threads(cores)
         tc = time.perf_counter()
         oracle.layer(od, rh, blobs, shh, x_h[:nt])
